@@ -1,0 +1,287 @@
+"""CPU oracle for block-sparse GQA attention over a pooled, page-aware block cache.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain reference that the
+GPU library is checked against.  Only the test suite, the package smoke check
+and the benchmark's CPU-baseline leg may import it; the library itself never
+does, and it shares no code with the library (no kernels, headers, tables or
+helpers).  Inputs are numpy arrays (values as float32/float64, tables as
+int32); nothing here knows about torch or the GPU.
+
+What is computed, with the passage each step follows:
+
+1. Block representatives ("Art of Focus: Ling 2.0 and the Revolution in Sparse
+   Attention", section "Summarizing the Breakthrough": at prefill the tokens of
+   a block are aggregated into one representative that lives in a cache keyed
+   like the paged KV cache).  The aggregate is the arithmetic mean of the
+   block's keys per KV head.  Block size = page size, so the representative of
+   a logical block is stored at the block's physical page id.
+2. Group scores (same page, same section: the query heads of a GQA group share
+   one block selection; "MiniMax Sparse Attention (MSA)" post, second
+   paragraph: the index branch scores KV blocks and picks a top-k subset per
+   GQA group).  Score of block j for query token t of group g =
+   sum over the group's heads h of q[h, t] . rep[j, g]  (unscaled logits).
+3. Causal top-k (MSA post, second and third paragraphs: top-k per group,
+   ranked without any exponential).  Candidates are the blocks strictly before
+   the query's own block; the own block is always kept and counts toward k;
+   ranking is by score, higher first, equal scores keep the lower block index;
+   the kept list is sorted ascending and padded with -1.
+4. Exact attention over the selected blocks ("Sparse Attention + Linear
+   Backbones", section 5.5 "Pseudocode Sketch": softmax of q.k/sqrt(d) over the
+   selected keys, then times the selected values; "Sparse Attention for
+   Long-Context LLMs: Evolution and Practical Deployment", section 4.3: the
+   top-k mask restricts the softmax, read here as an additive minus-infinity
+   mask, i.e. the unselected keys do not take part).  Inside the own block a
+   key takes part only if its position is at most the query's position.
+
+Precision: attention and scores are computed in float64.  Two results are
+codes decided by floating point, and those decisions are taken in the
+library's own precision: the block-cache entry (float32 sum of the block's
+keys in token order, times 1/page_size, then rounded to nearest-even into the
+cache dtype) and the block ranking (float64 score rounded to float32, then
+ordered by (-score, index)).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits", "bf16_value", "round_to_cache", "gather_tokens", "block_pool",
+    "query_positions", "group_scores", "select_blocks", "selected_keys",
+    "sparse_attention", "prefill_reference", "decode_reference",
+]
+
+
+# ----------------------------------------------------------------------------
+# bf16 rounding (round to nearest, ties to even) on the float32 bit pattern
+# ----------------------------------------------------------------------------
+def bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Nearest-even bf16 code (uint16) of float32 values (finite inputs)."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """float32 value of bf16 codes."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_to_cache(x32: np.ndarray, cache_dtype: str) -> np.ndarray:
+    """float32 array -> values representable in the cache dtype (as float32)."""
+    if cache_dtype == "f32":
+        return np.asarray(x32, dtype=np.float32)
+    if cache_dtype == "bf16":
+        return bf16_value(bf16_bits(x32))
+    raise ValueError(cache_dtype)
+
+
+# ----------------------------------------------------------------------------
+# paged layout helpers
+# ----------------------------------------------------------------------------
+def gather_tokens(pages: np.ndarray, pt_row: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Logical tokens [Hkv, n_tokens, D] of one sequence from a paged pool.
+
+    ``pages``: [P, Hkv, bs, D]; logical block j lives in page ``pt_row[j]``.
+    """
+    P, Hkv, bs, D = pages.shape
+    nblk = (n_tokens + bs - 1) // bs
+    sel = pages[np.asarray(pt_row[:nblk], dtype=np.int64)]        # [nblk, Hkv, bs, D]
+    return sel.transpose(1, 0, 2, 3).reshape(Hkv, nblk * bs, D)[:, :n_tokens]
+
+
+def query_positions(kv_len: int, q_len: int, t_idx: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Position of query t: kv_len - q_len + t (the newest query is last)."""
+    t = np.arange(q_len) if t_idx is None else np.asarray(t_idx, dtype=np.int64)
+    return kv_len - q_len + t
+
+
+# ----------------------------------------------------------------------------
+# 1. block representatives
+# ----------------------------------------------------------------------------
+def block_pool(k_pages: np.ndarray, page_table: np.ndarray, kv_lens: Sequence[int],
+               cache_dtype: str, blk_begin: Optional[Sequence[int]] = None,
+               block_cache: Optional[np.ndarray] = None) -> np.ndarray:
+    """Mean of each complete block's keys, per KV head, into the block cache.
+
+    For sequence b and each complete logical block j in [blk_begin[b],
+    kv_len[b] // bs): ``cache[page_table[b, j], g, :]`` = round_to_cache(
+    (K[tok 0] + K[tok 1] + ... + K[tok bs-1]) * (1/bs)), the sum taken in
+    float32 in token order.  Entries of other pages are left as they were
+    (zero for a fresh cache).  Returns the block cache [P, Hkv, D] (float32
+    values, representable in ``cache_dtype``).
+    """
+    P, Hkv, bs, D = k_pages.shape
+    out = np.zeros((P, Hkv, D), np.float32) if block_cache is None else np.array(block_cache, np.float32)
+    inv = np.float32(1.0 / bs)
+    for b, L in enumerate(kv_lens):
+        begin = 0 if blk_begin is None else int(blk_begin[b])
+        end = int(L) // bs
+        if end <= begin:
+            continue
+        phys = np.asarray(page_table[b, begin:end], dtype=np.int64)
+        keys = np.asarray(k_pages[phys], dtype=np.float32)            # [n, Hkv, bs, D]
+        acc = np.zeros((len(phys), Hkv, D), np.float32)
+        for i in range(bs):                                           # token order
+            acc = acc + keys[:, :, i, :]
+        out[phys] = round_to_cache(acc * inv, cache_dtype)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# 2. group scores
+# ----------------------------------------------------------------------------
+def group_scores(q: np.ndarray, block_cache: np.ndarray, page_table: np.ndarray,
+                 kv_lens: Sequence[int], num_kv_heads: int, page_size: int,
+                 t_idx: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Scores [B, Hkv, T, nb_max] in float64; -inf where j is not a candidate.
+
+    q: [B, Hq, q_len, D].  Candidates of a query at position p are the blocks
+    j < p // page_size, i.e. strictly before its own block.
+    """
+    B, Hq, q_len, D = q.shape
+    G = Hq // num_kv_heads
+    nb_max = page_table.shape[1]
+    T = q_len if t_idx is None else len(t_idx)
+    out = np.full((B, num_kv_heads, T, nb_max), -np.inf, np.float64)
+    tsel = np.arange(q_len) if t_idx is None else np.asarray(t_idx, dtype=np.int64)
+    for b in range(B):
+        pos = query_positions(int(kv_lens[b]), q_len, tsel)
+        own = pos // page_size
+        nb = int(own.max()) if T else 0
+        if nb == 0:
+            continue
+        reps = np.asarray(block_cache[np.asarray(page_table[b, :nb], np.int64)], np.float64)  # [nb, Hkv, D]
+        for g in range(num_kv_heads):
+            qs = np.asarray(q[b, g * G:(g + 1) * G][:, tsel], np.float64).sum(axis=0)   # [T, D]
+            s = qs @ reps[:, g, :].T                                                   # [T, nb]
+            cand = np.arange(nb)[None, :] < own[:, None]
+            out[b, g, :, :nb] = np.where(cand, s, -np.inf)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# 3. causal top-k per group
+# ----------------------------------------------------------------------------
+def select_blocks(scores: np.ndarray, kv_lens: Sequence[int], q_len: int, page_size: int,
+                  top_k: int, t_idx: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Selected logical blocks [B, Hkv, T, top_k] (int32, ascending, -1 padded).
+
+    ``scores`` as returned by :func:`group_scores` for the same ``t_idx``.  The
+    ranking is decided on the float32 rounding of the scores: order by score
+    (higher first), equal scores by block index (lower first); keep the first
+    min(top_k - 1, own) candidates, then add the own block.
+    """
+    B, Hkv, T, nb_max = scores.shape
+    s32 = scores.astype(np.float32)
+    out = np.full((B, Hkv, T, top_k), -1, np.int32)
+    tsel = np.arange(q_len) if t_idx is None else np.asarray(t_idx, dtype=np.int64)
+    for b in range(B):
+        own = query_positions(int(kv_lens[b]), q_len, tsel) // page_size        # [T]
+        # stable sort of -score: descending score, ascending index among equals;
+        # non-candidates (-inf) end up last
+        order = np.argsort(-s32[b], axis=-1, kind="stable")                     # [Hkv, T, nb]
+        m = top_k - 1
+        if m > 0:
+            top = order[..., :m] if nb_max >= m else np.concatenate(
+                [order, np.full(order.shape[:-1] + (m - nb_max,), np.iinfo(np.int64).max)], axis=-1)
+            valid = top < own[None, :, None]
+            sel = np.where(valid, top, np.iinfo(np.int64).max)
+        else:
+            sel = np.zeros((Hkv, T, 0), np.int64)
+        full = np.concatenate([sel, np.broadcast_to(own[None, :, None], (Hkv, T, 1))], axis=-1)
+        full = np.sort(full, axis=-1)
+        full = np.where(full == np.iinfo(np.int64).max, -1, full)
+        out[b] = full.astype(np.int32)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# 4. exact attention over the selected blocks
+# ----------------------------------------------------------------------------
+def selected_keys(sel_row: Sequence[int], pos: int, page_size: int) -> np.ndarray:
+    """Key positions a query at ``pos`` attends to: the tokens of its selected
+    blocks, restricted to positions <= pos."""
+    idx = []
+    for j in sel_row:
+        j = int(j)
+        if j < 0:
+            continue
+        lo = j * page_size
+        hi = min(lo + page_size, pos + 1)
+        if hi > lo:
+            idx.append(np.arange(lo, hi))
+    return np.concatenate(idx) if idx else np.zeros((0,), np.int64)
+
+
+def sparse_attention(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, page_table: np.ndarray,
+                     kv_lens: Sequence[int], block_idx: np.ndarray, scale: float,
+                     t_idx: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(out [B, Hq, T, D], lse [B, Hq, T]) in float64.
+
+    ``block_idx`` [B, Hkv, T, k] for the same ``t_idx``.  For query head h of
+    group g = h // G at position p: z_i = (q . k_i) * scale over the selected
+    keys i, out = sum_i softmax(z)_i v_i, lse = max z + log(sum exp(z - max z)).
+    """
+    B, Hq, q_len, D = q.shape
+    _, Hkv, bs, _ = k_pages.shape
+    G = Hq // Hkv
+    tsel = np.arange(q_len) if t_idx is None else np.asarray(t_idx, dtype=np.int64)
+    T = len(tsel)
+    out = np.zeros((B, Hq, T, D), np.float64)
+    lse = np.full((B, Hq, T), -np.inf, np.float64)
+    for b in range(B):
+        L = int(kv_lens[b])
+        K = np.asarray(gather_tokens(k_pages, page_table[b], L), np.float64)   # [Hkv, L, D]
+        V = np.asarray(gather_tokens(v_pages, page_table[b], L), np.float64)
+        pos_all = query_positions(L, q_len, tsel)
+        for g in range(Hkv):
+            for ti in range(T):
+                keys = selected_keys(block_idx[b, g, ti], int(pos_all[ti]), bs)
+                if keys.size == 0:
+                    continue
+                qh = np.asarray(q[b, g * G:(g + 1) * G, tsel[ti]], np.float64)   # [G, D]
+                z = (qh @ K[g, keys].T) * scale                                  # [G, n]
+                m = z.max(axis=1, keepdims=True)
+                w = np.exp(z - m)
+                l = w.sum(axis=1, keepdims=True)
+                out[b, g * G:(g + 1) * G, ti] = (w @ V[g, keys]) / l
+                lse[b, g * G:(g + 1) * G, ti] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# whole path
+# ----------------------------------------------------------------------------
+def prefill_reference(q, k_pages, v_pages, page_table, kv_lens, page_size, top_k, cache_dtype,
+                      scale: Optional[float] = None, t_idx=None):
+    """Block pool -> group scores -> top-k -> sparse attention, for the queries
+    ``t_idx`` (default all).  Returns dict(block_cache, scores, block_idx, out, lse)."""
+    B, Hq, q_len, D = q.shape
+    Hkv = k_pages.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    cache = block_pool(k_pages, page_table, kv_lens, cache_dtype)
+    sc = group_scores(q, cache, page_table, kv_lens, Hkv, page_size, t_idx)
+    idx = select_blocks(sc, kv_lens, q_len, page_size, top_k, t_idx)
+    out, lse = sparse_attention(q, k_pages, v_pages, page_table, kv_lens, idx, scale, t_idx)
+    return dict(block_cache=cache, scores=sc, block_idx=idx, out=out, lse=lse)
+
+
+def decode_reference(q, k_pages, v_pages, page_table, kv_lens, page_size, top_k, cache_dtype,
+                     scale: Optional[float] = None, block_cache=None):
+    """One decode step (q_len = 1).  The block cache holds every complete block
+    of each sequence; it is built here unless given."""
+    if block_cache is None:
+        block_cache = block_pool(k_pages, page_table, kv_lens, cache_dtype)
+    B, Hq, q_len, D = q.shape
+    Hkv = k_pages.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    sc = group_scores(q, block_cache, page_table, kv_lens, Hkv, page_size)
+    idx = select_blocks(sc, kv_lens, q_len, page_size, top_k)
+    out, lse = sparse_attention(q, k_pages, v_pages, page_table, kv_lens, idx, scale)
+    return dict(block_cache=block_cache, scores=sc, block_idx=idx, out=out, lse=lse)
