@@ -1,0 +1,13 @@
+"""Block-sparse GQA attention with a pooled, page-aware block cache, for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libbsg.so`` (C ABI in ``include/bsg.h``); this package
+only marshals torch tensors into its calls.  Build it with
+``python -m block_sparse_gqa_pool_amd.build``.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS, LIB_PATH, BsgDims, BsgError, block_pool, decode_workspace_bytes, dims, group_score,
+    group_score_topk, group_score_topk_workspace_bytes, lib, sparse_attn_decode, sparse_attn_prefill,
+    topk_blocks,
+)
+
+__version__ = "1.0.0"

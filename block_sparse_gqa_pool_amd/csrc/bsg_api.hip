@@ -1,0 +1,131 @@
+// C entry points: host-side validation, then launches on the caller's stream.
+// Every check runs before anything is enqueued, so an error leaves the stream untouched.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bsg.h"
+#include "bsg_internal.h"
+
+namespace {
+
+int check_dims(const bsg_dims* d) {
+  if (!d) return BSG_ERR_NULL;
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->page_size < 1 ||
+      d->top_k < 1 || d->num_pages < 1 || d->pt_stride < 1)
+    return BSG_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return BSG_ERR_SHAPE;
+  if (d->dtype != BSG_F32 && d->dtype != BSG_BF16) return BSG_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return BSG_ERR_UNSUPPORTED;
+  if (d->page_size != 64 && d->page_size != 128) return BSG_ERR_UNSUPPORTED;
+  if (d->top_k > 64) return BSG_ERR_UNSUPPORTED;
+  // 32-bit element offsets inside one sequence's page row and safe grid sizes
+  if ((long long)d->pt_stride * d->page_size > (1LL << 30)) return BSG_ERR_UNSUPPORTED;
+  return BSG_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? BSG_OK : BSG_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int bsg_version(void) { return 10000; }
+
+const char* bsg_status_str(int status) {
+  switch (status) {
+    case BSG_OK: return "BSG_OK";
+    case BSG_ERR_NULL: return "BSG_ERR_NULL: a required pointer is NULL";
+    case BSG_ERR_SHAPE: return "BSG_ERR_SHAPE: inconsistent or non-positive sizes";
+    case BSG_ERR_UNSUPPORTED: return "BSG_ERR_UNSUPPORTED: dtype, head_dim, page_size or top_k not supported";
+    case BSG_ERR_WORKSPACE: return "BSG_ERR_WORKSPACE: workspace missing or too small";
+    case BSG_ERR_HIP: return "BSG_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown bsg status";
+  }
+}
+
+int bsg_block_pool(const bsg_dims* dims, const void* k_cache, const int32_t* page_table, const int32_t* kv_lens,
+                   const int32_t* blk_begin, void* block_cache, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!k_cache || !page_table || !kv_lens || !block_cache) return BSG_ERR_NULL;
+  return to_status(bsg::launch_block_pool(*dims, k_cache, page_table, kv_lens, blk_begin, block_cache,
+                                          (hipStream_t)stream));
+}
+
+int bsg_group_score(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                    const void* block_cache, const int32_t* page_table, float* scores, int32_t score_stride,
+                    void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !kv_lens || !block_cache || !page_table || !scores) return BSG_ERR_NULL;
+  if (q_len < 1 || score_stride < 1) return BSG_ERR_SHAPE;
+  return to_status(bsg::launch_group_score(*dims, q, q_len, kv_lens, block_cache, page_table, scores, score_stride,
+                                           (hipStream_t)stream));
+}
+
+int bsg_topk_blocks(const bsg_dims* dims, const float* scores, int32_t q_len, int32_t score_stride,
+                    const int32_t* kv_lens, int32_t* block_idx, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!scores || !kv_lens || !block_idx) return BSG_ERR_NULL;
+  if (q_len < 1 || score_stride < 1) return BSG_ERR_SHAPE;
+  return to_status(bsg::launch_topk(*dims, scores, q_len, score_stride, kv_lens, block_idx, (hipStream_t)stream));
+}
+
+size_t bsg_group_score_topk_workspace_bytes(const bsg_dims* dims, int32_t q_len) {
+  if (check_dims(dims) || q_len < 1) return 0;
+  if (bsg::group_score_topk_fused_supported(*dims, q_len)) return 0;
+  return (size_t)dims->batch * dims->num_kv_heads * (size_t)q_len * dims->pt_stride * sizeof(float);
+}
+
+int bsg_group_score_topk(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                         const void* block_cache, const int32_t* page_table, int32_t* block_idx, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !kv_lens || !block_cache || !page_table || !block_idx) return BSG_ERR_NULL;
+  if (q_len < 1) return BSG_ERR_SHAPE;
+  const size_t need = bsg_group_score_topk_workspace_bytes(dims, q_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BSG_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (need == 0)
+    return to_status(bsg::launch_group_score_topk_fused(*dims, q, q_len, kv_lens, block_cache, page_table,
+                                                        block_idx, s));
+  float* scores = (float*)workspace;
+  hipError_t e = bsg::launch_group_score(*dims, q, q_len, kv_lens, block_cache, page_table, scores,
+                                         dims->pt_stride, s);
+  if (e != hipSuccess) return BSG_ERR_HIP;
+  return to_status(bsg::launch_topk(*dims, scores, q_len, dims->pt_stride, kv_lens, block_idx, s));
+}
+
+int bsg_sparse_attn_prefill(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                            const void* k_cache, const void* v_cache, const int32_t* page_table,
+                            const int32_t* block_idx, float scale, void* out, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !kv_lens || !k_cache || !v_cache || !page_table || !block_idx || !out) return BSG_ERR_NULL;
+  if (q_len < 1) return BSG_ERR_SHAPE;
+  return to_status(bsg::launch_attn_prefill(*dims, q, q_len, kv_lens, k_cache, v_cache, page_table, block_idx,
+                                            scale, out, lse, (hipStream_t)stream));
+}
+
+size_t bsg_decode_workspace_bytes(const bsg_dims* dims) {
+  if (check_dims(dims)) return 0;
+  return bsg::decode_workspace_bytes(*dims);
+}
+
+int bsg_sparse_attn_decode(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* k_cache,
+                           const void* v_cache, const int32_t* page_table, const int32_t* block_idx, float scale,
+                           void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !kv_lens || !k_cache || !v_cache || !page_table || !block_idx || !out) return BSG_ERR_NULL;
+  const int G = dims->num_q_heads / dims->num_kv_heads;
+  if (G * dims->head_dim > 2048) return BSG_ERR_UNSUPPORTED;
+  const size_t need = bsg::decode_workspace_bytes(*dims);
+  if (!workspace || workspace_bytes < need) return BSG_ERR_WORKSPACE;
+  return to_status(bsg::launch_attn_decode(*dims, q, kv_lens, k_cache, v_cache, page_table, block_idx, scale,
+                                           workspace, out, lse, (hipStream_t)stream));
+}
+
+}  // extern "C"

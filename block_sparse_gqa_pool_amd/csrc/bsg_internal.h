@@ -1,0 +1,42 @@
+// Host-side launchers shared between the kernel sources and the C entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bsg.h"
+
+namespace bsg {
+
+hipError_t launch_block_pool(const bsg_dims& d, const void* k_cache, const int32_t* page_table,
+                             const int32_t* kv_lens, const int32_t* blk_begin, void* block_cache,
+                             hipStream_t stream);
+
+hipError_t launch_group_score(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
+                              const void* block_cache, const int32_t* page_table, float* scores,
+                              int score_stride, hipStream_t stream);
+
+hipError_t launch_topk(const bsg_dims& d, const float* scores, int q_len, int score_stride,
+                       const int32_t* kv_lens, int32_t* block_idx, hipStream_t stream);
+
+// Fused prefill scoring + selection (bf16, q_len > 1): MFMA scores, per-row streaming top-k.
+bool group_score_topk_fused_supported(const bsg_dims& d, int q_len);
+hipError_t launch_group_score_topk_fused(const bsg_dims& d, const void* q, int q_len,
+                                         const int32_t* kv_lens, const void* block_cache,
+                                         const int32_t* page_table, int32_t* block_idx,
+                                         hipStream_t stream);
+
+hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
+                               const void* k_cache, const void* v_cache, const int32_t* page_table,
+                               const int32_t* block_idx, float scale, void* out, float* lse,
+                               hipStream_t stream);
+
+int decode_num_splits(const bsg_dims& d);
+size_t decode_workspace_bytes(const bsg_dims& d);
+hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* kv_lens,
+                              const void* k_cache, const void* v_cache, const int32_t* page_table,
+                              const int32_t* block_idx, float scale, void* workspace, void* out,
+                              float* lse, hipStream_t stream);
+
+}  // namespace bsg

@@ -1,0 +1,200 @@
+/*
+ * bsg.h -- C ABI of the block-sparse GQA attention library for AMD MI355X (gfx950).
+ *
+ * The method (Ling 2.0 sparse attention / MiniMax Sparse Attention):
+ *   - keys and values live in a paged KV cache; a block is one page;
+ *   - each complete block is summarised by the mean of its keys, per KV head,
+ *     in a block cache that is indexed by the same physical page ids as the KV
+ *     cache ("Art of Focus: Ling 2.0 and the Revolution in Sparse Attention",
+ *     section "Summarizing the Breakthrough": block representations are built
+ *     at prefill, kept in a page-aware block cache that shares the KV cache's
+ *     indexing, and only the chosen blocks are fetched at decode);
+ *   - all query heads of a GQA group share one block selection: the group's
+ *     summed query is scored against the block representatives and the top-k
+ *     causal blocks are kept, the query's own block always among them
+ *     (same section; "MiniMax Sparse Attention (MSA)" post, second paragraph);
+ *   - exact softmax attention then runs over the selected blocks only
+ *     ("Sparse Attention + Linear Backbones", section 5.5 "Pseudocode Sketch";
+ *     MSA post, second paragraph).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *   - Every tensor pointer is a DEVICE pointer to contiguous row-major memory
+ *     owned by the caller.  `dims` points to HOST memory.  The library keeps
+ *     no state between calls, allocates no device memory, and is reentrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; nothing synchronises.  Calls on one stream run in order.
+ *   - Every call validates its host-side arguments first.  On any error it
+ *     returns a negative bsg_status and enqueues nothing.  A failed kernel
+ *     launch returns BSG_ERR_HIP.
+ *   - Device-side contents are trusted: page ids must be < num_pages, block
+ *     ids in block_idx must be -1 or < ceil(kv_len / page_size), and
+ *     q_len <= kv_len <= pt_stride * page_size.  Kernels clamp page and block
+ *     ids into range (so a bad table cannot make them read out of bounds) but
+ *     the results for such inputs are unspecified.
+ *   - Layouts (B = batch, Hq / Hkv = query / KV heads, G = Hq / Hkv,
+ *     D = head_dim, bs = page_size = block size, P = num_pages):
+ *       k_cache, v_cache : [P, Hkv, bs, D]   dtype
+ *       block_cache      : [P, Hkv, D]       dtype (representative of the block
+ *                                            stored in page p, per KV head)
+ *       page_table       : int32 [B, pt_stride]; logical block j of sequence b
+ *                          is physical page page_table[b*pt_stride + j]
+ *       kv_lens          : int32 [B]; tokens of sequence b in the cache
+ *       q                : [B, Hq, q_len, D] dtype; query t of sequence b sits
+ *                          at position kv_lens[b] - q_len + t (decode: q_len = 1)
+ *       block_idx        : int32 [B, Hkv, q_len, top_k]; logical block ids of
+ *                          the selection, ascending, padded with -1 at the end
+ *       out              : [B, Hq, q_len, D] dtype;  lse : fp32 [B, Hq, q_len]
+ *     Query head h belongs to group g = h / G.
+ *   - Supported: dtype f32 or bf16; head_dim 64 or 128; page_size 64 or 128;
+ *     1 <= top_k <= 64; Hq a multiple of Hkv.
+ */
+#ifndef BSG_H
+#define BSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSG_OK = 0,
+  BSG_ERR_NULL = -1,        /* a required pointer is NULL */
+  BSG_ERR_SHAPE = -2,       /* inconsistent or non-positive sizes */
+  BSG_ERR_UNSUPPORTED = -3, /* valid but not implemented (dtype, D, page size, k) */
+  BSG_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  BSG_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+} bsg_status;
+
+typedef enum { BSG_F32 = 0, BSG_BF16 = 1 } bsg_dtype;
+
+typedef struct {
+  int32_t batch;        /* B */
+  int32_t num_q_heads;  /* Hq */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* D */
+  int32_t page_size;    /* bs: tokens per page = tokens per block */
+  int32_t top_k;        /* blocks kept per (sequence, group, query), own block included */
+  int32_t num_pages;    /* P: pages in the K / V pools and in the block cache */
+  int32_t pt_stride;    /* row stride of page_table = max logical blocks per sequence */
+  int32_t dtype;        /* bsg_dtype of q, caches and out */
+} bsg_dims;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int bsg_version(void);
+
+/* Human-readable name of a bsg_status value (static string). */
+const char* bsg_status_str(int status);
+
+/*
+ * bsg_block_pool -- write block representatives for complete blocks.
+ * Follows the Ling 2.0 page, "Summarizing the Breakthrough" (blocks are
+ * aggregated into representatives stored in a cache that shares the KV
+ * cache's page indexing); the aggregate is the mean of the block's keys.
+ *
+ * For each sequence b and each complete logical block
+ *     j in [blk_begin[b], kv_lens[b] / page_size)
+ * with p = page_table[b, j]:
+ *     block_cache[p, g, :] = round(  (K[p, g, 0, :] + ... + K[p, g, bs-1, :])
+ *                                   * (1 / bs) )
+ * where the sum is taken in fp32 in token order and round() is
+ * round-to-nearest-even into the cache dtype.  Entries of other pages are not
+ * touched.  blk_begin may be NULL (= 0 for every sequence); pass
+ * blk_begin[b] = kv_lens[b] / bs - 1 after a page completes to refresh only
+ * that page.  The result is bit-identical for every launch configuration.
+ */
+int bsg_block_pool(const bsg_dims* dims, const void* k_cache, const int32_t* page_table,
+                   const int32_t* kv_lens, const int32_t* blk_begin, void* block_cache,
+                   void* stream);
+
+/*
+ * bsg_group_score -- materialised group scores.
+ * Follows the Ling 2.0 page, "Summarizing the Breakthrough" (the heads of a
+ * GQA group share the selection) and the MSA post, second paragraph (blocks
+ * are scored per GQA group).
+ *
+ * scores: fp32 [B, Hkv, q_len, score_stride].  For query t at position p and
+ * own block o = p / page_size:
+ *     scores[b, g, t, j] = sum over the G heads h of group g of
+ *                          q[b, h, t, :] . block_cache[page_table[b, j], g, :]
+ * for j < min(o, score_stride), computed in fp32; every other entry
+ * j < score_stride is -inf.  No 1/sqrt(D) factor (it does not change ranks).
+ */
+int bsg_group_score(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                    const void* block_cache, const int32_t* page_table, float* scores,
+                    int32_t score_stride, void* stream);
+
+/*
+ * bsg_topk_blocks -- causal top-k selection from materialised scores.
+ * Follows the MSA post, second and third paragraphs (top-k per GQA group,
+ * selected without exponentials).
+ *
+ * For each row (b, g, t) with own block o: the min(top_k - 1, o) candidates
+ * j < o with the largest scores[b, g, t, j] are kept (equal scores: the lower
+ * block index wins; -0.0 equals +0.0), the own block o is added, and the
+ * kept ids are written ascending to block_idx[b, g, t, :], padded with -1.
+ * Requires score_stride >= the largest own block of any row.
+ */
+int bsg_topk_blocks(const bsg_dims* dims, const float* scores, int32_t q_len, int32_t score_stride,
+                    const int32_t* kv_lens, int32_t* block_idx, void* stream);
+
+/*
+ * bsg_group_score_topk -- fused scoring and selection (no materialised scores).
+ * Same result as bsg_group_score followed by bsg_topk_blocks, except that the
+ * fp32 scores may be accumulated in a different order, so rows whose k-th
+ * and (k+1)-th candidates score within fp32 rounding of each other may
+ * differ.  `workspace` (device, may be NULL when the query below returns 0)
+ * must hold bsg_group_score_topk_workspace_bytes(dims, q_len) bytes.
+ */
+size_t bsg_group_score_topk_workspace_bytes(const bsg_dims* dims, int32_t q_len);
+int bsg_group_score_topk(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                         const void* block_cache, const int32_t* page_table, int32_t* block_idx,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bsg_sparse_attn_prefill -- exact attention over the selected blocks.
+ * Follows "Sparse Attention + Linear Backbones", section 5.5 (softmax of
+ * q.k / sqrt(d) over the selected keys times their values) and "Sparse
+ * Attention for Long-Context LLMs", section 4.3 (the top-k mask removes the
+ * unselected keys; read as an additive -inf mask, so they are skipped).
+ *
+ * For query head h (group g) at position p, the keys are the tokens
+ * i <= p of the blocks listed in block_idx[b, g, t, :] (-1 entries ignored):
+ *     z_i   = scale * (q[b, h, t, :] . K_i)
+ *     out   = sum_i softmax(z)_i V_i          (rounded to the dtype)
+ *     lse   = max z + ln(sum_i exp(z_i - max z))    (fp32; lse may be NULL)
+ * Accumulation is fp32; bf16 inputs use bf16 matrix-core products.  Token
+ * slots of a page beyond kv_len are never used (their contents may be
+ * anything, NaN included).
+ */
+int bsg_sparse_attn_prefill(const bsg_dims* dims, const void* q, int32_t q_len,
+                            const int32_t* kv_lens, const void* k_cache, const void* v_cache,
+                            const int32_t* page_table, const int32_t* block_idx, float scale,
+                            void* out, float* lse, void* stream);
+
+/*
+ * bsg_sparse_attn_decode -- one query token per sequence (q_len = 1), split
+ * over the selected blocks with a log-sum-exp merge.  Same definition as
+ * bsg_sparse_attn_prefill with q_len = 1; block_idx is [B, Hkv, top_k].
+ * Follows the Ling 2.0 page, "Summarizing the Breakthrough" (at decode only
+ * the selected blocks are fetched).
+ *
+ * The selected blocks of each (sequence, group) are split over several
+ * workgroups; each writes a partial (max, sum, unnormalised output) per query
+ * head to `workspace`, and a second pass merges them:
+ *     m = max_s m_s,  l = sum_s l_s e^(m_s - m),  out = sum_s o_s e^(m_s - m) / l.
+ * `workspace` (device) must hold bsg_decode_workspace_bytes(dims) bytes.
+ */
+size_t bsg_decode_workspace_bytes(const bsg_dims* dims);
+int bsg_sparse_attn_decode(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
+                           const void* k_cache, const void* v_cache, const int32_t* page_table,
+                           const int32_t* block_idx, float scale, void* workspace,
+                           size_t workspace_bytes, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSG_H */

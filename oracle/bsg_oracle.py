@@ -49,7 +49,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits", "bf16_value", "round_to_cache", "gather_tokens", "block_pool",
-    "query_positions", "group_scores", "select_blocks", "selected_keys",
+    "query_positions", "group_scores", "select_blocks",
     "sparse_attention", "prefill_reference", "decode_reference",
 ]
 
@@ -202,21 +202,6 @@ def select_blocks(scores: np.ndarray, kv_lens: Sequence[int], q_len: int, page_s
 # ----------------------------------------------------------------------------
 # 4. exact attention over the selected blocks
 # ----------------------------------------------------------------------------
-def selected_keys(sel_row: Sequence[int], pos: int, page_size: int) -> np.ndarray:
-    """Key positions a query at ``pos`` attends to: the tokens of its selected
-    blocks, restricted to positions <= pos."""
-    idx = []
-    for j in sel_row:
-        j = int(j)
-        if j < 0:
-            continue
-        lo = j * page_size
-        hi = min(lo + page_size, pos + 1)
-        if hi > lo:
-            idx.append(np.arange(lo, hi))
-    return np.concatenate(idx) if idx else np.zeros((0,), np.int64)
-
-
 def sparse_attention(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, page_table: np.ndarray,
                      kv_lens: Sequence[int], block_idx: np.ndarray, scale: float,
                      t_idx: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
@@ -225,6 +210,7 @@ def sparse_attention(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, pa
     ``block_idx`` [B, Hkv, T, k] for the same ``t_idx``.  For query head h of
     group g = h // G at position p: z_i = (q . k_i) * scale over the selected
     keys i, out = sum_i softmax(z)_i v_i, lse = max z + log(sum exp(z - max z)).
+    Only the pages of the selected blocks are read.
     """
     B, Hq, q_len, D = q.shape
     _, Hkv, bs, _ = k_pages.shape
@@ -235,20 +221,31 @@ def sparse_attention(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, pa
     lse = np.full((B, Hq, T), -np.inf, np.float64)
     for b in range(B):
         L = int(kv_lens[b])
-        K = np.asarray(gather_tokens(k_pages, page_table[b], L), np.float64)   # [Hkv, L, D]
-        V = np.asarray(gather_tokens(v_pages, page_table[b], L), np.float64)
         pos_all = query_positions(L, q_len, tsel)
         for g in range(Hkv):
             for ti in range(T):
-                keys = selected_keys(block_idx[b, g, ti], int(pos_all[ti]), bs)
-                if keys.size == 0:
+                pos = int(pos_all[ti])
+                Ks, Vs = [], []
+                for j in block_idx[b, g, ti]:
+                    j = int(j)
+                    if j < 0:
+                        continue
+                    n = min(bs, pos - j * bs + 1)          # keys of block j at positions <= pos
+                    if n <= 0:
+                        continue
+                    page = int(page_table[b, j])
+                    Ks.append(np.asarray(k_pages[page, g, :n], np.float64))
+                    Vs.append(np.asarray(v_pages[page, g, :n], np.float64))
+                if not Ks:
                     continue
+                K = np.concatenate(Ks)
+                V = np.concatenate(Vs)
                 qh = np.asarray(q[b, g * G:(g + 1) * G, tsel[ti]], np.float64)   # [G, D]
-                z = (qh @ K[g, keys].T) * scale                                  # [G, n]
+                z = (qh @ K.T) * scale                                           # [G, n]
                 m = z.max(axis=1, keepdims=True)
                 w = np.exp(z - m)
                 l = w.sum(axis=1, keepdims=True)
-                out[b, g * G:(g + 1) * G, ti] = (w @ V[g, keys]) / l
+                out[b, g * G:(g + 1) * G, ti] = (w @ V) / l
                 lse[b, g * G:(g + 1) * G, ti] = (m + np.log(l))[:, 0]
     return out, lse
 

@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library is loaded (built first if missing; hipcc cross-compiles for gfx950 without a
+GPU), every symbol that include/bsg.h declares must be exported with C linkage, and the
+host-side argument validation must reject bad calls before anything is launched.  Only
+calls that fail validation, or that are pure host queries, are made here.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_gqa_pool_amd import _lib
+from block_sparse_gqa_pool_amd import build as bld
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsg.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        bld.build()
+    return _lib.lib()
+
+
+def _dims(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=64, top_k=8, num_pages=64,
+                pt_stride=32, dtype=_lib.BSG_BF16)
+    base.update(kw)
+    return _lib.BsgDims(**base)
+
+
+def test_header_declarations_match_exports(L):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(bsg_[a-z_0-9]+)\s*\(", text))
+    assert declared == set(_lib.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (bsg_\w+)$", out, re.M))
+    assert declared <= exported, declared - exported
+    for name in declared:
+        getattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert L.bsg_version() == 10000
+    for st, name in _lib.STATUS.items():
+        assert L.bsg_status_str(st).decode().startswith(name)
+    assert b"unknown" in L.bsg_status_str(7)
+
+
+BAD = ctypes.c_void_p(0x10)  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("dims,expect", [
+    (None, -1),
+    (_dims(num_q_heads=6, num_kv_heads=4), -2),
+    (_dims(batch=0), -2),
+    (_dims(top_k=0), -2),
+    (_dims(head_dim=96), -3),
+    (_dims(page_size=32), -3),
+    (_dims(top_k=65), -3),
+    (_dims(dtype=7), -3),
+])
+def test_validation_of_dims(L, dims, expect):
+    dp = None if dims is None else ctypes.byref(dims)
+    s = None
+    assert L.bsg_block_pool(dp, BAD, BAD, BAD, None, BAD, s) == expect
+    assert L.bsg_group_score(dp, BAD, 4, BAD, BAD, BAD, BAD, 32, s) == expect
+    assert L.bsg_topk_blocks(dp, BAD, 4, 32, BAD, BAD, s) == expect
+    assert L.bsg_group_score_topk(dp, BAD, 4, BAD, BAD, BAD, BAD, BAD, 1 << 30, s) == expect
+    assert L.bsg_sparse_attn_prefill(dp, BAD, 4, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, None, s) == expect
+    assert L.bsg_sparse_attn_decode(dp, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, 1 << 30, BAD, None, s) == expect
+    if dims is not None and expect != 0:
+        assert L.bsg_decode_workspace_bytes(dp) == 0
+        assert L.bsg_group_score_topk_workspace_bytes(dp, 4) == 0
+
+
+def test_validation_of_pointers_and_sizes(L):
+    d = ctypes.byref(_dims())
+    s = None
+    assert L.bsg_block_pool(d, None, BAD, BAD, None, BAD, s) == -1
+    assert L.bsg_block_pool(d, BAD, BAD, None, None, BAD, s) == -1
+    assert L.bsg_group_score(d, BAD, 0, BAD, BAD, BAD, BAD, 32, s) == -2
+    assert L.bsg_group_score(d, BAD, 4, BAD, BAD, BAD, None, 32, s) == -1
+    assert L.bsg_topk_blocks(d, BAD, 4, 0, BAD, BAD, s) == -2
+    assert L.bsg_sparse_attn_prefill(d, BAD, 0, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, None, s) == -2
+    assert L.bsg_sparse_attn_prefill(d, BAD, 4, BAD, BAD, BAD, BAD, BAD, 0.1, None, None, s) == -1
+    # decode: missing or short workspace
+    need = L.bsg_decode_workspace_bytes(d)
+    assert need > 0
+    assert L.bsg_sparse_attn_decode(d, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, None, need, BAD, None, s) == -4
+    assert L.bsg_sparse_attn_decode(d, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, need - 1, BAD, None, s) == -4
+    # decode with G * D beyond what the split kernel holds
+    big = ctypes.byref(_dims(num_q_heads=64, num_kv_heads=2))
+    n2 = L.bsg_decode_workspace_bytes(big)
+    assert L.bsg_sparse_attn_decode(big, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, n2, BAD, None, s) == -3
+
+
+def test_decode_workspace_size_formula(L):
+    for B, Hq, Hkv, D, k in [(32, 32, 4, 128, 32), (4, 64, 8, 128, 32), (1, 8, 2, 64, 4), (3, 16, 16, 64, 1)]:
+        d = _dims(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, top_k=k)
+        n = L.bsg_decode_workspace_bytes(ctypes.byref(d))
+        per_split = B * Hkv * (Hq // Hkv) * (D + 2) * 4
+        assert n % per_split == 0 and 1 <= n // per_split <= k

@@ -1,0 +1,267 @@
+"""GPU parity: each library call against the CPU oracle on the same seeded inputs.
+
+Sizes are reduced versions of the five workloads (same heads, head_dim, block size, top-k,
+planting), large enough to span several tiles and a ragged tail.  Stage tests feed the
+oracle's own intermediate results into one library call; end-to-end tests run the whole
+path on the device and compare selections (bit-exact up to the tie window) and outputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_gqa_pool_amd as bsg
+import oracle as O
+from workloads import SPECS, make_workload
+
+from gpu_util import (check_out, compare_selection, gpu_prefill, note, np_inputs, sample_tokens, to_np)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# reduced shapes of the five workloads (name -> spec)
+SMALL = {
+    "c0_tiny_f32": SPECS[0],
+    "c1_bf16_g8_bs64": SPECS[1].replace(seq_len=4096 + 40),
+    "c3_bf16_g8_bs128": SPECS[3].replace(seq_len=8192 + 77, region=1024, num_q_heads=16, num_kv_heads=2),
+    "c2_decode": SPECS[2].replace(batch=5, ctx_len=64 * 300 + 7),
+    "c4_decode_ragged": SPECS[4].replace(batch=3, ctx_range=(64 * 200, 64 * 700), num_q_heads=16, num_kv_heads=2),
+}
+PREFILL = ["c0_tiny_f32", "c1_bf16_g8_bs64", "c3_bf16_g8_bs128"]
+DECODE = ["c2_decode", "c4_decode_ragged"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded():
+    bsg.lib()
+
+
+def _work(name, seed=7, **kw):
+    note(f"[case] {name} seed={seed} {kw}")
+    spec = SMALL[name].replace(**kw) if kw else SMALL[name]
+    return make_workload(spec, seed).to(DEV)
+
+
+# ---------------------------------------------------------------- block pool
+@pytest.mark.parametrize("name", list(SMALL))
+def test_block_pool_bit_exact(name):
+    spec = SMALL[name]
+    w = make_workload(spec, 3, tail_fill=float("nan")).to(DEV)
+    note(f"[case] block_pool {name}")
+    q, kp, vp, pt, kv = np_inputs(w)
+    ref = O.block_pool(kp, pt, kv, spec.dtype)   # complete blocks never contain the NaN tail slots
+    cache = torch.zeros(kp.shape[0], spec.num_kv_heads, spec.head_dim, dtype=w.k_cache.dtype, device=DEV)
+    bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+    torch.cuda.synchronize()
+    got = to_np(cache)
+    if spec.dtype == "bf16":
+        gb = cache.view(torch.int16).cpu().numpy().view(np.uint16)
+        rb = O.bf16_bits(ref)
+        assert np.array_equal(gb, rb)
+    else:
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_block_pool_incremental_refresh():
+    """Refreshing one completed page per sequence (blk_begin) writes exactly that page."""
+    w = _work("c2_decode")
+    s = w.spec
+    q, kp, vp, pt, kv = np_inputs(w)
+    cache = torch.zeros(kp.shape[0], s.num_kv_heads, s.head_dim, dtype=w.k_cache.dtype, device=DEV)
+    short = torch.tensor([x - 3 * 64 for x in kv], dtype=torch.int32, device=DEV)
+    bsg.block_pool(w.k_cache, w.page_table, short, cache)
+    begin = torch.tensor([(x - 3 * 64) // 64 for x in kv], dtype=torch.int32, device=DEV)
+    bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache, blk_begin=begin)
+    torch.cuda.synchronize()
+    ref = O.block_pool(kp, pt, kv, "bf16")
+    assert np.array_equal(cache.view(torch.int16).cpu().numpy().view(np.uint16), O.bf16_bits(ref))
+
+
+# ---------------------------------------------------------------- scores
+@pytest.mark.parametrize("name", list(SMALL))
+def test_group_score_matches_oracle(name):
+    w = _work(name)
+    s = w.spec
+    q, kp, vp, pt, kv = np_inputs(w)
+    ref_cache = O.block_pool(kp, pt, kv, s.dtype)
+    # the oracle's block cache bytes are the input of this stage
+    cache = torch.from_numpy(ref_cache).to(w.k_cache.dtype).to(DEV)
+    B, Hq, ql, D = w.q.shape
+    sc = torch.empty(B, s.num_kv_heads, ql, w.pt_stride, dtype=torch.float32, device=DEV)
+    bsg.group_score(w.q, w.kv_lens, cache, w.page_table, sc, page_size=s.page_size)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    ref = O.group_scores(q, ref_cache, pt, kv, s.num_kv_heads, s.page_size)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(got))
+    assert np.all(np.isneginf(got[~fin]))
+    err = np.abs(got[fin] - ref[fin])
+    note(f"  score max abs err {err.max() if err.size else 0:.3e}")
+    assert np.all(err <= 1e-5 * np.maximum(np.abs(ref[fin]), 10.0))
+
+
+# ---------------------------------------------------------------- top-k
+def _oracle_scores_f32(name, seed=7):
+    w = _work(name, seed)
+    s = w.spec
+    q, kp, vp, pt, kv = np_inputs(w)
+    cache = O.block_pool(kp, pt, kv, s.dtype)
+    sc = O.group_scores(q, cache, pt, kv, s.num_kv_heads, s.page_size)
+    return w, sc
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_topk_blocks_bit_exact_on_oracle_scores(name):
+    w, sc = _oracle_scores_f32(name)
+    s = w.spec
+    B, Hkv, ql, nb = sc.shape
+    dsc = torch.from_numpy(sc.astype(np.float32)).to(DEV)
+    idx = torch.empty(B, Hkv, ql, s.top_k, dtype=torch.int32, device=DEV)
+    bsg.topk_blocks(dsc, w.kv_lens, idx, page_size=s.page_size)
+    torch.cuda.synchronize()
+    ref = O.select_blocks(sc, w.kv_lens_host, ql, s.page_size, s.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("rows_B,ncand,k", [(2, 3000, 32), (64, 700, 17), (1, 16385, 64), (3, 40, 1), (5, 9, 32)])
+def test_topk_blocks_constructed_ties(rows_B, ncand, k):
+    """Scores drawn from a handful of values (massive exact ties, +-0.0 mixed) -> lower index wins."""
+    rng = np.random.default_rng(ncand)
+    bs = 64
+    kv = [ncand * bs + 1 + b for b in range(rows_B)]              # decode rows; own = ncand
+    sc = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 2.0, 2.0000002], np.float32), size=(rows_B, 2, 1, ncand + 1))
+    sc[..., ncand:] = -np.inf
+    note(f"[case] ties B={rows_B} ncand={ncand} k={k}")
+    dsc = torch.from_numpy(sc).to(DEV)
+    kvl = torch.tensor(kv, dtype=torch.int32, device=DEV)
+    idx = torch.empty(rows_B, 2, 1, k, dtype=torch.int32, device=DEV)
+    bsg.topk_blocks(dsc, kvl, idx, page_size=bs)
+    torch.cuda.synchronize()
+    ref = O.select_blocks(sc.astype(np.float64), kv, 1, bs, k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------- attention stages
+def _prefill_stage(w, top_k, scale=None):
+    s = w.spec
+    q, kp, vp, pt, kv = np_inputs(w)
+    D = s.head_dim
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    cache = O.block_pool(kp, pt, kv, s.dtype)
+    ql = w.q.shape[2]
+    tsel = None if ql <= 2048 else sample_tokens(ql, s.page_size, 300)
+    sc = O.group_scores(q, cache, pt, kv, s.num_kv_heads, s.page_size, tsel)
+    idx = O.select_blocks(sc, kv, ql, s.page_size, top_k, tsel)
+    # the device needs a full block_idx: the oracle's rows where sampled, full oracle otherwise
+    if tsel is not None:
+        sc_all = O.group_scores(q, cache, pt, kv, s.num_kv_heads, s.page_size)
+        idx_all = O.select_blocks(sc_all, kv, ql, s.page_size, top_k)
+    else:
+        idx_all = idx
+    ref_out, ref_lse = O.sparse_attention(q, kp, vp, pt, kv, idx, scale, tsel)
+    didx = torch.from_numpy(idx_all).to(DEV)
+    out = torch.empty_like(w.q)
+    lse = torch.empty(w.q.shape[:3], dtype=torch.float32, device=DEV)
+    bsg.sparse_attn_prefill(w.q, w.kv_lens, w.k_cache, w.v_cache, w.page_table, didx, scale, out, lse)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    gl = lse.cpu().numpy()
+    if tsel is not None:
+        got, gl = got[:, :, tsel], gl[:, :, tsel]
+    return got, gl, ref_out, ref_lse
+
+
+@pytest.mark.parametrize("name", PREFILL)
+def test_prefill_attention_on_oracle_selection(name):
+    w = make_workload(SMALL[name], 11, tail_fill=float("nan")).to(DEV)
+    note(f"[case] prefill attention {name}")
+    got, gl, ref, rl = _prefill_stage(w, w.spec.top_k)
+    check_out(got, ref, w.spec.dtype, "out")
+    tol = 2e-3 if w.spec.dtype == "bf16" else 1e-4
+    assert np.abs(gl - rl).max() <= tol
+
+
+@pytest.mark.parametrize("case", [
+    dict(top_k=1),                                   # block-local causal attention
+    dict(top_k=64),                                  # every block: dense causal
+    dict(num_q_heads=4, num_kv_heads=4),             # G = 1
+    dict(num_q_heads=8, num_kv_heads=4),             # G = 2
+    dict(num_q_heads=16, num_kv_heads=4),            # G = 4
+    dict(num_q_heads=64, num_kv_heads=4),            # G = 16
+    dict(num_q_heads=24, num_kv_heads=4),            # G = 6 (not a power of two)
+    dict(head_dim=64),
+    dict(page_size=128, top_k=5),
+    dict(q_len=333),                                 # queries over an existing prefix
+    dict(batch=3),
+])
+def test_prefill_attention_edge_shapes(case):
+    spec = SPECS[1].replace(seq_len=64 * 24 + 13, **case)
+    note(f"[case] prefill edge {case}")
+    w = make_workload(spec, 5, tail_fill=float("nan")).to(DEV)
+    got, gl, ref, rl = _prefill_stage(w, spec.top_k)
+    check_out(got, ref, "bf16", f"out {case}")
+    assert np.abs(gl - rl).max() <= 2e-3
+
+
+@pytest.mark.parametrize("name", DECODE)
+def test_decode_attention_on_oracle_selection(name):
+    w = make_workload(SMALL[name], 13, tail_fill=float("nan")).to(DEV)
+    note(f"[case] decode attention {name}")
+    s = w.spec
+    q, kp, vp, pt, kv = np_inputs(w)
+    scale = 1.0 / math.sqrt(s.head_dim)
+    r = O.decode_reference(q, kp, vp, pt, kv, s.page_size, s.top_k, s.dtype, scale)
+    didx = torch.from_numpy(r["block_idx"][:, :, 0]).contiguous().to(DEV)
+    B, Hq = w.q.shape[:2]
+    out = torch.empty(B, Hq, s.head_dim, dtype=w.q.dtype, device=DEV)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+    bsg.sparse_attn_decode(w.q[:, :, 0].contiguous(), w.kv_lens, w.k_cache, w.v_cache, w.page_table, didx, scale,
+                           out, lse)
+    torch.cuda.synchronize()
+    check_out(to_np(out), r["out"][:, :, 0], s.dtype, "decode out")
+    assert np.abs(lse.cpu().numpy() - r["lse"][:, :, 0]).max() <= 2e-3
+
+
+# ---------------------------------------------------------------- end to end
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name", PREFILL)
+def test_prefill_end_to_end(name, fused):
+    w = _work(name, seed=21)
+    s = w.spec
+    g = gpu_prefill(w, s.top_k, fused=fused)
+    q, kp, vp, pt, kv = np_inputs(w)
+    r = O.prefill_reference(q, kp, vp, pt, kv, s.page_size, s.top_k, s.dtype)
+    assert np.array_equal(to_np(g["block_cache"]), r["block_cache"])
+    gi = g["block_idx"].cpu().numpy()
+    bad, exempt = compare_selection(gi, r["block_idx"], r["scores"], s.top_k)
+    note(f"  selection rows: {gi.shape[0] * gi.shape[1] * gi.shape[2]}, exempt ties {len(exempt)}, bad {len(bad)}")
+    assert not bad, bad[:10]
+    same = ~(gi != r["block_idx"]).any(-1)                       # [B, Hkv, T]
+    G = s.group_size
+    rows = np.repeat(same, G, axis=1)                            # per query head
+    check_out(to_np(g["out"])[rows], r["out"][rows], s.dtype, "out")
+
+
+@pytest.mark.parametrize("name", DECODE)
+def test_decode_end_to_end(name):
+    w = _work(name, seed=23)
+    s = w.spec
+    B, Hq, _, D = w.q.shape
+    scale = 1.0 / math.sqrt(D)
+    cache = torch.zeros(w.k_cache.shape[0], s.num_kv_heads, D, dtype=w.k_cache.dtype, device=DEV)
+    bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+    idx = torch.empty(B, s.num_kv_heads, 1, s.top_k, dtype=torch.int32, device=DEV)
+    bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, idx, page_size=s.page_size)
+    out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
+    bsg.sparse_attn_decode(w.q[:, :, 0].contiguous(), w.kv_lens, w.k_cache, w.v_cache, w.page_table,
+                           idx[:, :, 0].contiguous(), scale, out)
+    torch.cuda.synchronize()
+    q, kp, vp, pt, kv = np_inputs(w)
+    r = O.decode_reference(q, kp, vp, pt, kv, s.page_size, s.top_k, s.dtype, scale)
+    gi = idx.cpu().numpy()
+    bad, exempt = compare_selection(gi, r["block_idx"], r["scores"], s.top_k)
+    note(f"  exempt ties {len(exempt)}, bad {len(bad)}")
+    assert not bad, bad
+    check_out(to_np(out), r["out"][:, :, 0], s.dtype, "decode out")
