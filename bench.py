@@ -1,0 +1,307 @@
+"""Benchmark: block-sparse GQA attention at 128K context on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  prefill workload: block_pool -> group_score_topk -> sparse_attn_prefill
+  decode workload:  group_score_topk -> sparse_attn_decode (block cache built beforehand)
+Inputs are generated on the GPU and resident in HBM before timing starts.  The default
+workload is the 128K prefill (B=1, S=131072, Hq=64, Hkv=8, D=128, 128-token blocks,
+top-16); the 128K decode step (B=32, context 131072, Hq=32, Hkv=4, 64-token pages,
+top-32) is measured in the same run and reported under "decode".
+
+Prints ONE JSON line.  `value` is prefill tokens/s (or decode steps/s-free us/step for
+--workload decode).  `roofline` covers the dominant kernel of the step, timed with HIP
+events on the stream the library launches on; its algorithmic work is counted from the
+actual selection (4*D FLOPs per selected, causally valid key per query head for prefill;
+selected K+V bytes + block-cache bytes + page-table bytes for decode).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse GQA attn: prefill tok/s + decode µs/step at 128K, % roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def _kernel_hash(*files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "block_sparse_gqa_pool_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key: str, src_files) -> float | None:
+    """HBM bytes per launch from a committed counter summary, if it matches the current source."""
+    path = os.path.join(PROFILE_DIR, f"{kernel_key}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != _kernel_hash(*src_files):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------
+def prefill_flops(block_idx, kv_lens, q_len, page_size, G, D):
+    """4*D FLOPs per (query head, selected key at a position <= the query)."""
+    import torch
+    B, Hkv, T, k = block_idx.shape
+    pos = (kv_lens.view(B, 1, 1, 1).long() - q_len + torch.arange(T, device=block_idx.device).view(1, 1, T, 1))
+    j = block_idx.long()
+    n = torch.clamp(pos - j * page_size + 1, min=0, max=page_size)
+    n = torch.where(j >= 0, n, torch.zeros_like(n))
+    return float(n.sum().item()) * G * 4 * D
+
+
+def decode_bytes(block_idx, kv_lens, page_size, Hkv, D, elem=2):
+    """Selected K+V bytes + block-cache bytes of every candidate + page-table bytes."""
+    import torch
+    B = block_idx.shape[0]
+    pos = kv_lens.view(B, 1, 1).long() - 1
+    j = block_idx.view(B, Hkv, -1).long()
+    n = torch.clamp(pos - j * page_size + 1, min=0, max=page_size)
+    n = torch.where(j >= 0, n, torch.zeros_like(n))
+    kv = float(n.sum().item()) * D * elem * 2
+    own = (kv_lens.long() - 1) // page_size
+    reps = float(own.sum().item()) * Hkv * D * elem
+    pt = float((own + 1).sum().item()) * 4
+    return kv + reps + pt, dict(selected_kv=kv, block_cache=reps, page_table=pt)
+
+
+# ------------------------------------------------------------------------------------
+def run_prefill(spec, seed, steps, warmup):
+    import torch
+    import block_sparse_gqa_pool_amd as bsg
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    w = make_workload(spec, seed, device=dev)
+    B, Hq, S, D = w.q.shape
+    Hkv, bs, k = spec.num_kv_heads, spec.page_size, spec.top_k
+    scale = 1.0 / math.sqrt(D)
+    cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
+    idx = torch.empty(B, Hkv, S, k, dtype=torch.int32, device=dev)
+    out = torch.empty_like(w.q)
+    need = bsg.group_score_topk_workspace_bytes(w.q, cache, w.page_table, bs, k)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+        if ev:
+            ev[1].record(stream)
+        bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, idx, page_size=bs, workspace=ws)
+        if ev:
+            ev[2].record(stream)
+        bsg.sparse_attn_prefill(w.q, w.kv_lens, w.k_cache, w.v_cache, w.page_table, idx, scale, out)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(3)]
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    flops = prefill_flops(idx, w.kv_lens, S, bs, spec.group_size, D)
+    res = dict(
+        tokens=B * S, wall_s=wall, ms_per_step=sum(step_ms) / steps, wall_ms_per_step=1e3 * wall / steps,
+        stage_ms={n: sum(v) / steps for n, v in zip(("block_pool", "group_score_topk", "sparse_attn_prefill"), stage)},
+        attn_flops=flops,
+    )
+    del w, cache, idx, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_decode(spec, seed, steps, warmup):
+    import torch
+    import block_sparse_gqa_pool_amd as bsg
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    w = make_workload(spec, seed, device=dev)
+    B, Hq, _, D = w.q.shape
+    Hkv, bs, k = spec.num_kv_heads, spec.page_size, spec.top_k
+    scale = 1.0 / math.sqrt(D)
+    cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
+    bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)        # built at prefill (untimed)
+    idx = torch.empty(B, Hkv, 1, k, dtype=torch.int32, device=dev)
+    q1 = w.q[:, :, 0].contiguous()
+    out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=dev)
+    need = bsg.group_score_topk_workspace_bytes(w.q, cache, w.page_table, bs, k)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    dws = torch.empty(bsg.decode_workspace_bytes(w.k_cache, w.page_table, Hq, k), dtype=torch.uint8, device=dev)
+    idx3 = idx.view(B, Hkv, k)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, idx, page_size=bs, workspace=ws)
+        if ev:
+            ev[1].record(stream)
+        bsg.sparse_attn_decode(q1, w.kv_lens, w.k_cache, w.v_cache, w.page_table, idx3, scale, out, workspace=dws)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    score_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
+    nbytes, parts = decode_bytes(idx, w.kv_lens, bs, Hkv, D)
+    res = dict(us_per_step=1e3 * step_ms, wall_us_per_step=1e6 * wall / steps,
+               stage_us=dict(group_score_topk=1e3 * score_ms, sparse_attn_decode=1e3 * attn_ms),
+               bytes=nbytes, bytes_parts=parts)
+    del w, cache, idx, out, ws, dws
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------------------------
+def cpu_baseline_prefill(spec, seed, n_tokens):
+    """The CPU oracle on a bounded sample of the same workload (one BLAS thread)."""
+    import numpy as np
+    import torch
+    import oracle as O
+    from workloads import make_workload
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    w = make_workload(spec, seed, device="cuda:0" if torch.cuda.is_available() else "cpu")
+    q = w.q.float().cpu().numpy()
+    kp = w.k_cache.float().cpu().numpy()
+    vp = w.v_cache.float().cpu().numpy()
+    pt = w.page_table.cpu().numpy()
+    kv = list(w.kv_lens_host)
+    del w
+    torch.cuda.empty_cache()
+    S = q.shape[2]
+    rng = np.random.default_rng(0)
+    tsel = np.sort(rng.choice(S, size=n_tokens, replace=False))
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        t0 = time.perf_counter()
+        cache = O.block_pool(kp, pt, kv, spec.dtype)
+        t1 = time.perf_counter()
+        sc = O.group_scores(q, cache, pt, kv, spec.num_kv_heads, spec.page_size, tsel)
+        idx = O.select_blocks(sc, kv, S, spec.page_size, spec.top_k, tsel)
+        O.sparse_attention(q, kp, vp, pt, kv, idx, 1.0 / math.sqrt(spec.head_dim), tsel)
+        t2 = time.perf_counter()
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    per_tok = (t2 - t1) / n_tokens
+    est = (t1 - t0) + per_tok * S
+    return dict(value=S / est, unit="tok/s", cores=1, kind="oracle",
+                sample=(f"block_pool over all {pt.shape[1]} blocks ({t1 - t0:.1f} s) + scores, top-k and "
+                        f"attention for {n_tokens} random query tokens ({t2 - t1:.1f} s), extrapolated "
+                        f"linearly to all {S} tokens: {est:.0f} s per prefill"),
+                seconds=t2 - t0)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_bf16_s131072")
+    ap.add_argument("--decode-workload", default="decode_bf16_b32_ctx131072")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--seed", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library has no multi-GPU path; "
+              "sharding would split KV heads or sequences across GPUs with no exchange.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_gqa_pool_amd as bsg
+    from workloads import SPECS, spec_by_name
+
+    bsg.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    spec = spec_by_name(args.workload)
+    seed = args.seed if args.seed is not None else SPECS.index(spec)
+
+    line = {"metric": METRIC}
+    if spec.mode == "prefill":
+        r = run_prefill(spec, seed, args.steps, args.warmup)
+        tok_s = r["tokens"] / (r["ms_per_step"] / 1e3)
+        attn_ms = r["stage_ms"]["sparse_attn_prefill"]
+        achieved = r["attn_flops"] / (attn_ms / 1e3) / 1e12
+        line.update(value=tok_s, unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                    ms_per_step=r["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None,
+                    dtype="bf16", data="synthetic (seeded planted-block generator)",
+                    config={"workload": spec.name, "batch": spec.batch, "seq_len": spec.seq_len,
+                            "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+                            "head_dim": spec.head_dim, "block_size": spec.page_size, "top_k": spec.top_k},
+                    roofline={"kernel": "sparse_attn_prefill", "bound": "mfma", "achieved": achieved,
+                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                              "traffic": _traffic("sparse_attn_prefill_s131072", ["attn_prefill.hip"]),
+                              "flops_per_launch": r["attn_flops"], "avg_launch_ms": attn_ms},
+                    stages_ms=r["stage_ms"], wall_ms_per_step=r["wall_ms_per_step"],
+                    pipeline_mfma_frac=(r["attn_flops"] / (r["ms_per_step"] / 1e3) / 1e12) / PEAK_BF16_TFLOPS)
+        dspec = spec_by_name(args.decode_workload)
+        d = run_decode(dspec, SPECS.index(dspec), max(args.steps, 20), args.warmup)
+        gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9
+        line["decode"] = {"workload": dspec.name, "us_per_step": d["us_per_step"], "stages_us": d["stage_us"],
+                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": d["bytes"],
+                                       "bytes_parts": d["bytes_parts"]},
+                          "wall_us_per_step": d["wall_us_per_step"]}
+    else:
+        d = run_decode(spec, seed, args.steps, args.warmup)
+        gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9
+        line.update(value=d["us_per_step"], unit="us/step", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                    ms_per_step=d["us_per_step"] / 1e3, higher_is_better=False, scaling="weak", vs_baseline=None,
+                    dtype="bf16", data="synthetic (seeded planted-block generator)",
+                    config={"workload": spec.name, "batch": spec.batch, "num_q_heads": spec.num_q_heads,
+                            "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+                            "block_size": spec.page_size, "top_k": spec.top_k},
+                    roofline={"kernel": "decode step", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                              "bytes_per_step": d["bytes"]},
+                    stages_us=d["stage_us"])
+    if not args.no_cpu_baseline and spec.mode == "prefill":
+        line["cpu_baseline"] = cpu_baseline_prefill(spec, seed, args.cpu_tokens)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -265,3 +265,29 @@ def test_decode_end_to_end(name):
     note(f"  exempt ties {len(exempt)}, bad {len(bad)}")
     assert not bad, bad
     check_out(to_np(out), r["out"][:, :, 0], s.dtype, "decode out")
+
+
+@pytest.mark.parametrize("case", [
+    dict(top_k=1), dict(top_k=2), dict(top_k=64), dict(top_k=33),
+    dict(num_q_heads=4, num_kv_heads=4), dict(num_q_heads=16, num_kv_heads=4), dict(num_q_heads=24, num_kv_heads=4),
+    dict(head_dim=64), dict(page_size=128, top_k=5), dict(q_len=333), dict(batch=3), dict(seq_len=64 * 3 + 1),
+])
+def test_fused_selection_edge_shapes(case):
+    """Fused score + top-k against the oracle's selection (tie window) on edge shapes."""
+    kw = dict(seq_len=64 * 40 + 13)
+    kw.update(case)
+    spec = SPECS[1].replace(**kw)
+    note(f"[case] fused selection {case}")
+    w = make_workload(spec, 8).to(DEV)
+    q, kp, vp, pt, kv = np_inputs(w)
+    cache = O.block_pool(kp, pt, kv, "bf16")
+    sc = O.group_scores(q, cache, pt, kv, spec.num_kv_heads, spec.page_size)
+    ref = O.select_blocks(sc, kv, w.q.shape[2], spec.page_size, spec.top_k)
+    dcache = torch.from_numpy(cache).to(torch.bfloat16).to(DEV)
+    B, Hq, ql, D = w.q.shape
+    idx = torch.empty(B, spec.num_kv_heads, ql, spec.top_k, dtype=torch.int32, device=DEV)
+    bsg.group_score_topk(w.q, w.kv_lens, dcache, w.page_table, idx, page_size=spec.page_size)
+    torch.cuda.synchronize()
+    bad, exempt = compare_selection(idx.cpu().numpy(), ref, sc, spec.top_k)
+    note(f"  exempt {len(exempt)} bad {len(bad)}")
+    assert not bad, bad[:5]
