@@ -4,7 +4,7 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input:
   prefill workload: block_pool -> group_score_topk -> sparse_attn_prefill
-  decode workload:  group_score_topk -> sparse_attn_decode (block cache built beforehand)
+  decode workload:  decode_step = group scores + top-k + sparse attention (block cache built beforehand)
 Inputs are generated on the GPU and resident in HBM before timing starts.  The default
 workload is the 128K prefill (B=1, S=131072, Hq=64, Hkv=8, D=128, 128-token blocks,
 top-16); the 128K decode step (B=32, context 131072, Hq=32, Hkv=4, 64-token pages,
@@ -148,23 +148,18 @@ def run_decode(spec, seed, steps, warmup):
     scale = 1.0 / math.sqrt(D)
     cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
     bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)        # built at prefill (untimed)
-    idx = torch.empty(B, Hkv, 1, k, dtype=torch.int32, device=dev)
+    idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
     q1 = w.q[:, :, 0].contiguous()
     out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=dev)
-    need = bsg.group_score_topk_workspace_bytes(w.q, cache, w.page_table, bs, k)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    dws = torch.empty(bsg.decode_workspace_bytes(w.k_cache, w.page_table, Hq, k), dtype=torch.uint8, device=dev)
-    idx3 = idx.view(B, Hkv, k)
+    ws = torch.empty(bsg.decode_step_workspace_bytes(w.k_cache, w.page_table, Hq, k), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, idx, page_size=bs, workspace=ws)
+        bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx, out, workspace=ws)
         if ev:
             ev[1].record(stream)
-        bsg.sparse_attn_decode(q1, w.kv_lens, w.k_cache, w.v_cache, w.page_table, idx3, scale, out, workspace=dws)
-        if ev:
             ev[2].record(stream)
 
     for _ in range(warmup):
@@ -176,14 +171,10 @@ def run_decode(spec, seed, steps, warmup):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    score_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
     nbytes, parts = decode_bytes(idx, w.kv_lens, bs, Hkv, D)
-    res = dict(us_per_step=1e3 * step_ms, wall_us_per_step=1e6 * wall / steps,
-               stage_us=dict(group_score_topk=1e3 * score_ms, sparse_attn_decode=1e3 * attn_ms),
-               bytes=nbytes, bytes_parts=parts)
-    del w, cache, idx, out, ws, dws
+    res = dict(us_per_step=1e3 * step_ms, wall_us_per_step=1e6 * wall / steps, bytes=nbytes, bytes_parts=parts)
+    del w, cache, idx, out, ws
     torch.cuda.empty_cache()
     return res
 
@@ -278,7 +269,7 @@ def main():
         dspec = spec_by_name(args.decode_workload)
         d = run_decode(dspec, SPECS.index(dspec), max(args.steps, 20), args.warmup)
         gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9
-        line["decode"] = {"workload": dspec.name, "us_per_step": d["us_per_step"], "stages_us": d["stage_us"],
+        line["decode"] = {"workload": dspec.name, "us_per_step": d["us_per_step"], "api": "bsg_decode_step",
                           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                        "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": d["bytes"],
                                        "bytes_parts": d["bytes_parts"]},
@@ -294,8 +285,7 @@ def main():
                             "block_size": spec.page_size, "top_k": spec.top_k},
                     roofline={"kernel": "decode step", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None,
-                              "bytes_per_step": d["bytes"]},
-                    stages_us=d["stage_us"])
+                              "bytes_per_step": d["bytes"]})
     if not args.no_cpu_baseline and spec.mode == "prefill":
         line["cpu_baseline"] = cpu_baseline_prefill(spec, seed, args.cpu_tokens)
     else:

@@ -23,7 +23,8 @@ STATUS = {0: "BSG_OK", -1: "BSG_ERR_NULL", -2: "BSG_ERR_SHAPE", -3: "BSG_ERR_UNS
 # every symbol include/bsg.h declares
 EXPORTS = ("bsg_version", "bsg_status_str", "bsg_block_pool", "bsg_group_score", "bsg_topk_blocks",
            "bsg_group_score_topk_workspace_bytes", "bsg_group_score_topk", "bsg_sparse_attn_prefill",
-           "bsg_decode_workspace_bytes", "bsg_sparse_attn_decode")
+           "bsg_decode_workspace_bytes", "bsg_sparse_attn_decode", "bsg_decode_step_workspace_bytes",
+           "bsg_decode_step")
 
 
 class BsgDims(ctypes.Structure):
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
             "bsg_sparse_attn_prefill": ([dp, vp, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp], ctypes.c_int),
             "bsg_decode_workspace_bytes": ([dp], sz),
             "bsg_sparse_attn_decode": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp, vp], ctypes.c_int),
+            "bsg_decode_step_workspace_bytes": ([dp], sz),
+            "bsg_decode_step": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -241,6 +244,7 @@ def sparse_attn_prefill(q, kv_lens, k_cache, v_cache, page_table, block_idx, sca
 
 
 def decode_workspace_bytes(k_cache, page_table, num_q_heads: int, top_k: int) -> int:
+    """Bytes of the decode workspace (no initialisation needed)."""
     d = dims(k_cache, page_table, num_q_heads, top_k)
     return int(lib().bsg_decode_workspace_bytes(ctypes.byref(d)))
 
@@ -275,4 +279,44 @@ def sparse_attn_decode(q, kv_lens, k_cache, v_cache, page_table, block_idx, scal
         ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(block_idx),
         float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
         _stream(stream)))
+    return out
+
+
+def decode_step_workspace_bytes(k_cache, page_table, num_q_heads: int, top_k: int) -> int:
+    d = dims(k_cache, page_table, num_q_heads, top_k)
+    return int(lib().bsg_decode_step_workspace_bytes(ctypes.byref(d)))
+
+
+def decode_step(q, kv_lens, block_cache, k_cache, v_cache, page_table, scale: float, block_idx, out, lse=None,
+                workspace=None, stream=None):
+    """bsg_decode_step: q [B, Hq, D] -> out [B, Hq, D]; the selection goes to block_idx [B, Hkv, top_k]."""
+    _req(k_cache, "k_cache", None, 4)
+    dev = k_cache.device
+    _req(v_cache, "v_cache", k_cache.dtype, 4, dev)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    _req(block_cache, "block_cache", k_cache.dtype, 3, dev)
+    P, Hkv, bs, D = k_cache.shape
+    if tuple(block_cache.shape) != (P, Hkv, D):
+        raise ValueError("block_cache must be [num_pages, Hkv, D]")
+    _req(q, "q", k_cache.dtype, 3, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(block_idx, "block_idx", torch.int32, 3, dev)
+    _req(out, "out", k_cache.dtype, 3, dev)
+    B, Hq, D2 = q.shape
+    if out.shape != q.shape or D2 != D or page_table.shape[0] != B or tuple(block_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("shape mismatch between q, out, caches, page_table and block_idx")
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 2, dev)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
+    d = dims(k_cache, page_table, Hq, block_idx.shape[2])
+    need = int(lib().bsg_decode_step_workspace_bytes(ctypes.byref(d)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _req(workspace, "workspace", None, None, dev)
+    _check("bsg_decode_step", lib().bsg_decode_step(
+        ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(block_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        float(scale), _ptr(block_idx), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _ptr(lse), _stream(stream)))
     return out

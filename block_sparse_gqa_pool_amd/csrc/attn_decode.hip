@@ -153,6 +153,293 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const float* __res
   if (lse && d == 0) lse[(size_t)b * Hq + h] = m + logf(l);
 }
 
+// ---------------------------------------------------------------------------------------
+// bf16 matrix-core path (G <= 16).  Each wave takes `ppw` selected pages of one (sequence,
+// group) and runs, per 64-key sub-block,
+//   S^T (16 keys x 16 heads) = K (keys x D) . Q^T (D x heads)    A = K rows straight from HBM
+//   O^T (16 d x 16 heads)   += V^T (d x 32 keys) . P^T (keys x heads)   A = V^T from LDS via
+//                                                                  ds_read_b64_tr_b16
+// with v_mfma_f32_16x16x32_bf16 (heads beyond G are zero columns).  A head's scores sit in
+// the four lanes with the same lane % 16, so the online softmax needs two shuffles.  The
+// four waves of a workgroup merge in LDS and the workgroup writes one partial per head;
+// attn_decode_merge_kernel then merges the workgroups.
+namespace {
+constexpr int DM_VPAD = 16;
+}
+
+typedef __attribute__((address_space(3))) s16x4_t* dm_lds_s16x4_ptr;
+
+// Selection prologue of the fused decode step (one workgroup, all threads).  `lists` holds,
+// per chunk of candidate blocks, the chunk's best m = top_k - 1 keys sorted descending (0 =
+// none).  The cnt-th largest of the chunks' first T keys is a lower bound `tau` of the
+// cnt-th largest key overall (at least cnt keys reach it), so the kept keys are among the
+// list keys >= tau -- typically little more than cnt of them.  Those survivors are ranked
+// against each other; ranks below cnt are kept.  wl receives the kept block ids ascending.
+__device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, int nchunks, int m, int T, int cnt,
+                                       uint64_t* L, uint64_t* S, int* selj, int* wl, int* counters,
+                                       uint64_t* tau_s) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < nchunks * m; e += 256) L[e] = lists_row[e];
+  if (tid == 0) {
+    counters[0] = 0;   // valid tops
+    counters[1] = 0;   // survivors
+    *tau_s = 1ull;
+  }
+  __syncthreads();
+  const int NT = nchunks * T;
+  for (int e = tid; e < NT; e += 256)
+    if (L[(e / T) * m + (e % T)] != 0ull) atomicAdd(&counters[0], 1);
+  __syncthreads();
+  if (counters[0] >= cnt) {
+    for (int e = tid; e < NT; e += 256) {
+      const uint64_t key = L[(e / T) * m + (e % T)];
+      if (key == 0ull) continue;
+      int rank = 0;
+      for (int e2 = 0; e2 < NT; e2++) rank += L[(e2 / T) * m + (e2 % T)] > key ? 1 : 0;
+      if (rank == cnt - 1) *tau_s = key;
+    }
+  }
+  __syncthreads();
+  const uint64_t tau = *tau_s;
+  for (int c = tid; c < nchunks; c += 256) {
+    for (int i = 0; i < m; i++) {
+      const uint64_t key = L[c * m + i];
+      if (key < tau) break;
+      S[atomicAdd(&counters[1], 1)] = key;
+    }
+  }
+  __syncthreads();
+  const int ns = counters[1];
+  for (int e = tid; e < ns; e += 256) {
+    const uint64_t key = S[e];
+    int rank = 0;
+    for (int e2 = 0; e2 < ns; e2++) rank += S[e2] > key ? 1 : 0;
+    if (rank < cnt) selj[rank] = sel_key_index(key);
+  }
+  __syncthreads();
+  if (tid < cnt) {
+    const int ji = selj[tid];
+    int r = 0;
+    for (int i = 0; i < cnt; i++) r += selj[i] < ji ? 1 : 0;
+    wl[r] = ji;
+  }
+  __syncthreads();
+}
+
+template <int D, int BS, bool FUSED>
+__global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
+    const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table, int32_t* __restrict__ block_idx,
+    const uint64_t* __restrict__ lists, float scale, float* __restrict__ part, int Hq, int Hkv, int top_k,
+    int num_pages, int pt_stride, int nwg, int ppw, int nchunks, int T) {
+  constexpr int NDS = D / 32;          // k-steps of the score product
+  constexpr int NDT = D / 16;          // 16-wide d tiles of the output
+  constexpr int VS = D + DM_VPAD;      // LDS row stride of V (elements)
+  constexpr int SUB = 64;              // keys per sub-block
+  extern __shared__ __attribute__((aligned(16))) unsigned char dm_smem[];
+  const int G = Hq / Hkv;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, qd = lane >> 4;
+  bf16_t* Vs = reinterpret_cast<bf16_t*>(dm_smem) + (size_t)wave * SUB * VS;
+  const int L = kv_lens[b];
+  const int pos = L - 1;
+  int32_t* sl = block_idx + ((size_t)b * Hkv + g) * top_k;
+  const float c2 = scale * 1.4426950408889634f;
+  __shared__ int wl[64];          // fused: the selection, ascending, own block last
+  __shared__ int selj[64];
+  __shared__ int cnts[2];
+  __shared__ uint64_t tau_s;
+  if (FUSED) {
+    const int m = top_k - 1;
+    const int own = max(pos, 0) / BS;
+    const int cnt = min(m, min(own, pt_stride));
+    if (cnt > 0) {
+      uint64_t* Lk = reinterpret_cast<uint64_t*>(dm_smem);
+      decode_select_prologue(lists + ((size_t)b * Hkv + g) * nchunks * m, nchunks, m, T, cnt, Lk,
+                             Lk + (size_t)nchunks * m, selj, wl, cnts, &tau_s);
+    }
+    if (tid == 0) wl[cnt] = own;
+    for (int i = cnt + 1 + tid; i < top_k; i += 256) wl[i] = -1;
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = tid; i < top_k; i += 256) sl[i] = wl[i];
+  }
+
+  bf16x8_t qb[NDS];
+  {
+    const bool hv = n < G;
+    const bf16_t* qp = q + ((size_t)b * Hq + (size_t)g * G + (hv ? n : 0)) * D + 8 * qd;
+#pragma unroll
+    for (int s = 0; s < NDS; s++) {
+      uint4 v = hv ? *reinterpret_cast<const uint4*>(qp + 32 * s) : make_uint4(0, 0, 0, 0);
+      qb[s] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; i++) o[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int vtr = (16 * 0 + 4 * qd + ((lane & 15) >> 2)) * VS + 4 * (lane & 3);   // tr-read base (key, d)
+
+  const int e0 = (blockIdx.x * 4 + wave) * ppw;
+  const int e1 = min(e0 + ppw, top_k);
+  for (int e = e0; e < e1; e++) {
+    const int j = FUSED ? wl[e] : sl[e];
+    if (j < 0) break;
+    const int jj = clampi(j, 0, pt_stride - 1);
+    const int p = clampi(page_table[(size_t)b * pt_stride + jj], 0, num_pages - 1);
+    const int nk = clampi(pos - jj * BS + 1, 0, BS);
+    const bf16_t* kp = k_cache + (((size_t)p * Hkv + g) * BS) * D;
+    const bf16_t* vp = v_cache + (((size_t)p * Hkv + g) * BS) * D;
+#pragma unroll
+    for (int h2 = 0; h2 < BS / SUB; h2++) {
+      const int kb = h2 * SUB;
+      if (kb >= nk) break;
+      // V sub-block -> this wave's LDS rows (rows past nk are zero)
+      constexpr int PPR = D / 8;
+      uint4 vr[SUB * PPR / 64];
+#pragma unroll
+      for (int i = 0; i < SUB * PPR / 64; i++) {
+        const int pc = i * 64 + lane;
+        const int r = pc / PPR, c = pc % PPR;
+        vr[i] = (kb + r < nk) ? *reinterpret_cast<const uint4*>(vp + (size_t)(kb + r) * D + 8 * c)
+                              : make_uint4(0, 0, 0, 0);
+      }
+      // scores: S^T tiles of 16 keys
+      f32x4_t sacc[SUB / 16];
+#pragma unroll
+      for (int T = 0; T < SUB / 16; T++) {
+        sacc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const bf16_t* kr = kp + (size_t)(kb + 16 * T + n) * D + 8 * qd;
+#pragma unroll
+        for (int s = 0; s < NDS; s++) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(kr + 32 * s);
+          sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(&kv), qb[s], sacc[T],
+                                                              0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < SUB * PPR / 64; i++) {
+        const int pc = i * 64 + lane;
+        const int r = pc / PPR, c = pc % PPR;
+        *reinterpret_cast<uint4*>(Vs + r * VS + 8 * c) = vr[i];
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < SUB / 16; T++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int key = kb + 16 * T + 4 * qd + i;
+          const float sv = key < nk ? sacc[T][i] : -INFINITY;
+          sacc[T][i] = sv;
+          mx = fmaxf(mx, sv);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      m_run = m_new;
+      float rs = 0.0f;
+#pragma unroll
+      for (int T = 0; T < SUB / 16; T++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float pe = __builtin_amdgcn_exp2f((sacc[T][i] - m_use) * c2);
+          sacc[T][i] = pe;
+          rs += pe;
+        }
+      l_run = l_run * alpha + rs;
+#pragma unroll
+      for (int i = 0; i < NDT; i++) o[i] *= alpha;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int k2 = 0; k2 < SUB / 32; k2++) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          pb[i] = (__bf16)sacc[2 * k2][i];
+          pb[4 + i] = (__bf16)sacc[2 * k2 + 1][i];
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+          const bf16_t* vb = Vs + vtr + (32 * k2) * VS + 16 * dt;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb + 16 * VS));
+          bf16x8_t va;
+          *reinterpret_cast<s16x4_t*>(&va) = lo;
+          *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[dt], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  // per-head sum over the four lanes of the head
+  float l_h = l_run + __shfl_xor(l_run, 16, 64);
+  l_h += __shfl_xor(l_h, 32, 64);
+
+  // workgroup merge of the four waves (LDS), then this workgroup's partial to HBM
+  __syncthreads();
+  float* mrg = reinterpret_cast<float*>(dm_smem);               // [4][16][D + 2]
+  {
+    float* mw = mrg + ((size_t)wave * 16 + n) * (D + 2);
+    if (qd == 0) {
+      mw[0] = m_run;
+      mw[1] = l_h;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mw[2 + 16 * dt + 4 * qd + i] = o[dt][i];
+  }
+  __syncthreads();
+  const size_t pstride = (size_t)G * (D + 2);
+  float* myp = part + (((size_t)b * Hkv + g) * nwg + blockIdx.x) * pstride;
+  for (int e = tid; e < G * D; e += 256) {
+    const int h = e / D, d = e % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; w++) mm = fmaxf(mm, mrg[((size_t)w * 16 + h) * (D + 2)]);
+    float ll = 0.0f, oo = 0.0f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const float* mw = mrg + ((size_t)w * 16 + h) * (D + 2);
+        if (mw[0] == -INFINITY) continue;
+        const float sc = __builtin_amdgcn_exp2f((mw[0] - mm) * c2);
+        ll += mw[1] * sc;
+        oo += mw[2 + d] * sc;
+      }
+    }
+    myp[h * (D + 2) + 2 + d] = oo;
+    if (d == 0) {
+      myp[h * (D + 2)] = mm == -INFINITY ? -INFINITY : mm * scale;   // natural-log units
+      myp[h * (D + 2) + 1] = ll;
+    }
+  }
+}
+
+static bool decode_mfma_path(const bsg_dims& d) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  return d.dtype == BSG_BF16 && G <= 16;
+}
+
+static int decode_mfma_ppw(const bsg_dims& d) {
+  (void)d;
+  return 1;
+}
+
+static int decode_mfma_nwg(const bsg_dims& d) {
+  const int ppw = decode_mfma_ppw(d);
+  return (d.top_k + 4 * ppw - 1) / (4 * ppw);
+}
+
 int decode_num_splits(const bsg_dims& d) {
   long long units = (long long)d.batch * d.num_kv_heads;
   long long pps = (d.top_k * units + 512) / 1024;
@@ -163,6 +450,8 @@ int decode_num_splits(const bsg_dims& d) {
 
 size_t decode_workspace_bytes(const bsg_dims& d) {
   const int G = d.num_q_heads / d.num_kv_heads;
+  if (decode_mfma_path(d))
+    return (size_t)d.batch * d.num_kv_heads * decode_mfma_nwg(d) * G * (d.head_dim + 2) * sizeof(float);
   return (size_t)d.batch * d.num_kv_heads * decode_num_splits(d) * G * (d.head_dim + 2) * sizeof(float);
 }
 
@@ -175,6 +464,41 @@ static size_t decode_smem(const bsg_dims& d, size_t elem) {
 hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
                               const void* v_cache, const int32_t* page_table, const int32_t* block_idx,
                               float scale, void* workspace, void* out, float* lse, hipStream_t stream) {
+  if (decode_mfma_path(d)) {
+    const int G = d.num_q_heads / d.num_kv_heads;
+    const int nwg = decode_mfma_nwg(d);
+    float* part = (float*)workspace;
+    const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
+    const size_t smem_m = (size_t)4 * 16 * (d.head_dim + 2) * sizeof(float);
+    const size_t smem = smem_v > smem_m ? smem_v : smem_m;
+    dim3 grid(nwg, d.num_kv_heads, d.batch);
+#define BSG_DM(DD, BB)                                                                                            \
+  do {                                                                                                             \
+    auto kfn = attn_decode_mfma_kernel<DD, BB, false>;                                                             \
+    hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);  \
+    if (ea != hipSuccess) return ea;                                                                               \
+    hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache,      \
+                       (const bf16_t*)v_cache, page_table, const_cast<int32_t*>(block_idx), nullptr, scale, part,  \
+                       d.num_q_heads, d.num_kv_heads, d.top_k, d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d),  \
+                       0, 1);                                                                                      \
+  } while (0)
+    if (d.head_dim == 128) {
+      if (d.page_size == 64) BSG_DM(128, 64); else BSG_DM(128, 128);
+    } else {
+      if (d.page_size == 64) BSG_DM(64, 64); else BSG_DM(64, 128);
+    }
+#undef BSG_DM
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 mgrid(d.batch * d.num_q_heads);
+    if (d.head_dim == 128)
+      hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 128>), mgrid, dim3(128), 0, stream, part, (bf16_t*)out, lse,
+                         d.num_q_heads, d.num_kv_heads, nwg);
+    else
+      hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
+                         d.num_q_heads, d.num_kv_heads, nwg);
+    return hipGetLastError();
+  }
   const int nsplit = decode_num_splits(d);
   const int pps = (d.top_k + nsplit - 1) / nsplit;
   dim3 grid(nsplit, d.num_kv_heads, d.batch);
@@ -217,6 +541,63 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
       hipLaunchKernelGGL((attn_decode_merge_kernel<float, 64>), mgrid, dim3(64), 0, stream, ws, (float*)out, lse,
                          d.num_q_heads, d.num_kv_heads, nsplit);
   }
+  return hipGetLastError();
+}
+
+bool decode_step_fused_supported(const bsg_dims& d) { return decode_mfma_path(d) && decode_select_supported(d, 1); }
+
+size_t decode_step_workspace_bytes(const bsg_dims& d) {
+  if (!decode_step_fused_supported(d)) return 0;
+  const size_t a = (decode_select_workspace_bytes(d) + 255) / 256 * 256;
+  return a + decode_workspace_bytes(d);
+}
+
+hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
+                              const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
+                              int32_t* block_idx, void* workspace, void* out, float* lse, hipStream_t stream) {
+  const size_t a = (decode_select_workspace_bytes(d) + 255) / 256 * 256;
+  uint64_t* lists = (uint64_t*)workspace;
+  float* part = (float*)((char*)workspace + a);
+  hipError_t e = launch_decode_score_chunks(d, q, kv_lens, block_cache, page_table, lists, stream);
+  if (e != hipSuccess) return e;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  const int nwg = decode_mfma_nwg(d);
+  const int nchunks = decode_select_nchunks(d);
+  const int m = d.top_k - 1;
+  int T = 1;
+  while (m > 0 && nchunks * T < m && T < m) T <<= 1;
+  const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
+  const size_t smem_m = (size_t)4 * 16 * (d.head_dim + 2) * sizeof(float);
+  const size_t smem_s = (size_t)2 * nchunks * (m > 0 ? m : 1) * sizeof(uint64_t);
+  size_t smem = smem_v > smem_m ? smem_v : smem_m;
+  smem = smem > smem_s ? smem : smem_s;
+  if (smem > 150 * 1024) return hipErrorInvalidValue;
+  dim3 grid(nwg, d.num_kv_heads, d.batch);
+#define BSG_DF(DD, BB)                                                                                            \
+  do {                                                                                                             \
+    auto kfn = attn_decode_mfma_kernel<DD, BB, true>;                                                              \
+    hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);  \
+    if (ea != hipSuccess) return ea;                                                                               \
+    hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache,      \
+                       (const bf16_t*)v_cache, page_table, block_idx, lists, scale, part, d.num_q_heads,            \
+                       d.num_kv_heads, d.top_k, d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d), nchunks, T);     \
+  } while (0)
+  if (d.head_dim == 128) {
+    if (d.page_size == 64) BSG_DF(128, 64); else BSG_DF(128, 128);
+  } else {
+    if (d.page_size == 64) BSG_DF(64, 64); else BSG_DF(64, 128);
+  }
+#undef BSG_DF
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 mgrid(d.batch * d.num_q_heads);
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 128>), mgrid, dim3(128), 0, stream, part, (bf16_t*)out, lse,
+                       d.num_q_heads, d.num_kv_heads, nwg);
+  else
+    hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
+                       d.num_q_heads, d.num_kv_heads, nwg);
+  (void)G;
   return hipGetLastError();
 }
 

@@ -75,6 +75,7 @@ int bsg_topk_blocks(const bsg_dims* dims, const float* scores, int32_t q_len, in
 size_t bsg_group_score_topk_workspace_bytes(const bsg_dims* dims, int32_t q_len) {
   if (check_dims(dims) || q_len < 1) return 0;
   if (bsg::group_score_topk_fused_supported(*dims, q_len)) return 0;
+  if (bsg::decode_select_supported(*dims, q_len)) return bsg::decode_select_workspace_bytes(*dims);
   return (size_t)dims->batch * dims->num_kv_heads * (size_t)q_len * dims->pt_stride * sizeof(float);
 }
 
@@ -88,9 +89,11 @@ int bsg_group_score_topk(const bsg_dims* dims, const void* q, int32_t q_len, con
   const size_t need = bsg_group_score_topk_workspace_bytes(dims, q_len);
   if (need > 0 && (!workspace || workspace_bytes < need)) return BSG_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if (need == 0)
+  if (bsg::group_score_topk_fused_supported(*dims, q_len))
     return to_status(bsg::launch_group_score_topk_fused(*dims, q, q_len, kv_lens, block_cache, page_table,
                                                         block_idx, s));
+  if (bsg::decode_select_supported(*dims, q_len))
+    return to_status(bsg::launch_decode_select(*dims, q, kv_lens, block_cache, page_table, block_idx, workspace, s));
   float* scores = (float*)workspace;
   hipError_t e = bsg::launch_group_score(*dims, q, q_len, kv_lens, block_cache, page_table, scores,
                                          dims->pt_stride, s);
@@ -126,6 +129,43 @@ int bsg_sparse_attn_decode(const bsg_dims* dims, const void* q, const int32_t* k
   if (!workspace || workspace_bytes < need) return BSG_ERR_WORKSPACE;
   return to_status(bsg::launch_attn_decode(*dims, q, kv_lens, k_cache, v_cache, page_table, block_idx, scale,
                                            workspace, out, lse, (hipStream_t)stream));
+}
+
+static size_t decode_step_ws_split(const bsg_dims* d, size_t* a_out) {
+  // [selection workspace | attention partials], each 256-byte aligned
+  const size_t a = (bsg_group_score_topk_workspace_bytes(d, 1) + 255) / 256 * 256;
+  *a_out = a;
+  return a + bsg::decode_workspace_bytes(*d);
+}
+
+size_t bsg_decode_step_workspace_bytes(const bsg_dims* dims) {
+  if (check_dims(dims)) return 0;
+  if (bsg::decode_step_fused_supported(*dims)) return bsg::decode_step_workspace_bytes(*dims);
+  size_t a;
+  return decode_step_ws_split(dims, &a);
+}
+
+int bsg_decode_step(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* block_cache,
+                    const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
+                    int32_t* block_idx, void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !kv_lens || !block_cache || !k_cache || !v_cache || !page_table || !block_idx || !out)
+    return BSG_ERR_NULL;
+  const int G = dims->num_q_heads / dims->num_kv_heads;
+  if (G * dims->head_dim > 2048) return BSG_ERR_UNSUPPORTED;
+  const size_t need = bsg_decode_step_workspace_bytes(dims);
+  if (!workspace || workspace_bytes < need) return BSG_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (bsg::decode_step_fused_supported(*dims))
+    return to_status(bsg::launch_decode_step(*dims, q, kv_lens, block_cache, k_cache, v_cache, page_table, scale,
+                                             block_idx, workspace, out, lse, s));
+  size_t a;
+  decode_step_ws_split(dims, &a);
+  st = bsg_group_score_topk(dims, q, 1, kv_lens, block_cache, page_table, block_idx, workspace, a, stream);
+  if (st) return st;
+  return bsg_sparse_attn_decode(dims, q, kv_lens, k_cache, v_cache, page_table, block_idx, scale,
+                                (char*)workspace + a, workspace_bytes - a, out, lse, stream);
 }
 
 }  // extern "C"

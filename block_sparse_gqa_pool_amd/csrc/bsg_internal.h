@@ -27,6 +27,24 @@ hipError_t launch_group_score_topk_fused(const bsg_dims& d, const void* q, int q
                                          const int32_t* page_table, int32_t* block_idx,
                                          hipStream_t stream);
 
+// Decode scoring + selection (q_len = 1): chunked block-cache scan + tournament merge.
+bool decode_select_supported(const bsg_dims& d, int q_len);
+size_t decode_select_workspace_bytes(const bsg_dims& d);
+hipError_t launch_decode_select(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
+                                const int32_t* page_table, int32_t* block_idx, void* workspace, hipStream_t stream);
+
+int decode_select_nchunks(const bsg_dims& d);
+hipError_t launch_decode_score_chunks(const bsg_dims& d, const void* q, const int32_t* kv_lens,
+                                     const void* block_cache, const int32_t* page_table, uint64_t* lists,
+                                     hipStream_t stream);
+
+// Fused decode step: chunked scoring, then selection + split attention in one kernel, then merge.
+bool decode_step_fused_supported(const bsg_dims& d);
+size_t decode_step_workspace_bytes(const bsg_dims& d);
+hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
+                              const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
+                              int32_t* block_idx, void* workspace, void* out, float* lse, hipStream_t stream);
+
 hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
                                const void* k_cache, const void* v_cache, const int32_t* page_table,
                                const int32_t* block_idx, float scale, void* out, float* lse,

@@ -1,0 +1,270 @@
+// Decode-time scoring + causal top-k (one query per sequence).  Ling 2.0 page, "Summarizing
+// the Breakthrough": at decode the block cache is read and only the top-k blocks are
+// fetched; MSA post, second and third paragraphs: top-k per GQA group, without exponentials.
+//
+// The block cache of every candidate block is read exactly once (the dominant HBM stream of
+// a decode step), so scoring is organised for bandwidth:
+//
+//  A. decode_score_chunk_kernel, grid (chunks of 128 candidate blocks, B), 512 threads.
+//     The representatives of all KV heads of a page are contiguous (Hkv*D values), so the
+//     workgroup streams whole page rows with 16-byte loads; each 16-byte piece is dotted
+//     with the matching slice of the fp32 group-summed query and reduced over the D/8 lanes
+//     that hold one (block, group).  Then one wave per group sorts the chunk's 128 keys
+//     (score, lower-index-first) with a register bitonic network and writes its best
+//     top_k - 1 keys, sorted descending.
+//  B. decode_select_kernel, one workgroup per (sequence, group): exact selection from the
+//     sorted chunk lists by pruning and ranking (see the kernel), then the kept ids are
+//     written ascending, the own block appended and the row padded with -1.
+#include "bsg_device.h"
+#include "bsg_internal.h"
+
+namespace bsg {
+
+namespace {
+constexpr int DS_CH = 128;   // candidate blocks per workgroup of kernel A
+constexpr int DS_NT = 512;
+}  // namespace
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t w = shfl_xor_u64(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Bitonic sort (descending) of 64 * R keys held as v[r] = element r * 64 + lane.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(uint64_t v[R], int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64 * R; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < 64) {
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+          const int e = r * 64 + lane;
+          const uint64_t pv = shfl_xor_u64(v[r], j);
+          const bool desc = (e & k) == 0;          // this k-block sorts descending
+          const bool lower = (lane & j) == 0;      // e < e ^ j
+          const bool take_max = (lower == desc);
+          const uint64_t mx = v[r] > pv ? v[r] : pv, mn = v[r] > pv ? pv : v[r];
+          v[r] = take_max ? mx : mn;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+          const int r2 = r ^ (j >> 6);
+          if (r < r2) {                              // in-lane pair (r, r2), r is the lower element
+            const bool desc = ((r * 64 + lane) & k) == 0;
+            const uint64_t a = v[r], b2 = v[r2];
+            const uint64_t hi = a > b2 ? a : b2, lo = a > b2 ? b2 : a;
+            v[r] = desc ? hi : lo;
+            v[r2] = desc ? lo : hi;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ block_cache,
+    const int32_t* __restrict__ page_table, uint64_t* __restrict__ lists, int Hq, int Hkv, int bs, int m,
+    int num_pages, int pt_stride, int nchunks) {
+  extern __shared__ __attribute__((aligned(16))) float ds_smem[];
+  float* qs = ds_smem;                   // [Hkv][D]
+  float* sc = ds_smem + Hkv * D;         // [Hkv][DS_CH]
+  constexpr int SEG = D / 8;             // lanes per (block, group)
+  const int b = blockIdx.y, c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = Hq / Hkv;
+  const int j0 = c * DS_CH;
+  const int own = max(kv_lens[b] - 1, 0) / bs;
+  const int ncand = min(own, pt_stride);
+  const int nloc = max(0, min(DS_CH, ncand - j0));   // candidates in this chunk
+
+  for (int e = tid; e < Hkv * D; e += DS_NT) {
+    const int g = e / D, d = e % D;
+    const bf16_t* qp = q + ((size_t)b * Hq + (size_t)g * G) * D + d;
+    float s = 0.0f;
+    for (int h = 0; h < G; h++) s += bf16_to_f32(qp[(size_t)h * D]);
+    qs[e] = s;
+  }
+  __syncthreads();
+
+  const int ppb = Hkv * SEG;                  // 16-byte pieces per block row
+  const int total = nloc * ppb;
+  const int32_t* ptrow = page_table + (size_t)b * pt_stride + j0;
+  constexpr int U = 8;
+  for (int base = 0; base < total; base += DS_NT * U) {
+    uint4 raw[U];
+    int pi[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      pi[u] = base + u * DS_NT + tid;
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (pi[u] < total) {
+        const int jj = pi[u] / ppb, w = pi[u] % ppb;
+        const int p = clampi(ptrow[jj], 0, num_pages - 1);
+        raw[u] = *reinterpret_cast<const uint4*>(block_cache + (size_t)p * Hkv * D + (size_t)w * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int w = pi[u] % ppb;
+      const float* qv = qs + (size_t)w * 8;     // (g, d8) of this piece
+      const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        s = fmaf(qv[2 * i], __uint_as_float(wd[i] << 16), s);
+        s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
+      }
+#pragma unroll
+      for (int o = SEG / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+      if (pi[u] < total && (lane % SEG) == 0) {
+        const int jj = pi[u] / ppb, g = w / SEG;
+        sc[g * DS_CH + jj] = s;
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int g = wave; g < Hkv; g += DS_NT / 64) {
+    constexpr int R = DS_CH / 64;
+    uint64_t v[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int jj = r * 64 + lane;
+      v[r] = jj < nloc ? sel_key(sc[g * DS_CH + jj], j0 + jj) : 0ull;
+    }
+    wave_sort_desc<R>(v, lane);
+    if (lane < m) lists[(((size_t)b * Hkv + g) * nchunks + c) * m + lane] = v[0];
+  }
+}
+
+// Selection from the sorted chunk lists.  tau = max over chunks of the chunk's m-th key is
+// a lower bound of the global m-th key (that chunk alone holds m keys >= tau), so only keys
+// >= tau can be kept; they form a prefix of every list.  Each surviving key counts the keys
+// above it in every list prefix (binary search), which gives its global rank; ranks below
+// the number to keep are selected.  All keys are distinct, so the ranks are too.
+__global__ __launch_bounds__(256) void decode_select_kernel(const uint64_t* __restrict__ lists,
+                                                            const int32_t* __restrict__ kv_lens,
+                                                            int32_t* __restrict__ block_idx, int Hkv, int bs,
+                                                            int top_k, int nchunks, int pt_stride) {
+  extern __shared__ uint64_t dsel_smem[];   // [nchunks][m] keys, then [nchunks] prefix lengths
+  __shared__ int kept[64];
+  __shared__ uint64_t tau_s;
+  const int row = blockIdx.x;
+  const int b = row / Hkv;
+  const int tid = threadIdx.x;
+  const int m = top_k - 1;
+  const int own = max(kv_lens[b] - 1, 0) / bs;
+  const int ncand = min(own, pt_stride);
+  const int cnt = min(m, ncand);
+  int32_t* out = block_idx + (size_t)row * top_k;
+  if (cnt > 0) {
+    uint64_t* L = dsel_smem;
+    int* plen = reinterpret_cast<int*>(dsel_smem + (size_t)nchunks * m);
+    const uint64_t* src = lists + (size_t)row * nchunks * m;
+    for (int e = tid; e < nchunks * m; e += 256) L[e] = src[e];
+    if (tid == 0) tau_s = 0ull;
+    __syncthreads();
+    for (int c = tid; c < nchunks; c += 256) atomicMax((unsigned long long*)&tau_s, (unsigned long long)L[c * m + m - 1]);
+    __syncthreads();
+    const uint64_t tau = tau_s > 0ull ? tau_s : 1ull;       // keys are >= 1 when valid
+    for (int c = tid; c < nchunks; c += 256) {              // prefix of keys >= tau
+      int lo = 0, hi = m;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (L[c * m + mid] >= tau) lo = mid + 1; else hi = mid;
+      }
+      plen[c] = lo;
+    }
+    __syncthreads();
+    for (int e = tid; e < nchunks * m; e += 256) {
+      const int c = e / m, pidx = e % m;
+      if (pidx >= plen[c]) continue;
+      const uint64_t key = L[e];
+      int rank = 0;
+      for (int c2 = 0; c2 < nchunks && rank < cnt; c2++) {  // keys above `key` in list c2
+        int lo = 0, hi = plen[c2];
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (L[c2 * m + mid] > key) lo = mid + 1; else hi = mid;
+        }
+        rank += lo;
+      }
+      if (rank < cnt) kept[rank] = sel_key_index(key);
+    }
+    __syncthreads();
+    if (tid < cnt) {
+      const int ji = kept[tid];
+      int r2 = 0;
+      for (int i = 0; i < cnt; i++) r2 += kept[i] < ji ? 1 : 0;
+      out[r2] = ji;
+    }
+  }
+  if (tid == 0) out[cnt] = own;
+  for (int i = cnt + 1 + tid; i < top_k; i += 256) out[i] = -1;
+}
+
+int decode_select_nchunks(const bsg_dims& d) { return (d.pt_stride + DS_CH - 1) / DS_CH; }
+
+size_t decode_select_workspace_bytes(const bsg_dims& d) {
+  return (size_t)d.batch * d.num_kv_heads * decode_select_nchunks(d) * (size_t)(d.top_k > 1 ? d.top_k - 1 : 1) *
+         sizeof(uint64_t);
+}
+
+bool decode_select_supported(const bsg_dims& d, int q_len) {
+  const int nchunks = decode_select_nchunks(d);
+  return q_len == 1 && d.dtype == BSG_BF16 && (size_t)nchunks * (d.top_k - 1) * 8 + nchunks * 4 <= 120 * 1024;
+}
+
+hipError_t launch_decode_score_chunks(const bsg_dims& d, const void* q, const int32_t* kv_lens,
+                                     const void* block_cache, const int32_t* page_table, uint64_t* lists,
+                                     hipStream_t stream) {
+  const int nchunks = decode_select_nchunks(d);
+  const int m = d.top_k - 1;
+  if (m <= 0) return hipSuccess;
+  dim3 grid(nchunks, d.batch);
+  const size_t smem = (size_t)(d.num_kv_heads * d.head_dim + d.num_kv_heads * DS_CH) * sizeof(float);
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL(decode_score_chunk_kernel<128>, grid, dim3(DS_NT), smem, stream, (const bf16_t*)q, kv_lens,
+                       (const bf16_t*)block_cache, page_table, lists, d.num_q_heads, d.num_kv_heads, d.page_size, m,
+                       d.num_pages, d.pt_stride, nchunks);
+  else
+    hipLaunchKernelGGL(decode_score_chunk_kernel<64>, grid, dim3(DS_NT), smem, stream, (const bf16_t*)q, kv_lens,
+                       (const bf16_t*)block_cache, page_table, lists, d.num_q_heads, d.num_kv_heads, d.page_size, m,
+                       d.num_pages, d.pt_stride, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_select(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
+                                const int32_t* page_table, int32_t* block_idx, void* workspace, hipStream_t stream) {
+  const int nchunks = decode_select_nchunks(d);
+  const int m = d.top_k - 1;
+  uint64_t* lists = (uint64_t*)workspace;
+  hipError_t e = launch_decode_score_chunks(d, q, kv_lens, block_cache, page_table, lists, stream);
+  if (e != hipSuccess) return e;
+  const size_t smem2 = (size_t)nchunks * (m > 0 ? m : 1) * sizeof(uint64_t) + (size_t)nchunks * sizeof(int);
+  if (smem2 > 64 * 1024) {
+    hipError_t ea = hipFuncSetAttribute((const void*)decode_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)smem2);
+    if (ea != hipSuccess) return ea;
+  }
+  hipLaunchKernelGGL(decode_select_kernel, dim3(d.batch * d.num_kv_heads), dim3(256), smem2, stream, lists, kv_lens,
+                     block_idx, d.num_kv_heads, d.page_size, d.top_k, nchunks, d.pt_stride);
+  return hipGetLastError();
+}
+
+}  // namespace bsg

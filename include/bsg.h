@@ -183,15 +183,36 @@ int bsg_sparse_attn_prefill(const bsg_dims* dims, const void* q, int32_t q_len,
  *
  * The selected blocks of each (sequence, group) are split over several
  * workgroups; each writes a partial (max, sum, unnormalised output) per query
- * head to `workspace`, and a second pass merges them:
+ * head to `workspace`, and the partials are merged:
  *     m = max_s m_s,  l = sum_s l_s e^(m_s - m),  out = sum_s o_s e^(m_s - m) / l.
- * `workspace` (device) must hold bsg_decode_workspace_bytes(dims) bytes.
+ * `workspace` (device) must hold bsg_decode_workspace_bytes(dims) bytes; its
+ * contents need no initialisation.  Two calls that share a workspace must not
+ * run concurrently.
  */
 size_t bsg_decode_workspace_bytes(const bsg_dims* dims);
 int bsg_sparse_attn_decode(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
                            const void* k_cache, const void* v_cache, const int32_t* page_table,
                            const int32_t* block_idx, float scale, void* workspace,
                            size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * bsg_decode_step -- one whole decode step: group scores against the block
+ * cache, causal top-k selection, and sparse attention over the selected
+ * blocks, for q_len = 1.  Same results as bsg_group_score_topk followed by
+ * bsg_sparse_attn_decode (the selection is also written to block_idx,
+ * [B, Hkv, top_k]), but the selection is finished inside the attention
+ * kernel, which saves one launch and one pass over the selection lists.
+ * Follows the Ling 2.0 page, "Summarizing the Breakthrough" (decode reads the
+ * block cache, picks the top-k blocks and fetches only those).
+ * q: [B, Hq, D]; out: [B, Hq, D]; lse: fp32 [B, Hq] or NULL.  `workspace`
+ * (device, no initialisation needed) must hold
+ * bsg_decode_step_workspace_bytes(dims) bytes.
+ */
+size_t bsg_decode_step_workspace_bytes(const bsg_dims* dims);
+int bsg_decode_step(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* block_cache,
+                    const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
+                    int32_t* block_idx, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,7 +73,9 @@ def test_validation_of_dims(L, dims, expect):
     assert L.bsg_group_score_topk(dp, BAD, 4, BAD, BAD, BAD, BAD, BAD, 1 << 30, s) == expect
     assert L.bsg_sparse_attn_prefill(dp, BAD, 4, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, None, s) == expect
     assert L.bsg_sparse_attn_decode(dp, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, 1 << 30, BAD, None, s) == expect
+    assert L.bsg_decode_step(dp, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, BAD, 1 << 30, BAD, None, s) == expect
     if dims is not None and expect != 0:
+        assert L.bsg_decode_step_workspace_bytes(dp) == 0
         assert L.bsg_decode_workspace_bytes(dp) == 0
         assert L.bsg_group_score_topk_workspace_bytes(dp, 4) == 0
 
@@ -93,6 +95,10 @@ def test_validation_of_pointers_and_sizes(L):
     assert need > 0
     assert L.bsg_sparse_attn_decode(d, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, None, need, BAD, None, s) == -4
     assert L.bsg_sparse_attn_decode(d, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, need - 1, BAD, None, s) == -4
+    need2 = L.bsg_decode_step_workspace_bytes(d)
+    assert need2 >= need
+    assert L.bsg_decode_step(d, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, BAD, need2 - 1, BAD, None, s) == -4
+    assert L.bsg_decode_step(d, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, None, BAD, need2, BAD, None, s) == -1
     # decode with G * D beyond what the split kernel holds
     big = ctypes.byref(_dims(num_q_heads=64, num_kv_heads=2))
     n2 = L.bsg_decode_workspace_bytes(big)

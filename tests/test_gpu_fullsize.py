@@ -62,13 +62,17 @@ def test_full_decode_sampled(cfg, seqs):
     scale = 1.0 / math.sqrt(D)
     cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=DEV)
     bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
-    idx = torch.empty(B, Hkv, 1, k, dtype=torch.int32, device=DEV)
-    bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, idx, page_size=bs)
+    # the launch configuration bench.py times: the fused decode step
+    idx3 = torch.empty(B, Hkv, k, dtype=torch.int32, device=DEV)
     out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
-    bsg.sparse_attn_decode(w.q[:, :, 0].contiguous(), w.kv_lens, w.k_cache, w.v_cache, w.page_table,
-                           idx.view(B, Hkv, k), scale, out, lse)
+    bsg.decode_step(w.q[:, :, 0].contiguous(), w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx3,
+                    out, lse)
+    # and the separate calls must select the same blocks
+    idx = torch.empty(B, Hkv, 1, k, dtype=torch.int32, device=DEV)
+    bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, idx, page_size=bs)
     torch.cuda.synchronize()
+    assert torch.equal(idx[:, :, 0], idx3)
     if seqs is None:
         seqs = (int(np.argmin(w.kv_lens_host)),)
     note(f"  sampled sequences {seqs} of lengths {[w.kv_lens_host[b] for b in seqs]}")

@@ -244,27 +244,48 @@ def test_prefill_end_to_end(name, fused):
     check_out(to_np(g["out"])[rows], r["out"][rows], s.dtype, "out")
 
 
-@pytest.mark.parametrize("name", DECODE)
-def test_decode_end_to_end(name):
-    w = _work(name, seed=23)
+def run_decode_gpu(w, api="step", lse=True):
+    """Whole decode step on the device: separate calls ("split") or bsg_decode_step ("step")."""
     s = w.spec
     B, Hq, _, D = w.q.shape
     scale = 1.0 / math.sqrt(D)
     cache = torch.zeros(w.k_cache.shape[0], s.num_kv_heads, D, dtype=w.k_cache.dtype, device=DEV)
     bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
-    idx = torch.empty(B, s.num_kv_heads, 1, s.top_k, dtype=torch.int32, device=DEV)
-    bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, idx, page_size=s.page_size)
     out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
-    bsg.sparse_attn_decode(w.q[:, :, 0].contiguous(), w.kv_lens, w.k_cache, w.v_cache, w.page_table,
-                           idx[:, :, 0].contiguous(), scale, out)
+    l = torch.empty(B, Hq, dtype=torch.float32, device=DEV) if lse else None
+    q1 = w.q[:, :, 0].contiguous()
+    if api == "split":
+        idx = torch.empty(B, s.num_kv_heads, 1, s.top_k, dtype=torch.int32, device=DEV)
+        bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, idx, page_size=s.page_size)
+        idx = idx[:, :, 0].contiguous()
+        bsg.sparse_attn_decode(q1, w.kv_lens, w.k_cache, w.v_cache, w.page_table, idx, scale, out, l)
+    else:
+        idx = torch.full((B, s.num_kv_heads, s.top_k), -7, dtype=torch.int32, device=DEV)
+        bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx, out, l)
     torch.cuda.synchronize()
+    return cache, idx, out, l
+
+
+def check_decode(w, idx, out, lse):
+    s = w.spec
     q, kp, vp, pt, kv = np_inputs(w)
-    r = O.decode_reference(q, kp, vp, pt, kv, s.page_size, s.top_k, s.dtype, scale)
-    gi = idx.cpu().numpy()
+    r = O.decode_reference(q, kp, vp, pt, kv, s.page_size, s.top_k, s.dtype, 1.0 / math.sqrt(s.head_dim))
+    gi = idx.cpu().numpy()[:, :, None]
     bad, exempt = compare_selection(gi, r["block_idx"], r["scores"], s.top_k)
     note(f"  exempt ties {len(exempt)}, bad {len(bad)}")
     assert not bad, bad
-    check_out(to_np(out), r["out"][:, :, 0], s.dtype, "decode out")
+    same = np.repeat(~(gi != r["block_idx"]).any(-1)[:, :, 0], s.group_size, axis=1)
+    check_out(to_np(out)[same], r["out"][:, :, 0][same], s.dtype, "decode out")
+    if lse is not None:
+        assert np.abs(lse.cpu().numpy()[same] - r["lse"][:, :, 0][same]).max() <= 2e-3
+
+
+@pytest.mark.parametrize("api", ["split", "step"])
+@pytest.mark.parametrize("name", DECODE)
+def test_decode_end_to_end(name, api):
+    w = _work(name, seed=23)
+    cache, idx, out, lse = run_decode_gpu(w, api)
+    check_decode(w, idx, out, lse)
 
 
 @pytest.mark.parametrize("case", [
@@ -291,3 +312,65 @@ def test_fused_selection_edge_shapes(case):
     bad, exempt = compare_selection(idx.cpu().numpy(), ref, sc, spec.top_k)
     note(f"  exempt {len(exempt)} bad {len(bad)}")
     assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("case", [
+    dict(top_k=1), dict(top_k=3), dict(top_k=64), dict(num_q_heads=4, num_kv_heads=4),
+    dict(num_q_heads=64, num_kv_heads=4), dict(head_dim=64), dict(page_size=128, top_k=9),
+    dict(ctx_len=64 * 120 - 1),            # the new token completes its page
+    dict(ctx_len=70),                      # fewer candidates than top_k - 1
+    dict(num_q_heads=80, num_kv_heads=4, head_dim=64),  # G = 20: VALU split path
+])
+@pytest.mark.parametrize("api", ["split", "step"])
+def test_decode_edge_shapes_end_to_end(case, api):
+    spec = SPECS[2].replace(batch=3, ctx_len=64 * 150 + 11, **case) if "ctx_len" not in case else \
+        SPECS[2].replace(batch=3, **case)
+    note(f"[case] decode edge {case} {api}")
+    w = make_workload(spec, 17, tail_fill=float("nan")).to(DEV)
+    cache, idx, out, lse = run_decode_gpu(w, api)
+    check_decode(w, idx, out, lse)
+
+
+def test_decode_step_ragged_batch_and_reuse():
+    """Ragged lengths (some shorter than the others by many chunks); workspace reused."""
+    spec = SPECS[4].replace(batch=4, ctx_range=(64 * 30, 64 * 900), num_q_heads=16, num_kv_heads=2)
+    ws = None
+    for seed in (41, 42):
+        note(f"[case] ragged decode_step seed={seed}")
+        w = make_workload(spec, seed, tail_fill=float("nan")).to(DEV)
+        B, Hq, _, D = w.q.shape
+        cache = torch.zeros(w.k_cache.shape[0], spec.num_kv_heads, D, dtype=w.k_cache.dtype, device=DEV)
+        bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+        if ws is None:
+            ws = torch.empty(bsg.decode_step_workspace_bytes(w.k_cache, w.page_table, Hq, spec.top_k) + 4096,
+                             dtype=torch.uint8, device=DEV)
+        idx = torch.empty(B, spec.num_kv_heads, spec.top_k, dtype=torch.int32, device=DEV)
+        out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+        bsg.decode_step(w.q[:, :, 0].contiguous(), w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table,
+                        1.0 / math.sqrt(D), idx, out, lse, workspace=ws)
+        torch.cuda.synchronize()
+        check_decode(w, idx, out, lse)
+
+
+def test_decode_workspace_reuse_across_calls():
+    """The decode workspace is reused by consecutive calls (its counters reset themselves)."""
+    spec = SPECS[2].replace(batch=4, ctx_len=64 * 90 + 3)
+    ws = None
+    for seed in (31, 32, 33):
+        note(f"[case] workspace reuse seed={seed}")
+        w = make_workload(spec, seed).to(DEV)
+        B, Hq, _, D = w.q.shape
+        scale = 1.0 / math.sqrt(D)
+        if ws is None:
+            ws = torch.zeros(bsg.decode_workspace_bytes(w.k_cache, w.page_table, Hq, spec.top_k),
+                             dtype=torch.uint8, device=DEV)
+        q, kp, vp, pt, kv = np_inputs(w)
+        r = O.decode_reference(q, kp, vp, pt, kv, spec.page_size, spec.top_k, spec.dtype, scale)
+        didx = torch.from_numpy(r["block_idx"][:, :, 0]).contiguous().to(DEV)
+        out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
+        for _ in range(2):
+            bsg.sparse_attn_decode(w.q[:, :, 0].contiguous(), w.kv_lens, w.k_cache, w.v_cache, w.page_table, didx,
+                                   scale, out, workspace=ws)
+            torch.cuda.synchronize()
+            check_out(to_np(out), r["out"][:, :, 0], "bf16", "decode out (reused workspace)")
