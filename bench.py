@@ -4,7 +4,8 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input:
   prefill workload: block_pool -> group_score_topk -> sparse_attn_prefill
-  decode workload:  decode_step = group scores + top-k + sparse attention (block cache built beforehand)
+  decode workload:  decode_step = group scores + top-k + sparse attention (block cache built beforehand),
+                    captured (8 steps per HIP graph) and replayed: the step is three short kernels
 Inputs are generated on the GPU and resident in HBM before timing starts.  The default
 workload is the 128K prefill (B=1, S=131072, Hq=64, Hkv=8, D=128, 128-token blocks,
 top-16); the 128K decode step (B=32, context 131072, Hq=32, Hkv=4, 64-token pages,
@@ -154,27 +155,38 @@ def run_decode(spec, seed, steps, warmup):
     ws = torch.empty(bsg.decode_step_workspace_bytes(w.k_cache, w.page_table, Hq, k), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def step():
         bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx, out, workspace=ws)
-        if ev:
-            ev[1].record(stream)
-            ev[2].record(stream)
 
-    for _ in range(warmup):
+    # the step is three short kernels, faster than Python can launch them: capture
+    # PER_GRAPH whole steps in one HIP graph and replay it, so the timed region measures
+    # back-to-back GPU work rather than host launch cost
+    PER_GRAPH = 8
+    for _ in range(max(warmup, 1)):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(PER_GRAPH):
+            step()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, (steps + PER_GRAPH - 1) // PER_GRAPH)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i])
+    e0.record(stream)
+    for _ in range(n_rep):
+        graph.replay()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
+    steps = n_rep * PER_GRAPH
+    step_ms = e0.elapsed_time(e1) / steps
     nbytes, parts = decode_bytes(idx, w.kv_lens, bs, Hkv, D)
-    res = dict(us_per_step=1e3 * step_ms, wall_us_per_step=1e6 * wall / steps, bytes=nbytes, bytes_parts=parts)
-    del w, cache, idx, out, ws
+    res = dict(us_per_step=1e3 * step_ms, wall_us_per_step=1e6 * wall / steps, bytes=nbytes, bytes_parts=parts,
+               steps=steps)
+    del graph, w, cache, idx, out, ws
     torch.cuda.empty_cache()
     return res
 
@@ -267,9 +279,10 @@ def main():
                     stages_ms=r["stage_ms"], wall_ms_per_step=r["wall_ms_per_step"],
                     pipeline_mfma_frac=(r["attn_flops"] / (r["ms_per_step"] / 1e3) / 1e12) / PEAK_BF16_TFLOPS)
         dspec = spec_by_name(args.decode_workload)
-        d = run_decode(dspec, SPECS.index(dspec), max(args.steps, 20), args.warmup)
+        d = run_decode(dspec, SPECS.index(dspec), max(args.steps, 40), args.warmup)
         gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9
         line["decode"] = {"workload": dspec.name, "us_per_step": d["us_per_step"], "api": "bsg_decode_step",
+                          "steps": d["steps"], "timing": "8 steps per HIP graph replay, HIP events",
                           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                        "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": d["bytes"],
                                        "bytes_parts": d["bytes_parts"]},

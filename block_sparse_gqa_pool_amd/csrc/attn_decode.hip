@@ -431,8 +431,9 @@ static bool decode_mfma_path(const bsg_dims& d) {
 }
 
 static int decode_mfma_ppw(const bsg_dims& d) {
-  (void)d;
-  return 1;
+  // two pages per wave when that still leaves >= 512 workgroups (one resident round)
+  const long long wg2 = (long long)d.batch * d.num_kv_heads * ((d.top_k + 7) / 8);
+  return wg2 >= 512 ? 2 : 1;
 }
 
 static int decode_mfma_nwg(const bsg_dims& d) {

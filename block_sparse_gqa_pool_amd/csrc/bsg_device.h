@@ -64,4 +64,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over aligned groups of SEG (4, 8 or 16) lanes with DPP lane moves (no LDS traffic);
+// every lane of a group receives the group's sum.
+template <int SEG>
+__device__ __forceinline__ float seg_sum_dpp(float v) {
+  static_assert(SEG == 4 || SEG == 8 || SEG == 16, "segment of 4, 8 or 16 lanes");
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  if (SEG >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half mirror
+  if (SEG >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // mirror
+  return v;
+}
+
 }  // namespace bsg

@@ -5,11 +5,11 @@
 // The block cache of every candidate block is read exactly once (the dominant HBM stream of
 // a decode step), so scoring is organised for bandwidth:
 //
-//  A. decode_score_chunk_kernel, grid (chunks of 128 candidate blocks, B), 512 threads.
+//  A. decode_score_chunk_kernel, grid (chunks of 64 candidate blocks, B), 256 threads.
 //     The representatives of all KV heads of a page are contiguous (Hkv*D values), so the
 //     workgroup streams whole page rows with 16-byte loads; each 16-byte piece is dotted
 //     with the matching slice of the fp32 group-summed query and reduced over the D/8 lanes
-//     that hold one (block, group).  Then one wave per group sorts the chunk's 128 keys
+//     that hold one (block, group).  Then one wave per group sorts the chunk's 64 keys
 //     (score, lower-index-first) with a register bitonic network and writes its best
 //     top_k - 1 keys, sorted descending.
 //  B. decode_select_kernel, one workgroup per (sequence, group): exact selection from the
@@ -21,59 +21,9 @@
 namespace bsg {
 
 namespace {
-constexpr int DS_CH = 128;   // candidate blocks per workgroup of kernel A
-constexpr int DS_NT = 512;
+constexpr int DS_CH = 64;    // candidate blocks per workgroup of kernel A
+constexpr int DS_NT = 256;
 }  // namespace
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = shfl_xor_u64(v, o);
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
-// Bitonic sort (descending) of 64 * R keys held as v[r] = element r * 64 + lane.
-template <int R>
-__device__ __forceinline__ void wave_sort_desc(uint64_t v[R], int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64 * R; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < 64) {
-#pragma unroll
-        for (int r = 0; r < R; r++) {
-          const int e = r * 64 + lane;
-          const uint64_t pv = shfl_xor_u64(v[r], j);
-          const bool desc = (e & k) == 0;          // this k-block sorts descending
-          const bool lower = (lane & j) == 0;      // e < e ^ j
-          const bool take_max = (lower == desc);
-          const uint64_t mx = v[r] > pv ? v[r] : pv, mn = v[r] > pv ? pv : v[r];
-          v[r] = take_max ? mx : mn;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < R; r++) {
-          const int r2 = r ^ (j >> 6);
-          if (r < r2) {                              // in-lane pair (r, r2), r is the lower element
-            const bool desc = ((r * 64 + lane) & k) == 0;
-            const uint64_t a = v[r], b2 = v[r2];
-            const uint64_t hi = a > b2 ? a : b2, lo = a > b2 ? b2 : a;
-            v[r] = desc ? hi : lo;
-            v[r2] = desc ? lo : hi;
-          }
-        }
-      }
-    }
-  }
-}
 
 template <int D>
 __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
@@ -84,6 +34,7 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
   float* qs = ds_smem;                   // [Hkv][D]
   float* sc = ds_smem + Hkv * D;         // [Hkv][DS_CH]
   constexpr int SEG = D / 8;             // lanes per (block, group)
+  constexpr int U = 16;                  // 16-byte loads in flight per thread
   const int b = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
@@ -91,36 +42,27 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
   const int own = max(kv_lens[b] - 1, 0) / bs;
   const int ncand = min(own, pt_stride);
   const int nloc = max(0, min(DS_CH, ncand - j0));   // candidates in this chunk
-
-  for (int e = tid; e < Hkv * D; e += DS_NT) {
-    const int g = e / D, d = e % D;
-    const bf16_t* qp = q + ((size_t)b * Hq + (size_t)g * G) * D + d;
-    float s = 0.0f;
-    for (int h = 0; h < G; h++) s += bf16_to_f32(qp[(size_t)h * D]);
-    qs[e] = s;
-  }
-  __syncthreads();
-
-  const int ppb = Hkv * SEG;                  // 16-byte pieces per block row
+  const int ppb = Hkv * SEG;                          // 16-byte pieces per block row
   const int total = nloc * ppb;
   const int32_t* ptrow = page_table + (size_t)b * pt_stride + j0;
-  constexpr int U = 8;
-  for (int base = 0; base < total; base += DS_NT * U) {
-    uint4 raw[U];
-    int pi[U];
+
+  uint4 raw[U];
+  auto issue = [&](int base) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      pi[u] = base + u * DS_NT + tid;
+      const int pi = base + u * DS_NT + tid;
       raw[u] = make_uint4(0, 0, 0, 0);
-      if (pi[u] < total) {
-        const int jj = pi[u] / ppb, w = pi[u] % ppb;
-        const int p = clampi(ptrow[jj], 0, num_pages - 1);
-        raw[u] = *reinterpret_cast<const uint4*>(block_cache + (size_t)p * Hkv * D + (size_t)w * 8);
+      if (pi < total) {
+        const int p = clampi(ptrow[pi / ppb], 0, num_pages - 1);
+        raw[u] = *reinterpret_cast<const uint4*>(block_cache + (size_t)p * Hkv * D + (size_t)(pi % ppb) * 8);
       }
     }
+  };
+  auto consume = [&](int base) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int w = pi[u] % ppb;
+      const int pi = base + u * DS_NT + tid;
+      const int w = pi % ppb;
       const float* qv = qs + (size_t)w * 8;     // (g, d8) of this piece
       const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
       float s = 0.0f;
@@ -129,26 +71,43 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
         s = fmaf(qv[2 * i], __uint_as_float(wd[i] << 16), s);
         s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
       }
-#pragma unroll
-      for (int o = SEG / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-      if (pi[u] < total && (lane % SEG) == 0) {
-        const int jj = pi[u] / ppb, g = w / SEG;
-        sc[g * DS_CH + jj] = s;
-      }
+      s = seg_sum_dpp<SEG>(s);
+      if (pi < total && (lane % SEG) == 0) sc[(w / SEG) * DS_CH + pi / ppb] = s;
     }
+  };
+
+  if (total > 0) issue(0);                    // block-cache rows in flight while q is summed
+  for (int e = tid; e < Hkv * D; e += DS_NT) {
+    const int g = e / D, d = e % D;
+    const bf16_t* qp = q + ((size_t)b * Hq + (size_t)g * G) * D + d;
+    float s = 0.0f;
+    for (int h = 0; h < G; h++) s += bf16_to_f32(qp[(size_t)h * D]);
+    qs[e] = s;
+  }
+  __syncthreads();
+  for (int base = 0; base < total; base += DS_NT * U) {
+    if (base > 0) issue(base);
+    consume(base);
   }
   __syncthreads();
 
+  // per group: the chunk's best m keys, sorted descending (rank = number of larger keys)
+  uint64_t* kbuf = reinterpret_cast<uint64_t*>(sc + Hkv * DS_CH) + wave * 64;
   for (int g = wave; g < Hkv; g += DS_NT / 64) {
-    constexpr int R = DS_CH / 64;
-    uint64_t v[R];
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-      const int jj = r * 64 + lane;
-      v[r] = jj < nloc ? sel_key(sc[g * DS_CH + jj], j0 + jj) : 0ull;
+    const uint64_t key = lane < nloc ? sel_key(sc[g * DS_CH + lane], j0 + lane) : 0ull;
+    kbuf[lane] = key;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int rank = 0;                            // distinct ranks: equal (zero) keys ordered by lane
+#pragma unroll 8
+    for (int i = 0; i < 64; i++) {
+      const uint64_t o = kbuf[i];
+      rank += (o > key || (o == key && i < lane)) ? 1 : 0;
     }
-    wave_sort_desc<R>(v, lane);
-    if (lane < m) lists[(((size_t)b * Hkv + g) * nchunks + c) * m + lane] = v[0];
+    uint64_t* dst = lists + (((size_t)b * Hkv + g) * nchunks + c) * m;
+    if (rank < m) dst[rank] = key;
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -237,7 +196,8 @@ hipError_t launch_decode_score_chunks(const bsg_dims& d, const void* q, const in
   const int m = d.top_k - 1;
   if (m <= 0) return hipSuccess;
   dim3 grid(nchunks, d.batch);
-  const size_t smem = (size_t)(d.num_kv_heads * d.head_dim + d.num_kv_heads * DS_CH) * sizeof(float);
+  const size_t smem = (size_t)(d.num_kv_heads * d.head_dim + d.num_kv_heads * DS_CH) * sizeof(float) +
+                      (size_t)(DS_NT / 64) * 64 * sizeof(uint64_t);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(decode_score_chunk_kernel<128>, grid, dim3(DS_NT), smem, stream, (const bf16_t*)q, kv_lens,
                        (const bf16_t*)block_cache, page_table, lists, d.num_q_heads, d.num_kv_heads, d.page_size, m,

@@ -374,3 +374,47 @@ def test_decode_workspace_reuse_across_calls():
                                    scale, out, workspace=ws)
             torch.cuda.synchronize()
             check_out(to_np(out), r["out"][:, :, 0], "bf16", "decode out (reused workspace)")
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """bsg_decode_step captured in a HIP graph: every replay equals the eager call bit for bit,
+    with eager work and synchronisation between the replays."""
+    spec = SPECS[2].replace(batch=6, ctx_len=64 * 200 + 9)
+    w = make_workload(spec, 51).to(DEV)
+    B, Hq, _, D = w.q.shape
+    Hkv, k = spec.num_kv_heads, spec.top_k
+    scale = 1.0 / math.sqrt(D)
+    cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=DEV)
+    bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+    q1 = w.q[:, :, 0].contiguous()
+    ws = torch.empty(bsg.decode_step_workspace_bytes(w.k_cache, w.page_table, Hq, k), dtype=torch.uint8, device=DEV)
+    idx_e = torch.empty(B, Hkv, k, dtype=torch.int32, device=DEV)
+    out_e = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
+    lse_e = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+    bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx_e, out_e, lse_e, workspace=ws)
+    torch.cuda.synchronize()
+    idx_g = torch.empty_like(idx_e)
+    out_g = torch.empty_like(out_e)
+    lse_g = torch.empty_like(lse_e)
+    ws_g = torch.empty_like(ws)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx_g, out_g, lse_g,
+                        workspace=ws_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        idx_g.fill_(-5)
+        out_g.zero_()
+        lse_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        note(f"  replay {rep}")
+        assert torch.equal(idx_g, idx_e)
+        assert torch.equal(out_g, out_e)
+        assert torch.equal(lse_g, lse_e)
+        # eager work between replays (same workspace as the eager call)
+        bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx_e, out_e, lse_e,
+                        workspace=ws)
+        torch.cuda.synchronize()
+    check_decode(w, idx_e, out_e, lse_e)
