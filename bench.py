@@ -137,7 +137,7 @@ def run_prefill(spec, seed, steps, warmup):
     return res
 
 
-def run_decode(spec, seed, steps, warmup):
+def run_decode(spec, seed, steps, warmup, graph_replay=True):
     import torch
     import block_sparse_gqa_pool_amd as bsg
     from workloads import make_workload
@@ -165,6 +165,13 @@ def run_decode(spec, seed, steps, warmup):
     for _ in range(max(warmup, 1)):
         step()
     torch.cuda.synchronize()
+    if not graph_replay:                     # eager steps (counter collection)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        del w, cache, idx, out, ws
+        torch.cuda.empty_cache()
+        return None
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for _ in range(PER_GRAPH):
@@ -235,6 +242,76 @@ def cpu_baseline_prefill(spec, seed, n_tokens):
                 seconds=t2 - t0)
 
 
+# ------------------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters
+TRAFFIC_KERNELS = {
+    # key: (kernel-name substring, source files, workload)
+    "sparse_attn_prefill_s131072": ("attn_prefill_mfma_kernel", ["attn_prefill.hip"], "prefill_bf16_s131072"),
+    "decode_attn_b32_ctx131072": ("attn_decode_mfma_kernel", ["attn_decode.hip"], "decode_bf16_b32_ctx131072"),
+    "decode_scan_b32_ctx131072": ("decode_score_chunk_kernel", ["decode_select.hip"], "decode_bf16_b32_ctx131072"),
+}
+CALIB_BYTES = 1 << 30
+
+
+def traffic_run():
+    """One prefill step, one decode step, then a calibration copy of CALIB_BYTES (run under rocprofv3 --pmc)."""
+    import torch
+    from workloads import spec_by_name, SPECS
+    sp = spec_by_name("prefill_bf16_s131072")
+    run_prefill(sp, SPECS.index(sp), 1, 0)
+    sd = spec_by_name("decode_bf16_b32_ctx131072")
+    run_decode(sd, SPECS.index(sd), 4, 0, graph_replay=False)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)          # the last dispatch: reads and writes CALIB_BYTES
+    torch.cuda.synchronize()
+    print("traffic run done", flush=True)
+
+
+def _pmc_rows(directory):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    rows = list(csv.DictReader(open(files[0])))
+    per = {}
+    for r in rows:
+        did = int(r["Dispatch_Id"])
+        per.setdefault(did, {"name": r["Kernel_Name"], "val": 0.0})
+        per[did]["val"] += float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def summarize_traffic(fetch_dir, write_dir):
+    fetch, write = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    f_cal, w_cal = fetch[-1]["val"], write[-1]["val"]          # KiB read / written by the copy
+    kf = CALIB_BYTES / (f_cal * 1024.0)
+    kw = CALIB_BYTES / (w_cal * 1024.0)
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    lines = []
+    for key, (sub, files, wl) in TRAFFIC_KERNELS.items():
+        fv = [r["val"] for r in fetch if sub in r["name"]]
+        wv = [r["val"] for r in write if sub in r["name"]]
+        if not fv or not wv:
+            continue
+        f_b = sum(fv) / len(fv) * 1024.0 * kf
+        w_b = sum(wv) / len(wv) * 1024.0 * kw
+        rec = {"kernel": sub, "workload": wl, "source_hash": _kernel_hash(*files), "hbm_bytes_per_launch": f_b + w_b,
+               "fetch_bytes_per_launch": f_b, "write_bytes_per_launch": w_b, "launches": len(fv),
+               "calibration": {"copy_bytes": CALIB_BYTES, "fetch_kib": f_cal, "write_kib": w_cal,
+                               "fetch_factor": kf, "write_factor": kw}}
+        with open(os.path.join(PROFILE_DIR, f"{key}_traffic.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        lines.append(f"| {sub} | {wl} | {len(fv)} | {f_b / 1e6:.1f} | {w_b / 1e6:.1f} | {(f_b + w_b) / 1e6:.1f} |")
+    print(f"fetch factor {kf:.4f}, write factor {kw:.4f} (copy of {CALIB_BYTES} B read {f_cal:.0f} KiB, "
+          f"wrote {w_cal:.0f} KiB)")
+    print("| kernel | workload | launches | read MB/launch | written MB/launch | total MB/launch |")
+    print("|---|---|---|---|---|---|")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,7 +322,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--traffic-run", action="store_true", help="one prefill + decode step and a calibration copy")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output directories -> profiles/*_traffic.json")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library has no multi-GPU path; "
               "sharding would split KV heads or sequences across GPUs with no exchange.", file=sys.stderr)
@@ -257,6 +340,9 @@ def main():
 
     bsg.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.traffic_run:
+        traffic_run()
+        return
     spec = spec_by_name(args.workload)
     seed = args.seed if args.seed is not None else SPECS.index(spec)
 
@@ -281,11 +367,14 @@ def main():
         dspec = spec_by_name(args.decode_workload)
         d = run_decode(dspec, SPECS.index(dspec), max(args.steps, 40), args.warmup)
         gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9
+        tr_a = _traffic("decode_attn_b32_ctx131072", ["attn_decode.hip"])
+        tr_s = _traffic("decode_scan_b32_ctx131072", ["decode_select.hip"])
         line["decode"] = {"workload": dspec.name, "us_per_step": d["us_per_step"], "api": "bsg_decode_step",
                           "steps": d["steps"], "timing": "8 steps per HIP graph replay, HIP events",
                           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                        "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": d["bytes"],
-                                       "bytes_parts": d["bytes_parts"]},
+                                       "bytes_parts": d["bytes_parts"],
+                                       "traffic": (tr_a + tr_s) if (tr_a and tr_s) else None},
                           "wall_us_per_step": d["wall_us_per_step"]}
     else:
         d = run_decode(spec, seed, args.steps, args.warmup)
