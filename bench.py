@@ -246,7 +246,7 @@ def cpu_baseline_prefill(spec, seed, n_tokens):
 # HBM traffic from rocprofv3 counters
 TRAFFIC_KERNELS = {
     # key: (kernel-name substring, source files, workload)
-    "sparse_attn_prefill_s131072": ("attn_prefill_mfma_kernel", ["attn_prefill.hip"], "prefill_bf16_s131072"),
+    "sparse_attn_prefill_s131072": ("attn_prefill_mfma", ["attn_prefill.hip"], "prefill_bf16_s131072"),
     "decode_attn_b32_ctx131072": ("attn_decode_mfma_kernel", ["attn_decode.hip"], "decode_bf16_b32_ctx131072"),
     "decode_scan_b32_ctx131072": ("decode_score_chunk_kernel", ["decode_select.hip"], "decode_bf16_b32_ctx131072"),
 }

@@ -40,41 +40,62 @@ __device__ __forceinline__ int perm_key(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 
+// ---------------------------------------------------------------------------------------
+// Pipelining and scheduling:
+//  * K/V are staged in 64-key sub-blocks, double-buffered in LDS: the global loads of
+//    sub-block i+1 are issued into registers before sub-block i is computed and written to
+//    the other buffer afterwards, so one barrier per sub-block and the load latency hides
+//    behind the matrix work;
+//  * wave-uniform fast path without masks when every row of the wave selected the block
+//    and it is no row's own block; the running maximum (and with it the output) is only
+//    moved when some row's maximum exceeds it by more than a factor 2^8 in probability;
+//  * workgroups are mapped to tiles XCD by XCD: the dispatcher deals workgroups to the 8
+//    XCDs round robin, so consecutive ids are remapped to give each XCD a contiguous range
+//    of tiles, whose selections overlap, in its own L2.
 template <int D, int BS>
 __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ block_idx, float scale, bf16_t* __restrict__ out, float* __restrict__ lse,
-    int q_len, int Hq, int Hkv, int HG, int top_k, int num_pages, int pt_stride) {
-  constexpr int KS = D + PF_KPAD;  // LDS row strides (elements)
+    int q_len, int Hq, int Hkv, int HG, int top_k, int num_pages, int pt_stride, int n_tt) {
+  constexpr int SUB = 64;                 // keys per staged sub-block
+  constexpr int NSUB = BS / SUB;
+  constexpr int KS = D + PF_KPAD;
   constexpr int VS = D + PF_VPAD;
-  constexpr int NKC = BS / 32;     // 32-key chunks per block
-  constexpr int NDS = D / 16;      // k-steps of the first product
-  constexpr int NDC = D / 32;      // 32-wide d chunks of the output
-  extern __shared__ __attribute__((aligned(16))) unsigned char pf_smem[];
-  bf16_t* Ks = reinterpret_cast<bf16_t*>(pf_smem);
-  bf16_t* Vs = Ks + BS * KS;
+  constexpr int NDS = D / 16;
+  constexpr int NDC = D / 32;
+  constexpr int CH = D / 8;               // 16-byte chunks per row
+  constexpr int PT = SUB * CH / 256;      // chunks per thread per sub-block (each of K and V)
+  extern __shared__ __attribute__((aligned(16))) unsigned char pf2_smem[];
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(pf2_smem);           // [2][SUB][KS]
+  bf16_t* Vs = Ks + 2 * SUB * KS;                              // [2][SUB][VS]
   const int TT = PF_ROWS / HG;
-  int32_t* sel = reinterpret_cast<int32_t*>(Vs + BS * VS);   // [TT][top_k]
+  int32_t* sel = reinterpret_cast<int32_t*>(Vs + 2 * SUB * VS);
   const int nbw = (pt_stride + 31) >> 5;
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(sel + TT * top_k);  // [nbw]
-  int32_t* ulist = reinterpret_cast<int32_t*>(bitmap + nbw);        // [min(TT*top_k, pt_stride)]
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(sel + TT * top_k);
+  int32_t* ulist = reinterpret_cast<int32_t*>(bitmap + nbw);
   __shared__ int wsum[8];
   __shared__ int n_union;
 
+  // ---- XCD-aware tile: each XCD (workgroup id mod 8) gets a contiguous run of tiles
   const int G = Hq / Hkv;
   const int slices = G / HG;
-  const int g = blockIdx.y / slices;
-  const int hs = blockIdx.y % slices;
-  const int b = blockIdx.z;
-  const int t0 = blockIdx.x * TT;
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int qd8 = nwg >> 3, rd8 = nwg & 7;
+  const int logical = xcd * qd8 + min(xcd, rd8) + slot;
+  const int tile = logical % n_tt;
+  const int rest = logical / n_tt;
+  const int gs = rest % (Hkv * slices);
+  const int b = rest / (Hkv * slices);
+  const int g = gs / slices, hs = gs % slices;
+  const int t0 = tile * TT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int L = kv_lens[b];
   const int base_pos = L - q_len;
 
-  // ---- selections of the tile's tokens and their union (ascending block ids)
   for (int e = tid; e < TT * top_k; e += 256) {
     const int tt = e / top_k, s = e % top_k;
     const int t = t0 + tt;
@@ -90,7 +111,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
   }
   __syncthreads();
   {
-    // exclusive scan of per-word popcounts; each thread owns a contiguous run of words
     const int per = (nbw + 255) / 256;
     const int w0 = tid * per, w1 = min(w0 + per, nbw);
     int cnt = 0;
@@ -118,8 +138,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
   __syncthreads();
   const int U = n_union;
 
-  // ---- this lane's query row
-  const int col = lane & 31;          // row within the wave's 32
+  const int col = lane & 31;
   const int half = lane >> 5;
   const int r = wave * 32 + col;
   const int tt = r / HG;
@@ -127,8 +146,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
   const int t = t0 + tt;
   const bool row_ok = t < q_len;
   const int pos = base_pos + t;
-  const int own = pos / BS;
-  int sp = 0;                          // cursor into this token's ascending selection
+  const int own = row_ok ? pos / BS : -1;
+  int sp = 0;
   const int32_t* mysel = sel + tt * top_k;
 
   bf16x8_t qb[NDS];
@@ -141,115 +160,149 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     }
   }
   const float c2 = scale * LOG2E;
-  float m_i = -INFINITY;  // running max of raw scores
-  float l_i = 0.0f;       // this lane's share of the running sum
+  float m_i = -INFINITY;
+  float l_i = 0.0f;
   f32x16_t o[NDC];
 #pragma unroll
   for (int i = 0; i < NDC; i++)
 #pragma unroll
     for (int e = 0; e < 16; e++) o[i][e] = 0.0f;
 
-  // LDS read addresses (elements)
   const int kread = perm_key(col) * KS + 8 * half;
   const int qd = lane >> 4, ep = (lane & 15) >> 2, s4 = lane & 3;
   const int vread = (8 * (qd >> 1) + ep) * VS + 16 * (qd & 1) + 4 * s4;
+  const bf16_t* kbase = k_cache + (size_t)g * BS * D;   // + page * Hkv * BS * D
+  const bf16_t* vbase = v_cache + (size_t)g * BS * D;
 
-  for (int u = 0; u < U; u++) {
+  uint4 kr[PT], vr[PT];
+  auto gload = [&](int i) {
+    const int u = i / NSUB, h2 = i % NSUB;
     const int j = ulist[u];
     const int p = clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1);
-    const int nvalid = min(BS, L - j * BS);  // tokens of this block that exist
-    __syncthreads();                          // previous tiles fully consumed
-    {
-      const bf16_t* kp = k_cache + (((size_t)p * Hkv + g) * BS) * D;
-      const bf16_t* vp = v_cache + (((size_t)p * Hkv + g) * BS) * D;
-      constexpr int CH = D / 8;   // 16-byte chunks per row
+    const int nvalid = min(BS, L - j * BS) - h2 * SUB;    // valid keys of this sub-block
+    const size_t off = (size_t)p * Hkv * BS * D + (size_t)(h2 * SUB) * D;
 #pragma unroll
-      for (int e0 = 0; e0 < BS * CH; e0 += 256) {
-        const int e = e0 + tid;
-        const int key = e / CH, c = e % CH;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (key < nvalid) {
-          kv = *reinterpret_cast<const uint4*>(kp + (size_t)key * D + 8 * c);
-          vv = *reinterpret_cast<const uint4*>(vp + (size_t)key * D + 8 * c);
+    for (int c = 0; c < PT; c++) {
+      const int e = c * 256 + tid;
+      const int key = e / CH, ch = e % CH;
+      if (key < nvalid) {
+        kr[c] = *reinterpret_cast<const uint4*>(kbase + off + (size_t)key * D + 8 * ch);
+        vr[c] = *reinterpret_cast<const uint4*>(vbase + off + (size_t)key * D + 8 * ch);
+      } else {
+        kr[c] = make_uint4(0, 0, 0, 0);
+        vr[c] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < PT; c++) {
+      const int e = c * 256 + tid;
+      const int key = e / CH, ch = e % CH;
+      *reinterpret_cast<uint4*>(Ks + buf * SUB * KS + key * KS + 8 * ch) = kr[c];
+      *reinterpret_cast<uint4*>(Vs + buf * SUB * VS + key * VS + 8 * ch) = vr[c];
+    }
+  };
+
+  const int NS = U * NSUB;
+  if (NS > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  bool mine = false;
+  for (int i = 0; i < NS; i++) {
+    const int buf = i & 1;
+    if (i + 1 < NS) gload(i + 1);                 // next sub-block's loads in flight
+    const int u = i / NSUB, h2 = i % NSUB;
+    const int j = ulist[u];
+    if (h2 == 0) {
+      mine = row_ok && sp < top_k && mysel[sp] == j;
+      if (mine) sp++;
+    }
+    const uint64_t any = __ballot(mine);
+    if (any != 0) {
+      const bf16_t* Kb = Ks + buf * SUB * KS;
+      const bf16_t* Vb = Vs + buf * SUB * VS;
+      f32x16_t sacc[2];
+      const f32x16_t zero16 = {};
+#pragma unroll
+      for (int kc = 0; kc < 2; kc++) {
+#pragma unroll
+        for (int ks = 0; ks < NDS; ks++) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kb + kread + kc * 32 * KS + 16 * ks);
+          sacc[kc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], ks == 0 ? zero16 : sacc[kc], 0, 0, 0);
         }
-        *reinterpret_cast<uint4*>(Ks + key * KS + 8 * c) = kv;
-        *reinterpret_cast<uint4*>(Vs + key * VS + 8 * c) = vv;
+      }
+      // no masks needed when every row selected this block and it is nobody's own block
+      const bool plain = __ballot(mine && j < own) == ~0ull;
+      float mx = -INFINITY;
+      if (plain) {
+#pragma unroll
+        for (int kc = 0; kc < 2; kc++)
+#pragma unroll
+          for (int e = 0; e < 16; e++) mx = fmaxf(mx, sacc[kc][e]);
+      } else {
+        const int klim = mine ? min(pos - j * BS - h2 * SUB, SUB - 1) : -1;
+#pragma unroll
+        for (int kc = 0; kc < 2; kc++)
+#pragma unroll
+          for (int e = 0; e < 16; e++) {
+            const int key = kc * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
+            const float sv = key <= klim ? sacc[kc][e] : -INFINITY;
+            sacc[kc][e] = sv;
+            mx = fmaxf(mx, sv);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // The reference maximum m_i only moves when a row's maximum exceeds it by more than
+      // 2^8 in exp2 units; below that the probabilities stay <= 256 (exact in the
+      // arithmetic, since softmax does not depend on the subtracted constant).
+      const bool grow = mx * c2 > m_i * c2 + 8.0f;
+      if (__ballot(grow) != 0) {
+        const float m_new = grow ? mx : m_i;
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((m_i - m_use) * c2);
+        l_i *= alpha;
+#pragma unroll
+        for (int i2 = 0; i2 < NDC; i2++)
+#pragma unroll
+          for (int e = 0; e < 16; e++) o[i2][e] *= alpha;
+        m_i = m_new;
+      }
+      const float mc = (m_i == -INFINITY ? 0.0f : m_i) * c2;
+      float rs = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < 2; kc++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kc][e], c2, -mc));
+          sacc[kc][e] = pe;
+          rs += pe;
+        }
+      l_i += rs;
+#pragma unroll
+      for (int st = 0; st < SUB / 16; st++) {
+        const int kc = st >> 1, hh = st & 1;
+        bf16x8_t pb;
+#pragma unroll
+        for (int e = 0; e < 8; e++) pb[e] = (__bf16)sacc[kc][8 * hh + e];
+#pragma unroll
+        for (int dc = 0; dc < NDC; dc++) {
+          const bf16_t* vb = Vb + vread + (16 * st) * VS + 32 * dc;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb + 4 * VS));
+          bf16x8_t va;
+          *reinterpret_cast<s16x4_t*>(&va) = lo;
+          *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
+          o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dc], 0, 0, 0);
+        }
       }
     }
+    if (i + 1 < NS) lstore(buf ^ 1);
     __syncthreads();
-    bool mine = false;
-    if (row_ok && sp < top_k && mysel[sp] == j) {
-      mine = true;
-      sp++;
-    }
-    if (__ballot(mine) == 0) continue;   // no row of this wave selected block j
-
-    // ---- S^T = K . Q^T
-    f32x16_t sacc[NKC];
-#pragma unroll
-    for (int kc = 0; kc < NKC; kc++) {
-#pragma unroll
-      for (int e = 0; e < 16; e++) sacc[kc][e] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < NDS; ks++) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + kread + kc * 32 * KS + 16 * ks);
-        sacc[kc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc[kc], 0, 0, 0);
-      }
-    }
-    // ---- mask, online softmax
-    const int klim = mine ? min(pos - j * BS, BS - 1) : -1;   // last key index allowed
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kc = 0; kc < NKC; kc++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) {
-        const int key = kc * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
-        const float s = key <= klim ? sacc[kc][e] : -INFINITY;
-        sacc[kc][e] = s;
-        mx = fmaxf(mx, s);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_i, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = exp2f((m_i - m_use) * c2);
-    m_i = m_new;
-    const float mc = m_use * c2;
-    float rs = 0.0f;
-#pragma unroll
-    for (int kc = 0; kc < NKC; kc++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) {
-        const float pe = exp2f(fmaf(sacc[kc][e], c2, -mc));
-        sacc[kc][e] = pe;
-        rs += pe;
-      }
-    l_i = l_i * alpha + rs;
-#pragma unroll
-    for (int i = 0; i < NDC; i++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) o[i][e] *= alpha;
-
-    // ---- O^T += V^T . P^T
-#pragma unroll
-    for (int st = 0; st < BS / 16; st++) {
-      const int kc = st >> 1, hh = st & 1;
-      bf16x8_t pb;
-#pragma unroll
-      for (int i = 0; i < 8; i++) pb[i] = (__bf16)sacc[kc][8 * hh + i];
-#pragma unroll
-      for (int dc = 0; dc < NDC; dc++) {
-        const bf16_t* vbase = Vs + vread + (16 * st) * VS + 32 * dc;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vbase));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vbase + 4 * VS));
-        bf16x8_t va;
-        *reinterpret_cast<s16x4_t*>(&va) = lo;
-        *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
-        o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dc], 0, 0, 0);
-      }
-    }
   }
 
-  // ---- epilogue
   const float l = l_i + __shfl_xor(l_i, 32, 64);
   if (!row_ok) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
@@ -259,10 +312,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
 #pragma unroll
     for (int e4 = 0; e4 < 4; e4++) {
       const int d0 = 32 * dc + 8 * e4 + 4 * half;
-      uint2 w;
-      w.x = pack_bf16x2(o[dc][4 * e4 + 0] * inv, o[dc][4 * e4 + 1] * inv);
-      w.y = pack_bf16x2(o[dc][4 * e4 + 2] * inv, o[dc][4 * e4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + d0) = w;
+
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t v4;
+#pragma unroll
+      for (int x = 0; x < 4; x++) v4[x] = (__bf16)(o[dc][4 * e4 + x] * inv);   // v_cvt_pk_bf16_f32 (nearest even)
+      *reinterpret_cast<bf16x4_t*>(op + d0) = v4;
     }
   if (lse && half == 0) lse[((size_t)b * Hq + h) * q_len + t] = m_i * scale + logf(l);
 }
@@ -333,15 +388,6 @@ static int mfma_heads_per_tile(int G) {
   return hg;
 }
 
-static size_t mfma_smem_bytes(const bsg_dims& d, int HG) {
-  const int D = d.head_dim, BS = d.page_size;
-  const int TT = PF_ROWS / HG;
-  const int nbw = (d.pt_stride + 31) / 32;
-  const int ucap = TT * d.top_k < d.pt_stride ? TT * d.top_k : d.pt_stride;
-  return (size_t)BS * (D + PF_KPAD) * 2 + (size_t)BS * (D + PF_VPAD) * 2 + (size_t)TT * d.top_k * 4 +
-         (size_t)nbw * 4 + (size_t)ucap * 4;
-}
-
 hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
                                const void* k_cache, const void* v_cache, const int32_t* page_table,
                                const int32_t* block_idx, float scale, void* out, float* lse,
@@ -349,25 +395,32 @@ hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, cons
   const int G = d.num_q_heads / d.num_kv_heads;
   if (d.dtype == BSG_BF16) {
     const int HG = mfma_heads_per_tile(G);
-    const size_t smem = mfma_smem_bytes(d, HG);
+    const int TT = PF_ROWS / HG;
+    const int nbw = (d.pt_stride + 31) / 32;
+    const int ucap = TT * d.top_k < d.pt_stride ? TT * d.top_k : d.pt_stride;
+    const size_t smem = (size_t)2 * 64 * (d.head_dim + PF_KPAD) * 2 + (size_t)2 * 64 * (d.head_dim + PF_VPAD) * 2 +
+                        (size_t)TT * d.top_k * 4 + (size_t)nbw * 4 + (size_t)ucap * 4;
     if (smem <= 160 * 1024) {
-      const int TT = PF_ROWS / HG;
-      dim3 grid((q_len + TT - 1) / TT, d.num_kv_heads * (G / HG), d.batch);
+      const int n_tt = (q_len + TT - 1) / TT;
+      const long long nwg = (long long)n_tt * d.num_kv_heads * (G / HG) * d.batch;
+      if (nwg < (1LL << 31)) {
+        dim3 grid((unsigned)nwg);
 #define BSG_PF(DD, BB)                                                                                       \
   do {                                                                                                        \
-    auto kfn = attn_prefill_mfma_kernel<DD, BB>;                                                              \
-    { hipError_t ea_ = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); if (ea_ != hipSuccess) return ea_; }            \
+    auto kfn = attn_prefill_mfma_kernel<DD, BB>;                                                             \
+    { hipError_t ea_ = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); if (ea_ != hipSuccess) return ea_; } \
     hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache, \
                        (const bf16_t*)v_cache, page_table, block_idx, scale, (bf16_t*)out, lse, q_len,         \
-                       d.num_q_heads, d.num_kv_heads, HG, d.top_k, d.num_pages, d.pt_stride);                   \
+                       d.num_q_heads, d.num_kv_heads, HG, d.top_k, d.num_pages, d.pt_stride, n_tt);              \
   } while (0)
-      if (d.head_dim == 128) {
-        if (d.page_size == 64) BSG_PF(128, 64); else BSG_PF(128, 128);
-      } else {
-        if (d.page_size == 64) BSG_PF(64, 64); else BSG_PF(64, 128);
-      }
+        if (d.head_dim == 128) {
+          if (d.page_size == 64) BSG_PF(128, 64); else BSG_PF(128, 128);
+        } else {
+          if (d.page_size == 64) BSG_PF(64, 64); else BSG_PF(64, 128);
+        }
 #undef BSG_PF
-      return hipGetLastError();
+        return hipGetLastError();
+      }
     }
   }
   const long long rows = (long long)d.batch * d.num_q_heads * q_len;
