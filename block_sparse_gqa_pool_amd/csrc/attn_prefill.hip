@@ -27,9 +27,10 @@
 namespace bsg {
 
 namespace {
-constexpr int PF_ROWS = 128;   // query rows per workgroup
-constexpr int PF_KPAD = 8;     // K row padding (bf16 elements) in LDS
-constexpr int PF_VPAD = 16;    // V row padding (bf16 elements) in LDS
+constexpr int PF_WAVES = 8;                 // waves per workgroup
+constexpr int PF_ROWS = 32 * PF_WAVES;      // query rows per workgroup (32 per wave)
+constexpr int PF_SUB = 64;                  // keys per staged sub-block
+constexpr int PF_MAX_STAGES = 4;            // depth of the LDS ring of K/V sub-blocks
 constexpr float LOG2E = 1.4426950408889634f;
 }  // namespace
 
@@ -40,12 +41,40 @@ __device__ __forceinline__ int perm_key(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 
+// K and V tiles sit in LDS unpadded, D bf16 per row; the 16-byte chunk c of row r is stored
+// at chunk position c ^ swz(r).  With this permutation the 16 rows read by one ds_read_b128
+// group of the first product, and the 4 rows x 64 bytes read by one half-wave transposing
+// read of the second, fall into distinct banks.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// Asynchronous copy global -> LDS, 16 bytes per lane: lane l's 16 bytes land at byte
+// lds_base + 16 l (gfx950 global_load_lds_dwordx4; the LDS base goes through M0).  Written
+// as inline asm so that the compiler does not serialise the later LDS reads of other ring
+// stages behind it; completion is waited for explicitly with vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
+}
+
+// Wait until at most N of this wave's global->LDS copies are outstanding and all its LDS
+// accesses are done, then workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_copies_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------------------------------
-// Pipelining and scheduling:
-//  * K/V are staged in 64-key sub-blocks, double-buffered in LDS: the global loads of
-//    sub-block i+1 are issued into registers before sub-block i is computed and written to
-//    the other buffer afterwards, so one barrier per sub-block and the load latency hides
-//    behind the matrix work;
+// Data movement and scheduling:
+//  * the union's blocks are streamed in 64-key sub-blocks through a ring of nst LDS stages
+//    (K and V tile each); the copies of sub-block i+nst-1 are issued straight from global
+//    memory into LDS (no register staging) right after the barrier of iteration i, so up to
+//    nst-1 sub-blocks are in flight while one is computed;
+//  * a workgroup is 8 waves (256 query rows = 32 tokens x 8 heads for G = 8): the selections
+//    of neighbouring tokens overlap, so the union grows much slower than the row count and
+//    the K/V bytes fetched per query row drop with the tile size;
 //  * wave-uniform fast path without masks when every row of the wave selected the block
 //    and it is no row's own block; the running maximum (and with it the output) is only
 //    moved when some row's maximum exceeds it by more than a factor 2^8 in probability;
@@ -53,28 +82,30 @@ __device__ __forceinline__ int perm_key(int m) {
 //    XCDs round robin, so consecutive ids are remapped to give each XCD a contiguous range
 //    of tiles, whose selections overlap, in its own L2.
 template <int D, int BS>
-__global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
+__global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ block_idx, float scale, bf16_t* __restrict__ out, float* __restrict__ lse,
-    int q_len, int Hq, int Hkv, int HG, int top_k, int num_pages, int pt_stride, int n_tt) {
-  constexpr int SUB = 64;                 // keys per staged sub-block
+    int q_len, int Hq, int Hkv, int HG, int top_k, int num_pages, int pt_stride, int n_tt, int nst) {
+  constexpr int NT = 64 * PF_WAVES;
+  constexpr int SUB = PF_SUB;
   constexpr int NSUB = BS / SUB;
-  constexpr int KS = D + PF_KPAD;
-  constexpr int VS = D + PF_VPAD;
   constexpr int NDS = D / 16;
   constexpr int NDC = D / 32;
-  constexpr int CH = D / 8;               // 16-byte chunks per row
-  constexpr int PT = SUB * CH / 256;      // chunks per thread per sub-block (each of K and V)
-  extern __shared__ __attribute__((aligned(16))) unsigned char pf2_smem[];
-  bf16_t* Ks = reinterpret_cast<bf16_t*>(pf2_smem);           // [2][SUB][KS]
-  bf16_t* Vs = Ks + 2 * SUB * KS;                              // [2][SUB][VS]
+  constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  constexpr int TILE = SUB * D * 2;                // bytes of one K (or V) sub-block tile
+  constexpr int STG = 2 * TILE;                    // bytes of one ring stage
+  constexpr int NCP = TILE / 1024 / PF_WAVES;      // 1 KiB copies per wave per tile
+  static_assert(NCP >= 1 && NCP * 1024 * PF_WAVES == TILE, "tile split");
+  extern __shared__ __attribute__((aligned(16))) unsigned char pf_smem[];
   const int TT = PF_ROWS / HG;
-  int32_t* sel = reinterpret_cast<int32_t*>(Vs + 2 * SUB * VS);
+  int32_t* sel = reinterpret_cast<int32_t*>(pf_smem + nst * STG);   // [TT][top_k]
   const int nbw = (pt_stride + 31) >> 5;
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(sel + TT * top_k);
-  int32_t* ulist = reinterpret_cast<int32_t*>(bitmap + nbw);
-  __shared__ int wsum[8];
+  int32_t* ulist = reinterpret_cast<int32_t*>(bitmap + nbw);          // union, ascending
+  const int ucap = min(TT * top_k, pt_stride);
+  int32_t* upage = ulist + ucap;                                       // its physical pages
+  __shared__ int wsum[PF_WAVES];
   __shared__ int n_union;
 
   // ---- XCD-aware tile: each XCD (workgroup id mod 8) gets a contiguous run of tiles
@@ -96,22 +127,23 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
   const int L = kv_lens[b];
   const int base_pos = L - q_len;
 
-  for (int e = tid; e < TT * top_k; e += 256) {
+  // ---- the tile's selections and their union (ascending block ids)
+  for (int e = tid; e < TT * top_k; e += NT) {
     const int tt = e / top_k, s = e % top_k;
     const int t = t0 + tt;
     int j = -1;
     if (t < q_len) j = block_idx[(((size_t)b * Hkv + g) * q_len + t) * top_k + s];
     sel[e] = (j >= 0 && j < pt_stride) ? j : (j >= pt_stride ? pt_stride - 1 : -1);
   }
-  for (int w = tid; w < nbw; w += 256) bitmap[w] = 0u;
+  for (int w = tid; w < nbw; w += NT) bitmap[w] = 0u;
   __syncthreads();
-  for (int e = tid; e < TT * top_k; e += 256) {
+  for (int e = tid; e < TT * top_k; e += NT) {
     const int j = sel[e];
     if (j >= 0) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
   {
-    const int per = (nbw + 255) / 256;
+    const int per = (nbw + NT - 1) / NT;
     const int w0 = tid * per, w1 = min(w0 + per, nbw);
     int cnt = 0;
     for (int w = w0; w < w1; w++) cnt += __popc(bitmap[w]);
@@ -125,19 +157,23 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     __syncthreads();
     int off = incl - cnt;
     for (int w2 = 0; w2 < wave; w2++) off += wsum[w2];
-    if (tid == 255) n_union = off + cnt;
+    if (tid == NT - 1) n_union = off + cnt;
     for (int w = w0; w < w1; w++) {
       uint32_t bits = bitmap[w];
       while (bits) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1;
-        ulist[off++] = (w << 5) + bit;
+        const int j = (w << 5) + bit;
+        ulist[off] = j;
+        upage[off] = clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1);
+        off++;
       }
     }
   }
   __syncthreads();
   const int U = n_union;
 
+  // ---- this lane's query row
   const int col = lane & 31;
   const int half = lane >> 5;
   const int r = wave * 32 + col;
@@ -158,6 +194,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
       uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
       qb[ks] = *reinterpret_cast<bf16x8_t*>(&v);
     }
+    // Consume the loads here: the compiler then waits for them before the loop instead of
+    // at the first use inside it, where its wait would also drain the ring's copies.
+#pragma unroll
+    for (int ks = 0; ks < NDS; ks++) asm volatile("" ::"v"(qb[ks]));
   }
   const float c2 = scale * LOG2E;
   float m_i = -INFINITY;
@@ -168,69 +208,80 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
 #pragma unroll
     for (int e = 0; e < 16; e++) o[i][e] = 0.0f;
 
-  const int kread = perm_key(col) * KS + 8 * half;
-  const int qd = lane >> 4, ep = (lane & 15) >> 2, s4 = lane & 3;
-  const int vread = (8 * (qd >> 1) + ep) * VS + 16 * (qd & 1) + 4 * s4;
+  // LDS byte offsets of this lane's operand reads inside a stage
+  int koff[NDS];                 // first product: K row perm_key(col) (+32 per kc), chunk 2 ks + half
+  {
+    const int kr = perm_key(col);
+#pragma unroll
+    for (int ks = 0; ks < NDS; ks++) koff[ks] = kr * (D * 2) + (((2 * ks + half) ^ tile_swz<D>(kr)) << 4);
+  }
+  int voff[NDC][2];              // second product: V rows 16 st + 8 (qd>>1) + ep (+4), 8 bytes
+  {
+    const int qd = lane >> 4, ep = (lane & 15) >> 2, s4 = lane & 3;
+#pragma unroll
+    for (int dc = 0; dc < NDC; dc++)
+#pragma unroll
+      for (int hi = 0; hi < 2; hi++) {
+        const int vr = 8 * (qd >> 1) + ep + 4 * hi;
+        const int ch = 4 * dc + 2 * (qd & 1) + (s4 >> 1);
+        voff[dc][hi] = TILE + vr * (D * 2) + ((ch ^ tile_swz<D>(vr)) << 4) + 8 * (s4 & 1);
+      }
+  }
+  // this lane's share of the copies of one stage: tile rows and source chunk per copy
+  int crow[NCP], cchunk[NCP];
+#pragma unroll
+  for (int c = 0; c < NCP; c++) {
+    const int e = (wave + PF_WAVES * c) * 64 + lane;   // 16-byte slot of the tile
+    crow[c] = e / CPR;
+    cchunk[c] = ((e % CPR) ^ tile_swz<D>(crow[c])) * 8;
+  }
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)pf_smem;
   const bf16_t* kbase = k_cache + (size_t)g * BS * D;   // + page * Hkv * BS * D
   const bf16_t* vbase = v_cache + (size_t)g * BS * D;
-
-  uint4 kr[PT], vr[PT];
-  auto gload = [&](int i) {
+  auto issue = [&](int i) {                            // copies of sub-block i into stage i % nst
     const int u = i / NSUB, h2 = i % NSUB;
-    const int j = ulist[u];
-    const int p = clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1);
-    const int nvalid = min(BS, L - j * BS) - h2 * SUB;    // valid keys of this sub-block
-    const size_t off = (size_t)p * Hkv * BS * D + (size_t)(h2 * SUB) * D;
+    const int j = __builtin_amdgcn_readfirstlane(ulist[u]);
+    const int p = __builtin_amdgcn_readfirstlane(upage[u]);
+    const int nvb = min(BS, L - j * BS);                 // valid keys of block j (>= 1)
+    const size_t poff = (size_t)p * Hkv * BS * D;
+    const uint32_t sb = smem_base + (uint32_t)((i % nst) * STG);
 #pragma unroll
-    for (int c = 0; c < PT; c++) {
-      const int e = c * 256 + tid;
-      const int key = e / CH, ch = e % CH;
-      if (key < nvalid) {
-        kr[c] = *reinterpret_cast<const uint4*>(kbase + off + (size_t)key * D + 8 * ch);
-        vr[c] = *reinterpret_cast<const uint4*>(vbase + off + (size_t)key * D + 8 * ch);
-      } else {
-        kr[c] = make_uint4(0, 0, 0, 0);
-        vr[c] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < PT; c++) {
-      const int e = c * 256 + tid;
-      const int key = e / CH, ch = e % CH;
-      *reinterpret_cast<uint4*>(Ks + buf * SUB * KS + key * KS + 8 * ch) = kr[c];
-      *reinterpret_cast<uint4*>(Vs + buf * SUB * VS + key * VS + 8 * ch) = vr[c];
+    for (int c = 0; c < NCP; c++) {
+      const int key = h2 * SUB + crow[c];
+      // slots past the valid keys copy key 0 instead: finite data, masked out of the scores
+      const size_t eo = poff + (size_t)(key < nvb ? key : 0) * D + cchunk[c];
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wave + PF_WAVES * c) * 1024));
+      lds_dma16(kbase + eo, dst);
+      lds_dma16(vbase + eo, dst + TILE);
     }
   };
 
   const int NS = U * NSUB;
-  if (NS > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+  for (int i = 0; i < nst - 1 && i < NS; i++) issue(i);
   bool mine = false;
   for (int i = 0; i < NS; i++) {
-    const int buf = i & 1;
-    if (i + 1 < NS) gload(i + 1);                 // next sub-block's loads in flight
+    // stage i has landed once at most min(nst-2, NS-1-i) younger stages are outstanding
+    const int ahead = min(nst - 2, NS - 1 - i);
+    if (ahead >= 2) wait_copies_barrier<4 * NCP>();
+    else if (ahead == 1) wait_copies_barrier<2 * NCP>();
+    else wait_copies_barrier<0>();
+    if (i + nst - 1 < NS) issue(i + nst - 1);          // into the stage everyone finished with
     const int u = i / NSUB, h2 = i % NSUB;
     const int j = ulist[u];
     if (h2 == 0) {
       mine = row_ok && sp < top_k && mysel[sp] == j;
       if (mine) sp++;
     }
-    const uint64_t any = __ballot(mine);
-    if (any != 0) {
-      const bf16_t* Kb = Ks + buf * SUB * KS;
-      const bf16_t* Vb = Vs + buf * SUB * VS;
+    const int kfirst = j * BS + h2 * SUB;               // position of the sub-block's first key
+    if (__ballot(mine && kfirst <= pos) != 0) {
+      const unsigned char* sbp = pf_smem + (i % nst) * STG;
       f32x16_t sacc[2];
       const f32x16_t zero16 = {};
 #pragma unroll
       for (int kc = 0; kc < 2; kc++) {
 #pragma unroll
         for (int ks = 0; ks < NDS; ks++) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kb + kread + kc * 32 * KS + 16 * ks);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sbp + koff[ks] + kc * 32 * D * 2);
           sacc[kc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], ks == 0 ? zero16 : sacc[kc], 0, 0, 0);
         }
       }
@@ -243,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
 #pragma unroll
           for (int e = 0; e < 16; e++) mx = fmaxf(mx, sacc[kc][e]);
       } else {
-        const int klim = mine ? min(pos - j * BS - h2 * SUB, SUB - 1) : -1;
+        const int klim = mine ? min(pos - kfirst, SUB - 1) : -1;
 #pragma unroll
         for (int kc = 0; kc < 2; kc++)
 #pragma unroll
@@ -289,9 +340,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
         for (int e = 0; e < 8; e++) pb[e] = (__bf16)sacc[kc][8 * hh + e];
 #pragma unroll
         for (int dc = 0; dc < NDC; dc++) {
-          const bf16_t* vb = Vb + vread + (16 * st) * VS + 32 * dc;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb + 4 * VS));
+          const unsigned char* vb = sbp + st * 16 * D * 2;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb + voff[dc][0]));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb + voff[dc][1]));
           bf16x8_t va;
           *reinterpret_cast<s16x4_t*>(&va) = lo;
           *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
@@ -299,8 +350,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
         }
       }
     }
-    if (i + 1 < NS) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   const float l = l_i + __shfl_xor(l_i, 32, 64);
@@ -312,7 +361,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
 #pragma unroll
     for (int e4 = 0; e4 < 4; e4++) {
       const int d0 = 32 * dc + 8 * e4 + 4 * half;
-
       typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
       bf16x4_t v4;
 #pragma unroll
@@ -398,8 +446,11 @@ hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, cons
     const int TT = PF_ROWS / HG;
     const int nbw = (d.pt_stride + 31) / 32;
     const int ucap = TT * d.top_k < d.pt_stride ? TT * d.top_k : d.pt_stride;
-    const size_t smem = (size_t)2 * 64 * (d.head_dim + PF_KPAD) * 2 + (size_t)2 * 64 * (d.head_dim + PF_VPAD) * 2 +
-                        (size_t)TT * d.top_k * 4 + (size_t)nbw * 4 + (size_t)ucap * 4;
+    const size_t fixed = (size_t)TT * d.top_k * 4 + (size_t)nbw * 4 + (size_t)ucap * 8;
+    const size_t stage = (size_t)2 * PF_SUB * d.head_dim * 2;
+    int nst = PF_MAX_STAGES;                       // deepest ring that fits the 160 KiB of LDS
+    while (nst > 2 && fixed + nst * stage > 160 * 1024) nst--;
+    const size_t smem = fixed + nst * stage;
     if (smem <= 160 * 1024) {
       const int n_tt = (q_len + TT - 1) / TT;
       const long long nwg = (long long)n_tt * d.num_kv_heads * (G / HG) * d.batch;
@@ -409,9 +460,10 @@ hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, cons
   do {                                                                                                        \
     auto kfn = attn_prefill_mfma_kernel<DD, BB>;                                                             \
     { hipError_t ea_ = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); if (ea_ != hipSuccess) return ea_; } \
-    hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache, \
-                       (const bf16_t*)v_cache, page_table, block_idx, scale, (bf16_t*)out, lse, q_len,         \
-                       d.num_q_heads, d.num_kv_heads, HG, d.top_k, d.num_pages, d.pt_stride, n_tt);              \
+    hipLaunchKernelGGL(kfn, grid, dim3(64 * PF_WAVES), smem, stream, (const bf16_t*)q, kv_lens,             \
+                       (const bf16_t*)k_cache, (const bf16_t*)v_cache, page_table, block_idx, scale,          \
+                       (bf16_t*)out, lse, q_len, d.num_q_heads, d.num_kv_heads, HG, d.top_k, d.num_pages,    \
+                       d.pt_stride, n_tt, nst);                                                               \
   } while (0)
         if (d.head_dim == 128) {
           if (d.page_size == 64) BSG_PF(128, 64); else BSG_PF(128, 128);
