@@ -227,54 +227,85 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
         voff[dc][hi] = TILE + vr * (D * 2) + ((ch ^ tile_swz<D>(vr)) << 4) + 8 * (s4 & 1);
       }
   }
-  // this lane's share of the copies of one stage: tile rows and source chunk per copy
-  int crow[NCP], cchunk[NCP];
+  // this lane's share of the copies of one stage: tile row and element offset per copy
+  int crow[NCP], coff[NCP];
 #pragma unroll
   for (int c = 0; c < NCP; c++) {
     const int e = (wave + PF_WAVES * c) * 64 + lane;   // 16-byte slot of the tile
     crow[c] = e / CPR;
-    cchunk[c] = ((e % CPR) ^ tile_swz<D>(crow[c])) * 8;
+    coff[c] = crow[c] * D + ((e % CPR) ^ tile_swz<D>(crow[c])) * 8;
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)pf_smem;
+  const uint32_t wave_slot = __builtin_amdgcn_readfirstlane(wave * 1024);
   const bf16_t* kbase = k_cache + (size_t)g * BS * D;   // + page * Hkv * BS * D
   const bf16_t* vbase = v_cache + (size_t)g * BS * D;
-  auto issue = [&](int i) {                            // copies of sub-block i into stage i % nst
-    const int u = i / NSUB, h2 = i % NSUB;
-    const int j = __builtin_amdgcn_readfirstlane(ulist[u]);
-    const int p = __builtin_amdgcn_readfirstlane(upage[u]);
-    const int nvb = min(BS, L - j * BS);                 // valid keys of block j (>= 1)
-    const size_t poff = (size_t)p * Hkv * BS * D;
-    const uint32_t sb = smem_base + (uint32_t)((i % nst) * STG);
+  // copies of sub-block ic (block cj in page cp) into LDS stage c_stage; ic advances
+  int ic = 0, c_stage = 0;
+  auto issue = [&](int cj, int cp) {
+    const int h2 = ic % NSUB;
+    const int nvb = min(BS, L - cj * BS);                // valid keys of the block (>= 1)
+    const size_t poff = (size_t)cp * Hkv * BS * D + (size_t)h2 * SUB * D;
+    const bf16_t* kp = kbase + poff;
+    const bf16_t* vp = vbase + poff;
+    const uint32_t sb = smem_base + (uint32_t)(c_stage * STG) + wave_slot;
+    if (nvb >= (h2 + 1) * SUB) {                         // every key of the sub-block is valid
 #pragma unroll
-    for (int c = 0; c < NCP; c++) {
-      const int key = h2 * SUB + crow[c];
+      for (int c = 0; c < NCP; c++) {
+        lds_dma16(kp + coff[c], sb + c * PF_WAVES * 1024);
+        lds_dma16(vp + coff[c], sb + c * PF_WAVES * 1024 + TILE);
+      }
+    } else {
       // slots past the valid keys copy key 0 instead: finite data, masked out of the scores
-      const size_t eo = poff + (size_t)(key < nvb ? key : 0) * D + cchunk[c];
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wave + PF_WAVES * c) * 1024));
-      lds_dma16(kbase + eo, dst);
-      lds_dma16(vbase + eo, dst + TILE);
+#pragma unroll
+      for (int c = 0; c < NCP; c++) {
+        const int eo = h2 * SUB + crow[c] < nvb ? coff[c] : coff[c] - (h2 * SUB + crow[c]) * D;
+        lds_dma16(kp + eo, sb + c * PF_WAVES * 1024);
+        lds_dma16(vp + eo, sb + c * PF_WAVES * 1024 + TILE);
+      }
     }
+    ic++;
+    c_stage = c_stage + 1 == nst ? 0 : c_stage + 1;
   };
 
   const int NS = U * NSUB;
-  for (int i = 0; i < nst - 1 && i < NS; i++) issue(i);
+  while (ic < nst - 1 && ic < NS) {
+    const int u = ic / NSUB;
+    issue(__builtin_amdgcn_readfirstlane(ulist[u]), __builtin_amdgcn_readfirstlane(upage[u]));
+  }
+  // the block schedule is read one block ahead, so that no LDS latency sits between the
+  // barrier and the first product: jn = next union block, selc = this row's next selection
+  int jn = U > 0 ? ulist[0] : 0;
+  int selc = row_ok ? mysel[0] : -1;
+  int j = 0;
   bool mine = false;
+  int r_stage = 0;                                      // stage of sub-block i
   for (int i = 0; i < NS; i++) {
     // stage i has landed once at most min(nst-2, NS-1-i) younger stages are outstanding
     const int ahead = min(nst - 2, NS - 1 - i);
     if (ahead >= 2) wait_copies_barrier<4 * NCP>();
     else if (ahead == 1) wait_copies_barrier<2 * NCP>();
     else wait_copies_barrier<0>();
-    if (i + nst - 1 < NS) issue(i + nst - 1);          // into the stage everyone finished with
-    const int u = i / NSUB, h2 = i % NSUB;
-    const int j = ulist[u];
+    // schedule entry of this iteration's copy, read now and used at the end
+    int cj = 0, cp = 0;
+    if (ic < NS) {
+      cj = ulist[ic / NSUB];
+      cp = upage[ic / NSUB];
+    }
+    const int h2 = i % NSUB;
     if (h2 == 0) {
-      mine = row_ok && sp < top_k && mysel[sp] == j;
-      if (mine) sp++;
+      j = __builtin_amdgcn_readfirstlane(jn);
+      const int u = i / NSUB;
+      if (u + 1 < U) jn = ulist[u + 1];
+      mine = row_ok && selc == j;
+      if (mine) {
+        sp++;
+        selc = sp < top_k ? mysel[sp] : -1;
+      }
     }
     const int kfirst = j * BS + h2 * SUB;               // position of the sub-block's first key
-    if (__ballot(mine && kfirst <= pos) != 0) {
-      const unsigned char* sbp = pf_smem + (i % nst) * STG;
+    const bool act = mine && kfirst <= pos;             // the row attends to this sub-block
+    if (__ballot(act) != 0) {
+      const unsigned char* sbp = pf_smem + r_stage * STG;
       f32x16_t sacc[2];
       const f32x16_t zero16 = {};
 #pragma unroll
@@ -285,59 +316,60 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
           sacc[kc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], ks == 0 ? zero16 : sacc[kc], 0, 0, 0);
         }
       }
-      // no masks needed when every row selected this block and it is nobody's own block
-      const bool plain = __ballot(mine && j < own) == ~0ull;
-      float mx = -INFINITY;
-      if (plain) {
-#pragma unroll
-        for (int kc = 0; kc < 2; kc++)
-#pragma unroll
-          for (int e = 0; e < 16; e++) mx = fmaxf(mx, sacc[kc][e]);
-      } else {
-        const int klim = mine ? min(pos - kfirst, SUB - 1) : -1;
+      if (__ballot(act && j == own) != 0) {             // causal mask inside the own block
+        const int klim = j == own ? pos - kfirst : SUB - 1;
 #pragma unroll
         for (int kc = 0; kc < 2; kc++)
 #pragma unroll
           for (int e = 0; e < 16; e++) {
             const int key = kc * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
-            const float sv = key <= klim ? sacc[kc][e] : -INFINITY;
-            sacc[kc][e] = sv;
-            mx = fmaxf(mx, sv);
+            sacc[kc][e] = key <= klim ? sacc[kc][e] : -INFINITY;
           }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // The reference maximum m_i only moves when a row's maximum exceeds it by more than
-      // 2^8 in exp2 units; below that the probabilities stay <= 256 (exact in the
-      // arithmetic, since softmax does not depend on the subtracted constant).
-      const bool grow = mx * c2 > m_i * c2 + 8.0f;
-      if (__ballot(grow) != 0) {
-        const float m_new = grow ? mx : m_i;
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((m_i - m_use) * c2);
+      // Probabilities against the row's reference maximum m_i, which only moves when the
+      // sum would leave a safe range: softmax does not depend on the subtracted constant,
+      // so the weights only need to stay finite (the sum <= 2^64).  Rows that do not
+      // attend get probability 0 through an infinite offset.  A row seen for the first
+      // time (m_i = -inf) gets an infinite sum and so also takes the exact update.
+      bf16x8_t pb[SUB / 16];
+      float rs = 0.0f;
+      auto probs = [&]() {
+        const float mc = act ? m_i * c2 : INFINITY;
+        rs = 0.0f;
+#pragma unroll
+        for (int st = 0; st < SUB / 16; st++) {
+          const int kc = st >> 1, hh = st & 1;
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kc][8 * hh + e], c2, -mc));
+            pb[st][e] = (__bf16)pe;
+            rs += pe;
+          }
+        }
+      };
+      probs();
+      const bool bad = !(rs <= 0x1p64f);
+      if (__ballot(bad) != 0) {                          // rare: move the reference maximum
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kc = 0; kc < 2; kc++)
+#pragma unroll
+          for (int e = 0; e < 16; e++) mx = fmaxf(mx, sacc[kc][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const bool bad_row = bad || __shfl_xor((int)bad, 32, 64) != 0;
+        const float m_new = (act && bad_row) ? fmaxf(m_i, mx) : m_i;
+        const float alpha = m_new == m_i ? 1.0f : __builtin_amdgcn_exp2f((m_i - m_new) * c2);
         l_i *= alpha;
 #pragma unroll
         for (int i2 = 0; i2 < NDC; i2++)
 #pragma unroll
           for (int e = 0; e < 16; e++) o[i2][e] *= alpha;
         m_i = m_new;
+        probs();
       }
-      const float mc = (m_i == -INFINITY ? 0.0f : m_i) * c2;
-      float rs = 0.0f;
-#pragma unroll
-      for (int kc = 0; kc < 2; kc++)
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kc][e], c2, -mc));
-          sacc[kc][e] = pe;
-          rs += pe;
-        }
       l_i += rs;
 #pragma unroll
       for (int st = 0; st < SUB / 16; st++) {
-        const int kc = st >> 1, hh = st & 1;
-        bf16x8_t pb;
-#pragma unroll
-        for (int e = 0; e < 8; e++) pb[e] = (__bf16)sacc[kc][8 * hh + e];
 #pragma unroll
         for (int dc = 0; dc < NDC; dc++) {
           const unsigned char* vb = sbp + st * 16 * D * 2;
@@ -346,10 +378,13 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
           bf16x8_t va;
           *reinterpret_cast<s16x4_t*>(&va) = lo;
           *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
-          o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dc], 0, 0, 0);
+          o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[dc], 0, 0, 0);
         }
       }
     }
+    // next copy, into the stage everyone finished with before this iteration's barrier
+    if (ic < NS) issue(__builtin_amdgcn_readfirstlane(cj), __builtin_amdgcn_readfirstlane(cp));
+    r_stage = r_stage + 1 == nst ? 0 : r_stage + 1;
   }
 
   const float l = l_i + __shfl_xor(l_i, 32, 64);
