@@ -136,16 +136,33 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const float* __res
   const int d = threadIdx.x;
   const float* base = ws + (((size_t)b * Hkv + g) * nsplit) * G * (D + 2) + (size_t)hh * (D + 2);
   const size_t sstride = (size_t)G * (D + 2);
-  float m = -INFINITY;
-  for (int s = 0; s < nsplit; s++) m = fmaxf(m, base[s * sstride]);
-  float l = 0.0f, o = 0.0f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < nsplit; s++) {
-      const float ms = base[s * sstride];
-      if (ms == -INFINITY) continue;
-      const float w = __expf(ms - m);
-      l += base[s * sstride + 1] * w;
-      o += base[s * sstride + 2 + d] * w;
+  // all partials of the row in one batch of loads (up to 8 splits per pass)
+  float m = -INFINITY, l = 0.0f, o = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float ms[8], ls[8], os[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int s = s0 + u;
+      const bool v = s < nsplit;
+      ms[u] = v ? base[s * sstride] : -INFINITY;
+      ls[u] = v ? base[s * sstride + 1] : 0.0f;
+      os[u] = v ? base[s * sstride + 2 + d] : 0.0f;
+    }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < 8; u++) mn = fmaxf(mn, ms[u]);
+    if (mn != -INFINITY) {
+      const float sc = m == -INFINITY ? 0.0f : __expf(m - mn);
+      l *= sc;
+      o *= sc;
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        if (ms[u] == -INFINITY) continue;
+        const float w = __expf(ms[u] - mn);
+        l += ls[u] * w;
+        o += os[u] * w;
+      }
+      m = mn;
     }
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
@@ -175,53 +192,81 @@ typedef __attribute__((address_space(3))) s16x4_t* dm_lds_s16x4_ptr;
 // cnt-th largest key overall (at least cnt keys reach it), so the kept keys are among the
 // list keys >= tau -- typically little more than cnt of them.  Those survivors are ranked
 // against each other; ranks below cnt are kept.  wl receives the kept block ids ascending.
-__device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, int nchunks, int m, int T, int cnt,
-                                       uint64_t* L, uint64_t* S, int* selj, int* wl, int* counters,
-                                       uint64_t* tau_s) {
+// Number of keys in a[0, n) that are larger than key; a is 16-byte aligned and read two
+// keys per 16-byte load, 16 keys per batch.
+__device__ __forceinline__ int count_above(const uint64_t* a, int n, uint64_t key) {
+  int rank = 0, i = 0;
+  for (; i + 16 <= n; i += 16) {
+    ulonglong2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) v[u] = reinterpret_cast<const ulonglong2*>(a + i)[u];
+#pragma unroll
+    for (int u = 0; u < 8; u++) rank += (v[u].x > key ? 1 : 0) + (v[u].y > key ? 1 : 0);
+  }
+  for (; i < n; i++) rank += a[i] > key ? 1 : 0;
+  return rank;
+}
+
+// Selection prologue of the fused decode step (one workgroup, all threads).  `lists` holds,
+// per chunk of candidate blocks, the chunk's best m = top_k - 1 keys sorted descending (0 =
+// none).  The cnt-th largest of the chunks' first T keys is a lower bound `tau` of the
+// cnt-th largest key overall (at least cnt keys reach it), so the kept keys are among the
+// list keys >= tau -- a prefix of every list, typically little more than cnt keys in all.
+// Those survivors are ranked against each other; sel[r] receives the block id of rank r
+// (r < cnt, largest score first).
+__device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, int nchunks, int m, int lt, int cnt,
+                                       uint64_t* L, uint64_t* S, int* sel, int* counter, uint64_t* tau_s) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < nchunks * m; e += 256) L[e] = lists_row[e];
+  const int T = 1 << lt;                      // leading keys taken from every chunk list
+  const int NT = nchunks << lt;
+  const int NL = nchunks * m;
+  uint64_t* tops = S;                         // [NT], reused for the survivors afterwards
   if (tid == 0) {
-    counters[0] = 0;   // valid tops
-    counters[1] = 0;   // survivors
+    *counter = 0;
     *tau_s = 1ull;
   }
+  for (int e0 = 0; e0 < NL; e0 += 4 * 256) {  // lists -> LDS, 4 loads in flight per thread
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = e0 + u * 256 + tid;
+      v[u] = e < NL ? lists_row[e] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = e0 + u * 256 + tid;
+      if (e < NL) L[e] = v[u];
+    }
+  }
   __syncthreads();
-  const int NT = nchunks * T;
-  for (int e = tid; e < NT; e += 256)
-    if (L[(e / T) * m + (e % T)] != 0ull) atomicAdd(&counters[0], 1);
-  __syncthreads();
-  if (counters[0] >= cnt) {
+  int nvalid = 0;
+  for (int e0 = 0; e0 < NT; e0 += 256) {
+    const int e = e0 + tid;
+    const int i = e & (T - 1);                // position in the chunk's list (T may exceed m)
+    const uint64_t key = (e < NT && i < m) ? L[(e >> lt) * m + i] : 0ull;
+    if (e < NT) tops[e] = key;
+    nvalid += __syncthreads_count(key != 0ull);
+  }
+  if (nvalid >= cnt) {
     for (int e = tid; e < NT; e += 256) {
-      const uint64_t key = L[(e / T) * m + (e % T)];
-      if (key == 0ull) continue;
-      int rank = 0;
-      for (int e2 = 0; e2 < NT; e2++) rank += L[(e2 / T) * m + (e2 % T)] > key ? 1 : 0;
-      if (rank == cnt - 1) *tau_s = key;
+      const uint64_t key = tops[e];
+      if (key != 0ull && count_above(tops, NT, key) == cnt - 1) *tau_s = key;
     }
   }
   __syncthreads();
   const uint64_t tau = *tau_s;
-  for (int c = tid; c < nchunks; c += 256) {
-    for (int i = 0; i < m; i++) {
-      const uint64_t key = L[c * m + i];
-      if (key < tau) break;
-      S[atomicAdd(&counters[1], 1)] = key;
-    }
+  for (int c = tid; c < nchunks; c += 256) {   // this chunk's keys >= tau, appended as one run
+    int nc = 0;
+    while (nc < m && L[c * m + nc] >= tau) nc++;
+    const int at = nc > 0 ? atomicAdd(counter, nc) : 0;
+    for (int i = 0; i < nc; i++) S[at + i] = L[c * m + i];
   }
   __syncthreads();
-  const int ns = counters[1];
+  const int ns = *counter;
   for (int e = tid; e < ns; e += 256) {
     const uint64_t key = S[e];
-    int rank = 0;
-    for (int e2 = 0; e2 < ns; e2++) rank += S[e2] > key ? 1 : 0;
-    if (rank < cnt) selj[rank] = sel_key_index(key);
-  }
-  __syncthreads();
-  if (tid < cnt) {
-    const int ji = selj[tid];
-    int r = 0;
-    for (int i = 0; i < cnt; i++) r += selj[i] < ji ? 1 : 0;
-    wl[r] = ji;
+    const int rank = count_above(S, ns, key);
+    if (rank < cnt) sel[rank] = sel_key_index(key);
   }
   __syncthreads();
 }
@@ -231,7 +276,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table, int32_t* __restrict__ block_idx,
     const uint64_t* __restrict__ lists, float scale, float* __restrict__ part, int Hq, int Hkv, int top_k,
-    int num_pages, int pt_stride, int nwg, int ppw, int nchunks, int T) {
+    int num_pages, int pt_stride, int nwg, int ppw, int nchunks, int lt) {
   constexpr int NDS = D / 32;          // k-steps of the score product
   constexpr int NDT = D / 16;          // 16-wide d tiles of the output
   constexpr int VS = D + DM_VPAD;      // LDS row stride of V (elements)
@@ -246,9 +291,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
   const int pos = L - 1;
   int32_t* sl = block_idx + ((size_t)b * Hkv + g) * top_k;
   const float c2 = scale * 1.4426950408889634f;
-  __shared__ int wl[64];          // fused: the selection, ascending, own block last
-  __shared__ int selj[64];
-  __shared__ int cnts[2];
+  __shared__ int wl[64];          // fused: the selection in rank order, own block at [cnt]
+  __shared__ int cnt_s;
   __shared__ uint64_t tau_s;
   if (FUSED) {
     const int m = top_k - 1;
@@ -256,14 +300,12 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
     const int cnt = min(m, min(own, pt_stride));
     if (cnt > 0) {
       uint64_t* Lk = reinterpret_cast<uint64_t*>(dm_smem);
-      decode_select_prologue(lists + ((size_t)b * Hkv + g) * nchunks * m, nchunks, m, T, cnt, Lk,
-                             Lk + (size_t)nchunks * m, selj, wl, cnts, &tau_s);
+      decode_select_prologue(lists + ((size_t)b * Hkv + g) * nchunks * m, nchunks, m, lt, cnt, Lk,
+                             Lk + (((size_t)nchunks * m + 1) & ~(size_t)1), wl, &cnt_s, &tau_s);
     }
     if (tid == 0) wl[cnt] = own;
     for (int i = cnt + 1 + tid; i < top_k; i += 256) wl[i] = -1;
     __syncthreads();
-    if (blockIdx.x == 0)
-      for (int i = tid; i < top_k; i += 256) sl[i] = wl[i];
   }
 
   bf16x8_t qb[NDS];
@@ -380,6 +422,20 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
+  if (FUSED && blockIdx.x == 0) {  // the selection, ascending, to block_idx (own block last)
+    for (int i = tid; i < top_k; i += 256) {
+      const int v = wl[i];
+      int r = i;
+      if (v >= 0) {
+        r = 0;
+        for (int i2 = 0; i2 < top_k; i2++) {
+          const int o = wl[i2];
+          r += (o >= 0 && o < v) ? 1 : 0;
+        }
+      }
+      sl[r] = v;
+    }
+  }
   // per-head sum over the four lanes of the head
   float l_h = l_run + __shfl_xor(l_run, 16, 64);
   l_h += __shfl_xor(l_h, 32, 64);
@@ -466,7 +522,6 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
                               const void* v_cache, const int32_t* page_table, const int32_t* block_idx,
                               float scale, void* workspace, void* out, float* lse, hipStream_t stream) {
   if (decode_mfma_path(d)) {
-    const int G = d.num_q_heads / d.num_kv_heads;
     const int nwg = decode_mfma_nwg(d);
     float* part = (float*)workspace;
     const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
@@ -545,7 +600,27 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
   return hipGetLastError();
 }
 
-bool decode_step_fused_supported(const bsg_dims& d) { return decode_mfma_path(d) && decode_select_supported(d, 1); }
+// LDS of the fused decode attention kernel: V staging, the wave merge, or the selection
+// prologue's lists plus its tops / survivors, whichever is largest.  lt: log2 of the
+// number of leading keys the prologue takes from every chunk list.
+static size_t decode_step_smem(const bsg_dims& d, int* lt_out) {
+  const int nchunks = decode_select_nchunks(d);
+  const int m = d.top_k - 1;
+  int lt = 0;                                   // tops: 2^lt leading keys of every list, >= 2 m of them
+  while (m > 0 && (nchunks << lt) < 2 * m && (1 << lt) < m) lt++;
+  const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
+  const size_t smem_m = (size_t)4 * 16 * (d.head_dim + 2) * sizeof(float);
+  const size_t nl = (size_t)nchunks * (m > 0 ? m : 1);
+  const size_t nt = (size_t)nchunks << lt;
+  const size_t smem_s = (((nl + 1) & ~(size_t)1) + (nl > nt ? nl : nt)) * sizeof(uint64_t);   // S 16-byte aligned
+  size_t smem = smem_v > smem_m ? smem_v : smem_m;
+  if (lt_out) *lt_out = lt;
+  return smem > smem_s ? smem : smem_s;
+}
+
+bool decode_step_fused_supported(const bsg_dims& d) {
+  return decode_mfma_path(d) && decode_select_supported(d, 1) && decode_step_smem(d, nullptr) <= 150 * 1024;
+}
 
 size_t decode_step_workspace_bytes(const bsg_dims& d) {
   if (!decode_step_fused_supported(d)) return 0;
@@ -561,17 +636,10 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
   float* part = (float*)((char*)workspace + a);
   hipError_t e = launch_decode_score_chunks(d, q, kv_lens, block_cache, page_table, lists, stream);
   if (e != hipSuccess) return e;
-  const int G = d.num_q_heads / d.num_kv_heads;
   const int nwg = decode_mfma_nwg(d);
   const int nchunks = decode_select_nchunks(d);
-  const int m = d.top_k - 1;
-  int T = 1;
-  while (m > 0 && nchunks * T < m && T < m) T <<= 1;
-  const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
-  const size_t smem_m = (size_t)4 * 16 * (d.head_dim + 2) * sizeof(float);
-  const size_t smem_s = (size_t)2 * nchunks * (m > 0 ? m : 1) * sizeof(uint64_t);
-  size_t smem = smem_v > smem_m ? smem_v : smem_m;
-  smem = smem > smem_s ? smem : smem_s;
+  int lt = 0;
+  const size_t smem = decode_step_smem(d, &lt);
   if (smem > 150 * 1024) return hipErrorInvalidValue;
   dim3 grid(nwg, d.num_kv_heads, d.batch);
 #define BSG_DF(DD, BB)                                                                                            \
@@ -581,7 +649,7 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
     if (ea != hipSuccess) return ea;                                                                               \
     hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache,      \
                        (const bf16_t*)v_cache, page_table, block_idx, lists, scale, part, d.num_q_heads,            \
-                       d.num_kv_heads, d.top_k, d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d), nchunks, T);     \
+                       d.num_kv_heads, d.top_k, d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d), nchunks, lt);    \
   } while (0)
   if (d.head_dim == 128) {
     if (d.page_size == 64) BSG_DF(128, 64); else BSG_DF(128, 128);
@@ -598,7 +666,6 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
   else
     hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
                        d.num_q_heads, d.num_kv_heads, nwg);
-  (void)G;
   return hipGetLastError();
 }
 

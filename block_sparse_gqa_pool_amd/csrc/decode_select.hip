@@ -9,8 +9,10 @@
 //     The representatives of all KV heads of a page are contiguous (Hkv*D values), so the
 //     workgroup streams whole page rows with 16-byte loads; each 16-byte piece is dotted
 //     with the matching slice of the fp32 group-summed query and reduced over the D/8 lanes
-//     that hold one (block, group).  Then one wave per group sorts the chunk's 64 keys
-//     (score, lower-index-first) with a register bitonic network and writes its best
+//     that hold one (block, group).  The query row and the chunk's page ids are fetched
+//     first, with one load each per thread, so that all row loads then go out together
+//     (no page-table round trip between them).  Then one wave per group ranks the chunk's
+//     64 keys (score, lower-index-first; rank = number of larger keys) and writes its best
 //     top_k - 1 keys, sorted descending.
 //  B. decode_select_kernel, one workgroup per (sequence, group): exact selection from the
 //     sorted chunk lists by pruning and ranking (see the kernel), then the kept ids are
@@ -29,12 +31,12 @@ template <int D>
 __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ block_cache,
     const int32_t* __restrict__ page_table, uint64_t* __restrict__ lists, int Hq, int Hkv, int bs, int m,
-    int num_pages, int pt_stride, int nchunks) {
+    int num_pages, int pt_stride, int nchunks, uint32_t ppb_magic) {
   extern __shared__ __attribute__((aligned(16))) float ds_smem[];
   float* qs = ds_smem;                   // [Hkv][D]
   float* sc = ds_smem + Hkv * D;         // [Hkv][DS_CH]
   constexpr int SEG = D / 8;             // lanes per (block, group)
-  constexpr int U = 16;                  // 16-byte loads in flight per thread
+  constexpr int U = 8;                   // 16-byte loads in flight per thread
   const int b = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
@@ -46,23 +48,38 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
   const int total = nloc * ppb;
   const int32_t* ptrow = page_table + (size_t)b * pt_stride + j0;
 
+  // the sequence's query row (Hq x D bf16), 16 bytes per piece, goes out first
+  constexpr int QU = 4;
+  const int nq16 = Hq * (D / 8);
+  const uint4* q16 = reinterpret_cast<const uint4*>(q + (size_t)b * Hq * D);
+  uint4 qr[QU];
+#pragma unroll
+  for (int i = 0; i < QU; i++) {
+    const int e = i * DS_NT + tid;
+    qr[i] = e < nq16 ? q16[e] : make_uint4(0, 0, 0, 0);
+  }
+  // the chunk's page ids, one per lane (DS_CH = 64 = wave size): a block row's page is then a
+  // lane shuffle, so all row loads below go out without waiting on the page table
+  static_assert(DS_CH == 64, "one page id per lane");
+  const int pid = lane < nloc ? clampi(ptrow[lane], 0, num_pages - 1) : 0;
   uint4 raw[U];
   auto issue = [&](int base) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int pi = base + u * DS_NT + tid;
+      const int blk = (int)__umulhi((uint32_t)pi, ppb_magic);   // pi / ppb (exact: pi * ppb < 2^32)
+      const int p = __shfl(pid, blk & 63, 64);                  // page of this piece's block
       raw[u] = make_uint4(0, 0, 0, 0);
-      if (pi < total) {
-        const int p = clampi(ptrow[pi / ppb], 0, num_pages - 1);
-        raw[u] = *reinterpret_cast<const uint4*>(block_cache + (size_t)p * Hkv * D + (size_t)(pi % ppb) * 8);
-      }
+      if (pi < total)
+        raw[u] = *reinterpret_cast<const uint4*>(block_cache + (size_t)p * Hkv * D + (size_t)(pi - blk * ppb) * 8);
     }
   };
   auto consume = [&](int base) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int pi = base + u * DS_NT + tid;
-      const int w = pi % ppb;
+      const int blk = (int)__umulhi((uint32_t)pi, ppb_magic);
+      const int w = pi - blk * ppb;
       const float* qv = qs + (size_t)w * 8;     // (g, d8) of this piece
       const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
       float s = 0.0f;
@@ -72,16 +89,26 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
         s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
       }
       s = seg_sum_dpp<SEG>(s);
-      if (pi < total && (lane % SEG) == 0) sc[(w / SEG) * DS_CH + pi / ppb] = s;
+      if (pi < total && (lane % SEG) == 0) sc[(w / SEG) * DS_CH + blk] = s;
     }
   };
 
+  // q is in (the page-id wait above covered it): park it in LDS so that its registers are
+  // free before the row loads go out
+  uint4* qraw = reinterpret_cast<uint4*>(sc + Hkv * DS_CH + 2 * DS_NT);   // [Hq][D] bf16
+#pragma unroll
+  for (int i = 0; i < QU; i++) {
+    const int e = i * DS_NT + tid;
+    if (e < nq16) qraw[e] = qr[i];
+  }
   if (total > 0) issue(0);                    // block-cache rows in flight while q is summed
-  for (int e = tid; e < Hkv * D; e += DS_NT) {
+  for (int e = QU * DS_NT + tid; e < nq16; e += DS_NT) qraw[e] = q16[e];   // rows beyond QU pieces
+  __syncthreads();
+  const bf16_t* qh = reinterpret_cast<const bf16_t*>(qraw);
+  for (int e = tid; e < Hkv * D; e += DS_NT) {   // group sums in fp32, heads in order
     const int g = e / D, d = e % D;
-    const bf16_t* qp = q + ((size_t)b * Hq + (size_t)g * G) * D + d;
     float s = 0.0f;
-    for (int h = 0; h < G; h++) s += bf16_to_f32(qp[(size_t)h * D]);
+    for (int h = 0; h < G; h++) s += bf16_to_f32(qh[(size_t)(g * G + h) * D + d]);
     qs[e] = s;
   }
   __syncthreads();
@@ -197,15 +224,17 @@ hipError_t launch_decode_score_chunks(const bsg_dims& d, const void* q, const in
   if (m <= 0) return hipSuccess;
   dim3 grid(nchunks, d.batch);
   const size_t smem = (size_t)(d.num_kv_heads * d.head_dim + d.num_kv_heads * DS_CH) * sizeof(float) +
-                      (size_t)(DS_NT / 64) * 64 * sizeof(uint64_t);
+                      (size_t)(DS_NT / 64) * 64 * sizeof(uint64_t) + (size_t)d.num_q_heads * d.head_dim * 2;
+  const uint32_t ppb = (uint32_t)d.num_kv_heads * (d.head_dim / 8);
+  const uint32_t magic = (uint32_t)((0x100000000ull + ppb - 1) / ppb);   // ceil(2^32 / ppb)
   if (d.head_dim == 128)
     hipLaunchKernelGGL(decode_score_chunk_kernel<128>, grid, dim3(DS_NT), smem, stream, (const bf16_t*)q, kv_lens,
                        (const bf16_t*)block_cache, page_table, lists, d.num_q_heads, d.num_kv_heads, d.page_size, m,
-                       d.num_pages, d.pt_stride, nchunks);
+                       d.num_pages, d.pt_stride, nchunks, magic);
   else
     hipLaunchKernelGGL(decode_score_chunk_kernel<64>, grid, dim3(DS_NT), smem, stream, (const bf16_t*)q, kv_lens,
                        (const bf16_t*)block_cache, page_table, lists, d.num_q_heads, d.num_kv_heads, d.page_size, m,
-                       d.num_pages, d.pt_stride, nchunks);
+                       d.num_pages, d.pt_stride, nchunks, magic);
   return hipGetLastError();
 }
 
