@@ -5,10 +5,10 @@ only marshals torch tensors into its calls.  Build it with
 ``python -m block_sparse_gqa_pool_amd.build``.
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, LIB_PATH, BsgDims, BsgError, block_pool, decode_step, decode_step_workspace_bytes,
+    EXPORTS, LIB_PATH, BsgDims, BsgError, block_pool, decode_step, decode_step_gated, decode_step_workspace_bytes,
     decode_workspace_bytes, dims, group_score,
     group_score_topk, group_score_topk_workspace_bytes, lib, sparse_attn_decode, sparse_attn_prefill,
-    topk_blocks,
+    sparse_attn_prefill_gated, topk_blocks,
 )
 
 __version__ = "1.0.0"

@@ -23,8 +23,8 @@ STATUS = {0: "BSG_OK", -1: "BSG_ERR_NULL", -2: "BSG_ERR_SHAPE", -3: "BSG_ERR_UNS
 # every symbol include/bsg.h declares
 EXPORTS = ("bsg_version", "bsg_status_str", "bsg_block_pool", "bsg_group_score", "bsg_topk_blocks",
            "bsg_group_score_topk_workspace_bytes", "bsg_group_score_topk", "bsg_sparse_attn_prefill",
-           "bsg_decode_workspace_bytes", "bsg_sparse_attn_decode", "bsg_decode_step_workspace_bytes",
-           "bsg_decode_step")
+           "bsg_sparse_attn_prefill_gated", "bsg_decode_workspace_bytes", "bsg_sparse_attn_decode",
+           "bsg_decode_step_workspace_bytes", "bsg_decode_step", "bsg_decode_step_gated")
 
 
 class BsgDims(ctypes.Structure):
@@ -60,10 +60,14 @@ def lib() -> ctypes.CDLL:
             "bsg_group_score_topk_workspace_bytes": ([dp, i32], sz),
             "bsg_group_score_topk": ([dp, vp, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "bsg_sparse_attn_prefill": ([dp, vp, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp], ctypes.c_int),
+            "bsg_sparse_attn_prefill_gated": ([dp, vp, i32, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, vp, vp],
+                                              ctypes.c_int),
             "bsg_decode_workspace_bytes": ([dp], sz),
             "bsg_sparse_attn_decode": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp, vp], ctypes.c_int),
             "bsg_decode_step_workspace_bytes": ([dp], sz),
             "bsg_decode_step": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, vp, vp], ctypes.c_int),
+            "bsg_decode_step_gated": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, i32, vp, vp, vp, vp],
+                                      ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -243,6 +247,49 @@ def sparse_attn_prefill(q, kv_lens, k_cache, v_cache, page_table, block_idx, sca
     return out
 
 
+def _gate(gate, x, out):
+    """Check a gated-fusion pair against out: x like out; gate fp32 with out's shape (one gate
+    per element) or out's shape without its last dimension (one gate per row)."""
+    _req(x, "x", out.dtype, out.dim(), out.device)
+    if x.shape != out.shape:
+        raise ValueError("x must have the shape of out")
+    _req(gate, "gate", torch.float32, None, out.device)
+    if gate.shape == out.shape:
+        return 1
+    if gate.shape == out.shape[:-1]:
+        return 0
+    raise ValueError("gate must have the shape of out, or of out without its last dimension")
+
+
+def sparse_attn_prefill_gated(q, kv_lens, k_cache, v_cache, page_table, block_idx, scale: float, gate, x, out,
+                              lse=None, stream=None):
+    """bsg_sparse_attn_prefill_gated: out = gate * attention + (1 - gate) * x."""
+    _req(k_cache, "k_cache", None, 4)
+    dev = k_cache.device
+    _req(v_cache, "v_cache", k_cache.dtype, 4, dev)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    _req(q, "q", k_cache.dtype, 4, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(block_idx, "block_idx", torch.int32, 4, dev)
+    _req(out, "out", k_cache.dtype, 4, dev)
+    B, Hq, ql, D = q.shape
+    if out.shape != q.shape or D != k_cache.shape[3] or page_table.shape[0] != B:
+        raise ValueError("shape mismatch between q, out, k_cache and page_table")
+    if tuple(block_idx.shape[:3]) != (B, k_cache.shape[1], ql):
+        raise ValueError("block_idx must be [B, Hkv, q_len, top_k]")
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 3, dev)
+        if tuple(lse.shape) != (B, Hq, ql):
+            raise ValueError("lse must be [B, Hq, q_len]")
+    per_dim = _gate(gate, x, out)
+    d = dims(k_cache, page_table, Hq, block_idx.shape[3])
+    _check("bsg_sparse_attn_prefill_gated", lib().bsg_sparse_attn_prefill_gated(
+        ctypes.byref(d), _ptr(q), ql, _ptr(kv_lens), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        _ptr(block_idx), float(scale), _ptr(gate), per_dim, _ptr(x), _ptr(out), _ptr(lse), _stream(stream)))
+    return out
+
+
 def decode_workspace_bytes(k_cache, page_table, num_q_heads: int, top_k: int) -> int:
     """Bytes of the decode workspace (no initialisation needed)."""
     d = dims(k_cache, page_table, num_q_heads, top_k)
@@ -319,4 +366,40 @@ def decode_step(q, kv_lens, block_cache, k_cache, v_cache, page_table, scale: fl
         ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(block_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         float(scale), _ptr(block_idx), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
         _ptr(lse), _stream(stream)))
+    return out
+
+
+def decode_step_gated(q, kv_lens, block_cache, k_cache, v_cache, page_table, scale: float, block_idx, gate, x, out,
+                      lse=None, workspace=None, stream=None):
+    """bsg_decode_step_gated: one decode step with out = gate * attention + (1 - gate) * x."""
+    _req(k_cache, "k_cache", None, 4)
+    dev = k_cache.device
+    _req(v_cache, "v_cache", k_cache.dtype, 4, dev)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    _req(block_cache, "block_cache", k_cache.dtype, 3, dev)
+    P, Hkv, bs, D = k_cache.shape
+    if tuple(block_cache.shape) != (P, Hkv, D):
+        raise ValueError("block_cache must be [num_pages, Hkv, D]")
+    _req(q, "q", k_cache.dtype, 3, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(block_idx, "block_idx", torch.int32, 3, dev)
+    _req(out, "out", k_cache.dtype, 3, dev)
+    B, Hq, D2 = q.shape
+    if out.shape != q.shape or D2 != D or page_table.shape[0] != B or tuple(block_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("shape mismatch between q, out, caches, page_table and block_idx")
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 2, dev)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
+    per_dim = _gate(gate, x, out)
+    d = dims(k_cache, page_table, Hq, block_idx.shape[2])
+    need = int(lib().bsg_decode_step_workspace_bytes(ctypes.byref(d)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _req(workspace, "workspace", None, None, dev)
+    _check("bsg_decode_step_gated", lib().bsg_decode_step_gated(
+        ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(block_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        float(scale), _ptr(block_idx), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(gate),
+        per_dim, _ptr(x), _ptr(out), _ptr(lse), _stream(stream)))
     return out

@@ -128,7 +128,8 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const float* __restrict__ ws, T* __restrict__ out,
-                                                              float* __restrict__ lse, int Hq, int Hkv, int nsplit) {
+                                                              float* __restrict__ lse, int Hq, int Hkv, int nsplit,
+                                                              gate_args ga) {
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
   const int G = Hq / Hkv;
@@ -166,7 +167,13 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const float* __res
     }
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  st_any(out + ((size_t)b * Hq + h) * D + d, o * inv);
+  const size_t row = (size_t)b * Hq + h;
+  float a = o * inv;
+  if (ga.g) {                                          // out = g A + (1 - g) x, one rounding
+    const float gv = ga.per_dim ? ga.g[row * D + d] : ga.g[row];
+    a = gv * a + (1.0f - gv) * ld_any(static_cast<const T*>(ga.x) + row * D + d);
+  }
+  st_any(out + row * D + d, a);
   if (lse && d == 0) lse[(size_t)b * Hq + h] = m + logf(l);
 }
 
@@ -520,7 +527,8 @@ static size_t decode_smem(const bsg_dims& d, size_t elem) {
 
 hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
                               const void* v_cache, const int32_t* page_table, const int32_t* block_idx,
-                              float scale, void* workspace, void* out, float* lse, hipStream_t stream) {
+                              float scale, void* workspace, void* out, float* lse, hipStream_t stream,
+                              gate_args ga) {
   if (decode_mfma_path(d)) {
     const int nwg = decode_mfma_nwg(d);
     float* part = (float*)workspace;
@@ -549,10 +557,10 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
     dim3 mgrid(d.batch * d.num_q_heads);
     if (d.head_dim == 128)
       hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 128>), mgrid, dim3(128), 0, stream, part, (bf16_t*)out, lse,
-                         d.num_q_heads, d.num_kv_heads, nwg);
+                         d.num_q_heads, d.num_kv_heads, nwg, ga);
     else
       hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
-                         d.num_q_heads, d.num_kv_heads, nwg);
+                         d.num_q_heads, d.num_kv_heads, nwg, ga);
     return hipGetLastError();
   }
   const int nsplit = decode_num_splits(d);
@@ -585,17 +593,17 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
   if (d.dtype == BSG_BF16) {
     if (d.head_dim == 128)
       hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 128>), mgrid, dim3(128), 0, stream, ws, (bf16_t*)out, lse,
-                         d.num_q_heads, d.num_kv_heads, nsplit);
+                         d.num_q_heads, d.num_kv_heads, nsplit, ga);
     else
       hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, ws, (bf16_t*)out, lse,
-                         d.num_q_heads, d.num_kv_heads, nsplit);
+                         d.num_q_heads, d.num_kv_heads, nsplit, ga);
   } else {
     if (d.head_dim == 128)
       hipLaunchKernelGGL((attn_decode_merge_kernel<float, 128>), mgrid, dim3(128), 0, stream, ws, (float*)out, lse,
-                         d.num_q_heads, d.num_kv_heads, nsplit);
+                         d.num_q_heads, d.num_kv_heads, nsplit, ga);
     else
       hipLaunchKernelGGL((attn_decode_merge_kernel<float, 64>), mgrid, dim3(64), 0, stream, ws, (float*)out, lse,
-                         d.num_q_heads, d.num_kv_heads, nsplit);
+                         d.num_q_heads, d.num_kv_heads, nsplit, ga);
   }
   return hipGetLastError();
 }
@@ -630,7 +638,8 @@ size_t decode_step_workspace_bytes(const bsg_dims& d) {
 
 hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
                               const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
-                              int32_t* block_idx, void* workspace, void* out, float* lse, hipStream_t stream) {
+                              int32_t* block_idx, void* workspace, void* out, float* lse, hipStream_t stream,
+                              gate_args ga) {
   const size_t a = (decode_select_workspace_bytes(d) + 255) / 256 * 256;
   uint64_t* lists = (uint64_t*)workspace;
   float* part = (float*)((char*)workspace + a);
@@ -662,10 +671,10 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
   dim3 mgrid(d.batch * d.num_q_heads);
   if (d.head_dim == 128)
     hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 128>), mgrid, dim3(128), 0, stream, part, (bf16_t*)out, lse,
-                       d.num_q_heads, d.num_kv_heads, nwg);
+                       d.num_q_heads, d.num_kv_heads, nwg, ga);
   else
     hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
-                       d.num_q_heads, d.num_kv_heads, nwg);
+                       d.num_q_heads, d.num_kv_heads, nwg, ga);
   return hipGetLastError();
 }
 

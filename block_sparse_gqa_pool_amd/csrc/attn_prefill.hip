@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ block_idx, float scale, bf16_t* __restrict__ out, float* __restrict__ lse,
-    int q_len, int Hq, int Hkv, int HG, int top_k, int num_pages, int pt_stride, int n_tt, int nst) {
+    int q_len, int Hq, int Hkv, int HG, int top_k, int num_pages, int pt_stride, int n_tt, int nst, gate_args ga) {
   constexpr int NT = 64 * PF_WAVES;
   constexpr int SUB = PF_SUB;
   constexpr int NSUB = BS / SUB;
@@ -390,16 +390,32 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   const float l = l_i + __shfl_xor(l_i, 32, 64);
   if (!row_ok) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  bf16_t* op = out + (((size_t)b * Hq + h) * q_len + t) * D;
+  const size_t row = ((size_t)b * Hq + h) * q_len + t;
+  bf16_t* op = out + row * D;
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
     for (int e4 = 0; e4 < 4; e4++) {
       const int d0 = 32 * dc + 8 * e4 + 4 * half;
-      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      float a[4];
+#pragma unroll
+      for (int x = 0; x < 4; x++) a[x] = o[dc][4 * e4 + x] * inv;
+      if (ga.g) {                                      // out = g A + (1 - g) x, one rounding
+        const bf16x4_t xv = *reinterpret_cast<const bf16x4_t*>(static_cast<const bf16_t*>(ga.x) + row * D + d0);
+        float g4[4];
+        if (ga.per_dim) {
+          const float4 gv = *reinterpret_cast<const float4*>(ga.g + row * D + d0);
+          g4[0] = gv.x; g4[1] = gv.y; g4[2] = gv.z; g4[3] = gv.w;
+        } else {
+          g4[0] = g4[1] = g4[2] = g4[3] = ga.g[row];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; x++) a[x] = g4[x] * a[x] + (1.0f - g4[x]) * (float)xv[x];
+      }
       bf16x4_t v4;
 #pragma unroll
-      for (int x = 0; x < 4; x++) v4[x] = (__bf16)(o[dc][4 * e4 + x] * inv);   // v_cvt_pk_bf16_f32 (nearest even)
+      for (int x = 0; x < 4; x++) v4[x] = (__bf16)a[x];   // v_cvt_pk_bf16_f32 (nearest even)
       *reinterpret_cast<bf16x4_t*>(op + d0) = v4;
     }
   if (lse && half == 0) lse[((size_t)b * Hq + h) * q_len + t] = m_i * scale + logf(l);
@@ -413,7 +429,7 @@ __global__ __launch_bounds__(256) void attn_prefill_valu_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ kv_lens, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, const int32_t* __restrict__ page_table, const int32_t* __restrict__ block_idx,
     float scale, T* __restrict__ out, float* __restrict__ lse, int q_len, int Hq, int Hkv, int bs, int top_k,
-    int num_pages, int pt_stride, long long rows) {
+    int num_pages, int pt_stride, long long rows, gate_args ga) {
   constexpr int DPL = D / 64;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -458,9 +474,18 @@ __global__ __launch_bounds__(256) void attn_prefill_valu_kernel(
     }
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  T* op = out + (((size_t)b * Hq + h) * q_len + t) * D;
+  const size_t orow = ((size_t)b * Hq + h) * q_len + t;
+  T* op = out + orow * D;
 #pragma unroll
-  for (int i = 0; i < DPL; i++) st_any(op + lane + 64 * i, acc[i] * inv);
+  for (int i = 0; i < DPL; i++) {
+    float a = acc[i] * inv;
+    if (ga.g) {                                        // out = g A + (1 - g) x, one rounding
+      const int d = lane + 64 * i;
+      const float gv = ga.per_dim ? ga.g[orow * D + d] : ga.g[orow];
+      a = gv * a + (1.0f - gv) * ld_any(static_cast<const T*>(ga.x) + orow * D + d);
+    }
+    st_any(op + lane + 64 * i, a);
+  }
   if (lse && lane == 0) lse[((size_t)b * Hq + h) * q_len + t] = m + logf(l);
 }
 
@@ -474,7 +499,7 @@ static int mfma_heads_per_tile(int G) {
 hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
                                const void* k_cache, const void* v_cache, const int32_t* page_table,
                                const int32_t* block_idx, float scale, void* out, float* lse,
-                               hipStream_t stream) {
+                               hipStream_t stream, gate_args ga) {
   const int G = d.num_q_heads / d.num_kv_heads;
   if (d.dtype == BSG_BF16) {
     const int HG = mfma_heads_per_tile(G);
@@ -498,7 +523,7 @@ hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, cons
     hipLaunchKernelGGL(kfn, grid, dim3(64 * PF_WAVES), smem, stream, (const bf16_t*)q, kv_lens,             \
                        (const bf16_t*)k_cache, (const bf16_t*)v_cache, page_table, block_idx, scale,          \
                        (bf16_t*)out, lse, q_len, d.num_q_heads, d.num_kv_heads, HG, d.top_k, d.num_pages,    \
-                       d.pt_stride, n_tt, nst);                                                               \
+                       d.pt_stride, n_tt, nst, ga);                                                           \
   } while (0)
         if (d.head_dim == 128) {
           if (d.page_size == 64) BSG_PF(128, 64); else BSG_PF(128, 128);
@@ -515,7 +540,7 @@ hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, cons
 #define BSG_PV(T, DD)                                                                                          \
   hipLaunchKernelGGL((attn_prefill_valu_kernel<T, DD>), grid, dim3(256), 0, stream, (const T*)q, kv_lens,       \
                      (const T*)k_cache, (const T*)v_cache, page_table, block_idx, scale, (T*)out, lse, q_len,   \
-                     d.num_q_heads, d.num_kv_heads, d.page_size, d.top_k, d.num_pages, d.pt_stride, rows)
+                     d.num_q_heads, d.num_kv_heads, d.page_size, d.top_k, d.num_pages, d.pt_stride, rows, ga)
   if (d.dtype == BSG_BF16) {
     if (d.head_dim == 128) BSG_PV(bf16_t, 128); else BSG_PV(bf16_t, 64);
   } else {

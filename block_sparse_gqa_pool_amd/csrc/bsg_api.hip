@@ -112,6 +112,19 @@ int bsg_sparse_attn_prefill(const bsg_dims* dims, const void* q, int32_t q_len, 
                                             scale, out, lse, (hipStream_t)stream));
 }
 
+int bsg_sparse_attn_prefill_gated(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                                  const void* k_cache, const void* v_cache, const int32_t* page_table,
+                                  const int32_t* block_idx, float scale, const float* gate, int32_t gate_per_dim,
+                                  const void* x, void* out, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !kv_lens || !k_cache || !v_cache || !page_table || !block_idx || !out || !gate || !x)
+    return BSG_ERR_NULL;
+  if (q_len < 1 || (gate_per_dim != 0 && gate_per_dim != 1)) return BSG_ERR_SHAPE;
+  return to_status(bsg::launch_attn_prefill(*dims, q, q_len, kv_lens, k_cache, v_cache, page_table, block_idx,
+                                            scale, out, lse, (hipStream_t)stream, {gate, gate_per_dim, x}));
+}
+
 size_t bsg_decode_workspace_bytes(const bsg_dims* dims) {
   if (check_dims(dims)) return 0;
   return bsg::decode_workspace_bytes(*dims);
@@ -145,9 +158,10 @@ size_t bsg_decode_step_workspace_bytes(const bsg_dims* dims) {
   return decode_step_ws_split(dims, &a);
 }
 
-int bsg_decode_step(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* block_cache,
-                    const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
-                    int32_t* block_idx, void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+static int decode_step_impl(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* block_cache,
+                            const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
+                            int32_t* block_idx, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                            void* stream, bsg::gate_args ga) {
   int st = check_dims(dims);
   if (st) return st;
   if (!q || !kv_lens || !block_cache || !k_cache || !v_cache || !page_table || !block_idx || !out)
@@ -159,13 +173,36 @@ int bsg_decode_step(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
   hipStream_t s = (hipStream_t)stream;
   if (bsg::decode_step_fused_supported(*dims))
     return to_status(bsg::launch_decode_step(*dims, q, kv_lens, block_cache, k_cache, v_cache, page_table, scale,
-                                             block_idx, workspace, out, lse, s));
+                                             block_idx, workspace, out, lse, s, ga));
   size_t a;
   decode_step_ws_split(dims, &a);
   st = bsg_group_score_topk(dims, q, 1, kv_lens, block_cache, page_table, block_idx, workspace, a, stream);
   if (st) return st;
-  return bsg_sparse_attn_decode(dims, q, kv_lens, k_cache, v_cache, page_table, block_idx, scale,
-                                (char*)workspace + a, workspace_bytes - a, out, lse, stream);
+  if (!ga.g)
+    return bsg_sparse_attn_decode(dims, q, kv_lens, k_cache, v_cache, page_table, block_idx, scale,
+                                  (char*)workspace + a, workspace_bytes - a, out, lse, stream);
+  if (workspace_bytes - a < bsg::decode_workspace_bytes(*dims)) return BSG_ERR_WORKSPACE;
+  return to_status(bsg::launch_attn_decode(*dims, q, kv_lens, k_cache, v_cache, page_table, block_idx, scale,
+                                           (char*)workspace + a, out, lse, s, ga));
+}
+
+int bsg_decode_step(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* block_cache,
+                    const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
+                    int32_t* block_idx, void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+  return decode_step_impl(dims, q, kv_lens, block_cache, k_cache, v_cache, page_table, scale, block_idx, workspace,
+                          workspace_bytes, out, lse, stream, {nullptr, 0, nullptr});
+}
+
+int bsg_decode_step_gated(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* block_cache,
+                          const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
+                          int32_t* block_idx, void* workspace, size_t workspace_bytes, const float* gate,
+                          int32_t gate_per_dim, const void* x, void* out, float* lse, void* stream) {
+  const int st = check_dims(dims);
+  if (st) return st;
+  if (!gate || !x) return BSG_ERR_NULL;
+  if (gate_per_dim != 0 && gate_per_dim != 1) return BSG_ERR_SHAPE;
+  return decode_step_impl(dims, q, kv_lens, block_cache, k_cache, v_cache, page_table, scale, block_idx, workspace,
+                          workspace_bytes, out, lse, stream, {gate, gate_per_dim, x});
 }
 
 }  // extern "C"

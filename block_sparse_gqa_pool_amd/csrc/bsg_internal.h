@@ -8,6 +8,17 @@
 #include "bsg.h"
 
 namespace bsg {
+// Gated fusion of an attention output with a caller tensor ("Sparse Attention for
+// Long-Context LLMs", section 5.5, step 6: out = Gate * A + (1 - Gate) * X, the gate being
+// a scalar or a per-dimension vector).  g == nullptr: no fusion.  g is fp32, one value per
+// (sequence, head, query) row (per_dim = 0) or per element (per_dim = 1); x has the output's
+// dtype and layout.
+struct gate_args {
+  const float* g;
+  int per_dim;
+  const void* x;
+};
+
 
 hipError_t launch_block_pool(const bsg_dims& d, const void* k_cache, const int32_t* page_table,
                              const int32_t* kv_lens, const int32_t* blk_begin, void* block_cache,
@@ -43,18 +54,19 @@ bool decode_step_fused_supported(const bsg_dims& d);
 size_t decode_step_workspace_bytes(const bsg_dims& d);
 hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
                               const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
-                              int32_t* block_idx, void* workspace, void* out, float* lse, hipStream_t stream);
+                              int32_t* block_idx, void* workspace, void* out, float* lse, hipStream_t stream,
+                              gate_args ga = {nullptr, 0, nullptr});
 
 hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
                                const void* k_cache, const void* v_cache, const int32_t* page_table,
                                const int32_t* block_idx, float scale, void* out, float* lse,
-                               hipStream_t stream);
+                               hipStream_t stream, gate_args ga = {nullptr, 0, nullptr});
 
 int decode_num_splits(const bsg_dims& d);
 size_t decode_workspace_bytes(const bsg_dims& d);
 hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* kv_lens,
                               const void* k_cache, const void* v_cache, const int32_t* page_table,
                               const int32_t* block_idx, float scale, void* workspace, void* out,
-                              float* lse, hipStream_t stream);
+                              float* lse, hipStream_t stream, gate_args ga = {nullptr, 0, nullptr});
 
 }  // namespace bsg

@@ -175,6 +175,26 @@ int bsg_sparse_attn_prefill(const bsg_dims* dims, const void* q, int32_t q_len,
                             void* out, float* lse, void* stream);
 
 /*
+ * bsg_sparse_attn_prefill_gated -- bsg_sparse_attn_prefill followed by the gated fusion
+ * of its output A with a caller tensor x ("Sparse Attention for Long-Context LLMs",
+ * section 5.5, step 6: the output is Gate * A + (1 - Gate) * the original representation,
+ * the gate being a scalar or a per-dimension vector; the Linear Backbones page, section
+ * 5.5, ends its pseudocode the same way):
+ *     out = g * A + (1 - g) * x
+ * computed in fp32 from the fp32 attention output and rounded once to the dtype.
+ * gate : fp32, [B, Hq, q_len] (gate_per_dim = 0: one gate per head and query) or
+ *        [B, Hq, q_len, D] (gate_per_dim = 1: one gate per element); any values.
+ * x    : [B, Hq, q_len, D] in the dtype (the layout of out; may not alias out).
+ * lse is that of A.  gate and x must not be NULL (BSG_ERR_NULL); gate_per_dim other than
+ * 0 or 1 is BSG_ERR_SHAPE.  Everything else as bsg_sparse_attn_prefill.
+ */
+int bsg_sparse_attn_prefill_gated(const bsg_dims* dims, const void* q, int32_t q_len,
+                                  const int32_t* kv_lens, const void* k_cache, const void* v_cache,
+                                  const int32_t* page_table, const int32_t* block_idx, float scale,
+                                  const float* gate, int32_t gate_per_dim, const void* x, void* out,
+                                  float* lse, void* stream);
+
+/*
  * bsg_sparse_attn_decode -- one query token per sequence (q_len = 1), split
  * over the selected blocks with a log-sum-exp merge.  Same definition as
  * bsg_sparse_attn_prefill with q_len = 1; block_idx is [B, Hkv, top_k].
@@ -213,6 +233,17 @@ int bsg_decode_step(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
                     const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
                     int32_t* block_idx, void* workspace, size_t workspace_bytes, void* out, float* lse,
                     void* stream);
+
+/*
+ * bsg_decode_step_gated -- bsg_decode_step with the same gated fusion as
+ * bsg_sparse_attn_prefill_gated applied to its output (gate: fp32 [B, Hq] or [B, Hq, D];
+ * x: [B, Hq, D] in the dtype).  Workspace as bsg_decode_step.
+ */
+int bsg_decode_step_gated(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
+                          const void* block_cache, const void* k_cache, const void* v_cache,
+                          const int32_t* page_table, float scale, int32_t* block_idx, void* workspace,
+                          size_t workspace_bytes, const float* gate, int32_t gate_per_dim, const void* x,
+                          void* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

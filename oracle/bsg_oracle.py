@@ -32,6 +32,11 @@ What is computed, with the passage each step follows:
    top-k mask restricts the softmax, read here as an additive minus-infinity
    mask, i.e. the unselected keys do not take part).  Inside the own block a
    key takes part only if its position is at most the query's position.
+5. Gated fusion (optional; "Sparse Attention for Long-Context LLMs", section
+   5.5, step 6: the final output is the gate times the attention output plus
+   one minus the gate times the original representation, the gate being a
+   scalar or a vector per dimension).  Here the gate and the other tensor are
+   caller inputs: out = g * A + (1 - g) * x, in float64.
 
 Precision: attention and scores are computed in float64.  Two results are
 codes decided by floating point, and those decisions are taken in the
@@ -50,7 +55,7 @@ import numpy as np
 __all__ = [
     "bf16_bits", "bf16_value", "round_to_cache", "gather_tokens", "block_pool",
     "query_positions", "group_scores", "select_blocks",
-    "sparse_attention", "prefill_reference", "decode_reference",
+    "sparse_attention", "prefill_reference", "decode_reference", "gated_fusion",
 ]
 
 
@@ -282,3 +287,21 @@ def decode_reference(q, k_pages, v_pages, page_table, kv_lens, page_size, top_k,
     idx = select_blocks(sc, kv_lens, q_len, page_size, top_k)
     out, lse = sparse_attention(q, k_pages, v_pages, page_table, kv_lens, idx, scale)
     return dict(block_cache=block_cache, scores=sc, block_idx=idx, out=out, lse=lse)
+
+
+# ----------------------------------------------------------------------------
+# 5. gated fusion
+
+def gated_fusion(a: np.ndarray, gate: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """Gate * A + (1 - Gate) * X ("Sparse Attention for Long-Context LLMs", section 5.5,
+    step 6), in float64.  ``a`` and ``x`` have the output's shape [..., D]; ``gate`` has
+    that shape (one gate per dimension) or that shape without the last axis (one gate per
+    row, broadcast over D)."""
+    a = np.asarray(a, np.float64)
+    x = np.asarray(x, np.float64)
+    g = np.asarray(gate, np.float64)
+    if g.shape == a.shape[:-1]:
+        g = g[..., None]
+    elif g.shape != a.shape:
+        raise ValueError("gate must have the output's shape or the output's shape without D")
+    return g * a + (1.0 - g) * x

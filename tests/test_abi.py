@@ -74,6 +74,10 @@ def test_validation_of_dims(L, dims, expect):
     assert L.bsg_sparse_attn_prefill(dp, BAD, 4, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, None, s) == expect
     assert L.bsg_sparse_attn_decode(dp, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, 1 << 30, BAD, None, s) == expect
     assert L.bsg_decode_step(dp, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, BAD, 1 << 30, BAD, None, s) == expect
+    assert L.bsg_sparse_attn_prefill_gated(dp, BAD, 4, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, 0, BAD, BAD, None,
+                                           s) == expect
+    assert L.bsg_decode_step_gated(dp, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, BAD, 1 << 30, BAD, 0, BAD, BAD, None,
+                                   s) == expect
     if dims is not None and expect != 0:
         assert L.bsg_decode_step_workspace_bytes(dp) == 0
         assert L.bsg_decode_workspace_bytes(dp) == 0
@@ -111,3 +115,21 @@ def test_decode_workspace_size_formula(L):
         n = L.bsg_decode_workspace_bytes(ctypes.byref(d))
         per_split = B * Hkv * (Hq // Hkv) * (D + 2) * 4
         assert n % per_split == 0 and 1 <= n // per_split <= k
+
+
+def test_validation_of_gated_calls(L):
+    d = ctypes.byref(_dims())
+    s = None
+    pf = lambda gate, per_dim, x: L.bsg_sparse_attn_prefill_gated(d, BAD, 4, BAD, BAD, BAD, BAD, BAD, 0.1, gate,
+                                                                  per_dim, x, BAD, None, s)
+    assert pf(None, 0, BAD) == -1
+    assert pf(BAD, 0, None) == -1
+    assert pf(BAD, 2, BAD) == -2
+    assert pf(BAD, -1, BAD) == -2
+    need = L.bsg_decode_step_workspace_bytes(d)
+    ds = lambda gate, per_dim, x, ws=need: L.bsg_decode_step_gated(d, BAD, BAD, BAD, BAD, BAD, BAD, 0.1, BAD, BAD, ws,
+                                                                   gate, per_dim, x, BAD, None, s)
+    assert ds(None, 0, BAD) == -1
+    assert ds(BAD, 0, None) == -1
+    assert ds(BAD, 3, BAD) == -2
+    assert ds(BAD, 1, BAD, need - 1) == -4

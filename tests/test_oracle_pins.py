@@ -429,6 +429,29 @@ def test_chunked_prefill_rows_equal_full_prefill_rows():
 
 
 # --------------------------------------------------------------------------
+# gated fusion (Long-Context page, section 5.5, step 6)
+# --------------------------------------------------------------------------
+def test_gated_fusion_hand_values():
+    a = np.array([[1.0, 2.0], [3.0, 4.0]])
+    x = np.array([[5.0, 6.0], [7.0, 8.0]])
+    # one gate per row: row 0 a quarter attention, row 1 all attention
+    np.testing.assert_array_equal(O.gated_fusion(a, np.array([0.25, 1.0]), x), [[4.0, 5.0], [3.0, 4.0]])
+    # one gate per element
+    np.testing.assert_array_equal(O.gated_fusion(a, np.array([[0.0, 1.0], [0.5, 0.5]]), x), [[5.0, 2.0], [5.0, 6.0]])
+
+
+def test_gated_fusion_limits_and_broadcast():
+    rng = np.random.default_rng(3)
+    a, x = rng.standard_normal((2, 3, 4, 8)), rng.standard_normal((2, 3, 4, 8))
+    np.testing.assert_array_equal(O.gated_fusion(a, np.ones((2, 3, 4)), x), a)
+    np.testing.assert_array_equal(O.gated_fusion(a, np.zeros((2, 3, 4, 8)), x), x)
+    g = rng.uniform(-0.5, 1.5, (2, 3, 4))
+    np.testing.assert_array_equal(O.gated_fusion(a, g, x), O.gated_fusion(a, np.repeat(g[..., None], 8, -1), x))
+    with pytest.raises(ValueError):
+        O.gated_fusion(a, np.ones((2, 3)), x)
+
+
+# --------------------------------------------------------------------------
 # generator
 # --------------------------------------------------------------------------
 def test_generator_is_deterministic_and_seed_sensitive():
