@@ -37,6 +37,18 @@ What is computed, with the passage each step follows:
    one minus the gate times the original representation, the gate being a
    scalar or a vector per dimension).  Here the gate and the other tensor are
    caller inputs: out = g * A + (1 - g) * x, in float64.
+6. fp8 KV cache and block cache (optional; "Sparse Attention + Linear
+   Backbones", section 3, and "Sparse Attention for Long-Context LLMs",
+   section 8, list KV-cache quantization as a system-level optimisation to
+   combine with sparse attention; neither fixes a format).  Reading taken
+   here: OCP E4M3 codes with one power-of-two scale per (page, KV head) tile,
+   the smallest power of two 2^e with max|x| <= 448 * 2^e over the tile's
+   valid tokens; codes are x / 2^e rounded to nearest, ties to even; slots
+   past the sequence length hold code 0.  The fp8 block cache is built from
+   the fp8 keys: the float32 sum of the decoded codes in token order, times
+   scale / page_size, quantised the same way per (page, head).  Attention and
+   scores then run on the decoded values (code value times scale), exactly as
+   steps 2-4 on a float cache.
 
 Precision: attention and scores are computed in float64.  Two results are
 codes decided by floating point, and those decisions are taken in the
@@ -56,6 +68,7 @@ __all__ = [
     "bf16_bits", "bf16_value", "round_to_cache", "gather_tokens", "block_pool",
     "query_positions", "group_scores", "select_blocks",
     "sparse_attention", "prefill_reference", "decode_reference", "gated_fusion",
+    "e4m3_value", "e4m3_code", "fp8_scale_exp", "quantize_pages_fp8", "fp8_dequant", "block_pool_fp8",
 ]
 
 
@@ -305,3 +318,104 @@ def gated_fusion(a: np.ndarray, gate: np.ndarray, x: np.ndarray) -> np.ndarray:
     elif g.shape != a.shape:
         raise ValueError("gate must have the output's shape or the output's shape without D")
     return g * a + (1.0 - g) * x
+
+
+# ----------------------------------------------------------------------------
+# 6. fp8 (OCP E4M3) KV cache and block cache
+# ----------------------------------------------------------------------------
+def e4m3_value(codes) -> np.ndarray:
+    """float64 value of OCP E4M3 codes: sign, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no infinities."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    s, e, m = c >> 7, (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+_E4M3_MAG = e4m3_value(np.arange(127, dtype=np.uint8))     # codes 0x00..0x7E: 0 .. 448, ascending
+
+
+def e4m3_code(x) -> np.ndarray:
+    """Nearest E4M3 code of finite |x| <= 448, ties to the even code (the code's last bit is
+    the mantissa's last bit).  The sign bit follows the sign of x, -0.0 included."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    if not np.all(np.isfinite(a)) or np.any(a > 448.0):
+        raise ValueError("e4m3_code takes finite values of magnitude <= 448")
+    hi = np.minimum(np.searchsorted(_E4M3_MAG, a, side="left"), 126)   # first magnitude >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - _E4M3_MAG[lo], _E4M3_MAG[hi] - a
+    pick = np.where(d_hi == 0, hi, np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi))))
+    return (pick | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def fp8_scale_exp(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e (0 for amax = 0), clamped to [-126, 127].
+    With amax = f * 2^E, 0.5 <= f < 1, and 448 = 0.875 * 2^9: e = E - 9 if f <= 0.875,
+    else E - 8."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    f, E = math.frexp(amax)
+    e = E - 9 if f <= 0.875 else E - 8
+    return max(-126, min(127, e))
+
+
+def quantize_pages_fp8(pages: np.ndarray, page_table: np.ndarray, kv_lens: Sequence[int],
+                       page_size: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(codes uint8 [P, Hkv, bs, D], scales float32 [P, Hkv]) of a paged cache [P, Hkv, bs, D].
+
+    Every (page, head) tile of every sequence's blocks j < ceil(kv_len / bs) is quantised
+    over its valid tokens n = min(bs, kv_len - j bs): scale 2^e with e = fp8_scale_exp of
+    the tile's max |x|, codes e4m3_code(x / 2^e), code 0 past n.  Tiles no sequence
+    reaches keep code 0 and scale 1."""
+    P, Hkv, bs, D = pages.shape
+    codes = np.zeros((P, Hkv, bs, D), np.uint8)
+    scales = np.ones((P, Hkv), np.float32)
+    for b, L in enumerate(kv_lens):
+        nblk = min((int(L) + bs - 1) // bs, page_table.shape[1])
+        for j in range(nblk):
+            p = int(page_table[b, j])
+            n = min(bs, int(L) - j * bs)
+            for g in range(Hkv):
+                tile = np.asarray(pages[p, g, :n], np.float64)
+                e = fp8_scale_exp(np.abs(tile).max())
+                codes[p, g, :n] = e4m3_code(tile / 2.0 ** e)
+                codes[p, g, n:] = 0
+                scales[p, g] = 2.0 ** e
+    return codes, scales
+
+
+def fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Decoded values: e4m3_value(code) * scale of the code's (page, head), float64.
+    ``codes`` [P, Hkv, ..., D] and ``scales`` [P, Hkv]."""
+    v = e4m3_value(codes)
+    return v * np.asarray(scales, np.float64).reshape(scales.shape + (1,) * (v.ndim - 2))
+
+
+def block_pool_fp8(k_codes: np.ndarray, k_scales: np.ndarray, page_table: np.ndarray,
+                   kv_lens: Sequence[int], blk_begin: Optional[Sequence[int]] = None,
+                   rep_codes: Optional[np.ndarray] = None, rep_scales: Optional[np.ndarray] = None
+                   ) -> Tuple[np.ndarray, np.ndarray]:
+    """fp8 block cache (codes uint8 [P, Hkv, D], scales float32 [P, Hkv]) of the complete
+    blocks j in [blk_begin[b], kv_len // bs): the float32 sum of the block's decoded key
+    codes in token order, times (scale / bs) in float32, quantised per (page, head) like the
+    KV cache.  Other pages keep the given (or zero / unit) entries."""
+    P, Hkv, bs, D = k_codes.shape
+    rc = np.zeros((P, Hkv, D), np.uint8) if rep_codes is None else np.array(rep_codes, np.uint8)
+    rs = np.ones((P, Hkv), np.float32) if rep_scales is None else np.array(rep_scales, np.float32)
+    for b, L in enumerate(kv_lens):
+        begin = 0 if blk_begin is None else int(blk_begin[b])
+        end = min(int(L) // bs, page_table.shape[1])
+        for j in range(begin, end):
+            p = int(page_table[b, j])
+            acc = np.zeros((Hkv, D), np.float32)
+            for i in range(bs):                                       # token order
+                acc = acc + e4m3_value(k_codes[p, :, i, :]).astype(np.float32)
+            mean = acc * (np.asarray(k_scales[p], np.float32) * np.float32(1.0 / bs))[:, None]
+            for g in range(Hkv):
+                e = fp8_scale_exp(np.abs(mean[g].astype(np.float64)).max())
+                rc[p, g] = e4m3_code(mean[g].astype(np.float64) / 2.0 ** e)
+                rs[p, g] = 2.0 ** e
+    return rc, rs

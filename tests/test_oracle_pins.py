@@ -474,3 +474,123 @@ def test_generator_ragged_decode_lengths():
     for L in w.kv_lens_host:
         assert 1001 <= L <= 3001
     assert len(set(w.kv_lens_host)) > 1
+
+
+# ----------------------------------------------------------------------------
+# fp8 (OCP E4M3) KV cache: codes pinned to torch's float8_e4m3fn and to the format's
+# published constants; scales and block representatives to brute force and closed forms
+# ----------------------------------------------------------------------------
+def _torch_e4m3_value(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_value_matches_format_and_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    v = O.e4m3_value(codes)
+    t = _torch_e4m3_value(codes)
+    assert np.array_equal(np.isnan(v), np.isnan(t)) and np.array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+    # constants of the OCP E4M3 format: largest finite, smallest normal and subnormal, one
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0
+    assert v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9 and v[0x38] == 1.0 and v[0xC0] == -2.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.sum(np.isnan(v)) == 2
+
+
+def test_e4m3_code_ties_round_trip_and_torch():
+    # ties go to the even code (mantissa last bit 0)
+    cases = [(1.0625, 0x38), (1.1875, 0x3A), (1.5 * 2.0 ** -9, 0x02), (7.5 * 2.0 ** -9, 0x08),
+             (0.5 * 2.0 ** -9, 0x00), (2.5 * 2.0 ** -9, 0x02), (440.0, 0x7E), (-0.0, 0x80), (0.0, 0x00)]
+    for x, c in cases:
+        assert int(O.e4m3_code(x)) == c, (x, hex(int(O.e4m3_code(x))))
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    assert np.array_equal(O.e4m3_code(O.e4m3_value(finite)), finite)
+    rng = np.random.default_rng(5)
+    x = np.clip(rng.standard_normal(20000) * np.exp2(rng.integers(-12, 8, 20000)), -448, 448)
+    ct = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_code(x), ct)
+    # brute force: the nearest finite value, ties to the even code
+    vals = O.e4m3_value(finite)
+    for xv in x[:400]:
+        d = np.abs(vals - xv)
+        best = finite[d == d.min()]
+        best = best[(best & 1) == 0] if len(best) > 1 else best
+        if len(best) > 1:                                   # +0 / -0: the sign follows x
+            best = best[(best >> 7) == int(np.signbit(xv))]
+        assert int(O.e4m3_code(xv)) == int(best[0])
+
+
+def test_fp8_scale_exp_brute_force():
+    rng = np.random.default_rng(6)
+    vals = list(rng.random(300) * np.exp2(rng.integers(-60, 60, 300)))
+    vals += [448.0 * 2.0 ** k for k in range(-20, 20)] + [np.nextafter(448.0 * 2.0 ** k, np.inf) for k in range(-5, 5)]
+    vals += [0.875 * 2.0 ** k for k in range(-5, 5)] + [1.0, 3.0, 7.0]
+    for a in vals:
+        e_bf = next(e for e in range(-200, 200) if a <= 448.0 * 2.0 ** e)
+        assert O.fp8_scale_exp(a) == max(-126, min(127, e_bf)), a
+    assert O.fp8_scale_exp(0.0) == 0
+
+
+def _small_fp8_case(seed=8, P=12, Hkv=2, bs=64, D=64):
+    rng = np.random.default_rng(seed)
+    pages = (rng.standard_normal((P, Hkv, bs, D)) * np.exp2(rng.integers(-3, 4, (P, Hkv, 1, 1)))).astype(np.float32)
+    pt = np.array([[3, 7, 1, 10], [0, 5, 11, 2]], np.int32)
+    kv = [64 * 3 + 17, 64 * 2]
+    return pages, pt, kv
+
+
+def test_quantize_pages_fp8_bounds_and_layout():
+    pages, pt, kv = _small_fp8_case()
+    bs = pages.shape[2]
+    codes, scales = O.quantize_pages_fp8(pages, pt, kv, bs)
+    used = set()
+    for b, L in enumerate(kv):
+        for j in range((L + bs - 1) // bs):
+            p, n = int(pt[b, j]), min(bs, L - j * bs)
+            used.add(p)
+            for g in range(pages.shape[1]):
+                s = float(scales[p, g])
+                assert s == 2.0 ** round(math.log2(s))                   # a power of two
+                x = pages[p, g, :n].astype(np.float64)
+                y = O.e4m3_value(codes[p, g, :n]) * s
+                assert np.abs(x).max() <= 448 * s and np.abs(x).max() > 224 * s   # the smallest such scale
+                err = np.abs(y - x)
+                assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s))   # half an ulp
+                assert np.all(codes[p, g, n:] == 0)
+    for p in range(pages.shape[0]):
+        if p not in used:
+            assert np.all(codes[p] == 0) and np.all(scales[p] == 1.0)
+    # a tile whose maximum is 448 * 2^k is scaled by 2^k and its maximum gets code 0x7E
+    pages2 = pages.copy()
+    pages2[3, 0, 5, 7] = 448.0 * 2.0 ** -3
+    pages2[3, 0] = np.clip(pages2[3, 0], -448.0 * 2.0 ** -3, 448.0 * 2.0 ** -3)
+    c2, s2 = O.quantize_pages_fp8(pages2, pt, kv, bs)
+    assert s2[3, 0] == 2.0 ** -3 and c2[3, 0, 5, 7] == 0x7E
+
+
+def test_block_pool_fp8_closed_forms():
+    pages, pt, kv = _small_fp8_case(seed=9)
+    P, Hkv, bs, D = pages.shape
+    codes, scales = O.quantize_pages_fp8(pages, pt, kv, bs)
+    # constant keys: the representative decodes to the key itself
+    const = codes.copy()
+    const[:] = codes[:, :, :1, :]
+    rc, rs = O.block_pool_fp8(const, scales, pt, kv)
+    for b, L in enumerate(kv):
+        for j in range(L // bs):
+            p = int(pt[b, j])
+            assert np.array_equal(O.fp8_dequant(rc[p][None], rs[p][None])[0], O.fp8_dequant(const[p][None, :, 0], scales[p][None])[0])
+    # negated keys: sign bits flip, scales stay
+    neg = codes ^ np.uint8(0x80)
+    rc1, rs1 = O.block_pool_fp8(codes, scales, pt, kv)
+    rc2, rs2 = O.block_pool_fp8(neg, scales, pt, kv)
+    full = [int(pt[b, j]) for b, L in enumerate(kv) for j in range(L // bs)]
+    nz = O.e4m3_value(rc1[full]) != 0
+    assert np.array_equal((rc1[full] ^ np.uint8(0x80))[nz], rc2[full][nz]) and np.array_equal(rs1[full], rs2[full])
+    # against the exact mean of the decoded keys: within half an ulp of E4M3 (+ float32 sums)
+    for p in full:
+        mean = O.fp8_dequant(codes[p][None], scales[p][None])[0].mean(axis=1)        # [Hkv, D]
+        rep = O.fp8_dequant(rc1[p][None], rs1[p][None])[0]
+        s = rs1[p].astype(np.float64)[:, None]
+        assert np.all(np.abs(rep - mean) <= np.abs(mean) * (2.0 ** -4 + 1e-6) + 2.0 ** -10 * s + 1e-12)
+    # untouched pages keep their entries; blk_begin skips earlier blocks
+    rc3, rs3 = O.block_pool_fp8(codes, scales, pt, kv, blk_begin=[2, 1])
+    assert np.all(rc3[int(pt[0, 0])] == 0) and np.array_equal(rc3[int(pt[0, 2])], rc1[int(pt[0, 2])])
