@@ -69,7 +69,8 @@ def prefill_flops(block_idx, kv_lens, q_len, page_size, G, D):
 
 
 def decode_bytes(block_idx, kv_lens, page_size, Hkv, D, elem=2):
-    """Selected K+V bytes + block-cache bytes of every candidate + page-table bytes."""
+    """Selected K+V bytes + block-cache bytes of every candidate + page-table bytes (elem = 1:
+    fp8 caches, plus one 4-byte scale per selected K and V page and per candidate)."""
     import torch
     B = block_idx.shape[0]
     pos = kv_lens.view(B, 1, 1).long() - 1
@@ -80,7 +81,10 @@ def decode_bytes(block_idx, kv_lens, page_size, Hkv, D, elem=2):
     own = (kv_lens.long() - 1) // page_size
     reps = float(own.sum().item()) * Hkv * D * elem
     pt = float((own + 1).sum().item()) * 4
-    return kv + reps + pt, dict(selected_kv=kv, block_cache=reps, page_table=pt)
+    if elem != 1:
+        return kv + reps + pt, dict(selected_kv=kv, block_cache=reps, page_table=pt)
+    sc = float((j >= 0).sum().item()) * 8 + float(own.sum().item()) * Hkv * 4
+    return kv + reps + pt + sc, dict(selected_kv=kv, block_cache=reps, page_table=pt, scales=sc)
 
 
 # ------------------------------------------------------------------------------------
@@ -137,7 +141,7 @@ def run_prefill(spec, seed, steps, warmup):
     return res
 
 
-def run_decode(spec, seed, steps, warmup, graph_replay=True):
+def run_decode(spec, seed, steps, warmup, graph_replay=True, fp8=False):
     import torch
     import block_sparse_gqa_pool_amd as bsg
     from workloads import make_workload
@@ -157,6 +161,25 @@ def run_decode(spec, seed, steps, warmup, graph_replay=True):
 
     def step():
         bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx, out, workspace=ws)
+
+    if fp8:
+        # fp8 caches, quantised from the bf16 ones at prefill (untimed); the bf16 caches are freed
+        P = w.k_cache.shape[0]
+        kc = torch.zeros(P, Hkv, bs, D, dtype=torch.uint8, device=dev)
+        vc = torch.zeros_like(kc)
+        ks = torch.ones(P, Hkv, dtype=torch.float32, device=dev)
+        vs = torch.ones_like(ks)
+        bsg.quantize_pages_fp8(w.k_cache, w.page_table, w.kv_lens, kc, ks)
+        bsg.quantize_pages_fp8(w.v_cache, w.page_table, w.kv_lens, vc, vs)
+        rc = torch.zeros(P, Hkv, D, dtype=torch.uint8, device=dev)
+        rs = torch.ones(P, Hkv, dtype=torch.float32, device=dev)
+        bsg.block_pool_fp8(kc, ks, w.page_table, w.kv_lens, rc, rs)
+        w.k_cache = w.v_cache = None
+        cache = None
+        torch.cuda.empty_cache()
+
+        def step():
+            bsg.decode_step_fp8(q1, w.kv_lens, rc, rs, kc, ks, vc, vs, w.page_table, scale, idx, out, workspace=ws)
 
     # the step is three short kernels, faster than Python can launch them: capture
     # PER_GRAPH whole steps in one HIP graph and replay it, so the timed region measures
@@ -190,7 +213,7 @@ def run_decode(spec, seed, steps, warmup, graph_replay=True):
     wall = time.perf_counter() - t0
     steps = n_rep * PER_GRAPH
     step_ms = e0.elapsed_time(e1) / steps
-    nbytes, parts = decode_bytes(idx, w.kv_lens, bs, Hkv, D)
+    nbytes, parts = decode_bytes(idx, w.kv_lens, bs, Hkv, D, elem=1 if fp8 else 2)
     res = dict(us_per_step=1e3 * step_ms, wall_us_per_step=1e6 * wall / steps, bytes=nbytes, bytes_parts=parts,
                steps=steps)
     del graph, w, cache, idx, out, ws
@@ -376,6 +399,15 @@ def main():
                                        "bytes_parts": d["bytes_parts"],
                                        "traffic": (tr_a + tr_s) if (tr_a and tr_s) else None},
                           "wall_us_per_step": d["wall_us_per_step"]}
+        d8 = run_decode(dspec, SPECS.index(dspec), max(args.steps, 40), args.warmup, fp8=True)
+        gbs8 = d8["bytes"] / (d8["us_per_step"] / 1e6) / 1e9
+        line["decode_fp8"] = {"workload": dspec.name + " (K, V and block cache in fp8 E4M3)",
+                              "us_per_step": d8["us_per_step"], "api": "bsg_decode_step_fp8", "steps": d8["steps"],
+                              "timing": "8 steps per HIP graph replay, HIP events",
+                              "roofline": {"bound": "hbm", "achieved": gbs8, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                           "frac": gbs8 / PEAK_HBM_GBS, "bytes_per_step": d8["bytes"],
+                                           "bytes_parts": d8["bytes_parts"], "traffic": None},
+                              "wall_us_per_step": d8["wall_us_per_step"]}
     else:
         d = run_decode(spec, seed, args.steps, args.warmup)
         gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9

@@ -5,8 +5,8 @@ only marshals torch tensors into its calls.  Build it with
 ``python -m block_sparse_gqa_pool_amd.build``.
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, LIB_PATH, BsgDims, BsgError, block_pool, decode_step, decode_step_gated, decode_step_workspace_bytes,
-    decode_workspace_bytes, dims, group_score,
+    EXPORTS, LIB_PATH, BsgDims, BsgError, block_pool, block_pool_fp8, decode_step, decode_step_fp8, decode_step_gated,
+    decode_step_workspace_bytes, decode_workspace_bytes, dims, group_score, quantize_pages_fp8,
     group_score_topk, group_score_topk_workspace_bytes, lib, sparse_attn_decode, sparse_attn_prefill,
     sparse_attn_prefill_gated, topk_blocks,
 )

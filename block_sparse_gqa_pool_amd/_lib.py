@@ -24,7 +24,8 @@ STATUS = {0: "BSG_OK", -1: "BSG_ERR_NULL", -2: "BSG_ERR_SHAPE", -3: "BSG_ERR_UNS
 EXPORTS = ("bsg_version", "bsg_status_str", "bsg_block_pool", "bsg_group_score", "bsg_topk_blocks",
            "bsg_group_score_topk_workspace_bytes", "bsg_group_score_topk", "bsg_sparse_attn_prefill",
            "bsg_sparse_attn_prefill_gated", "bsg_decode_workspace_bytes", "bsg_sparse_attn_decode",
-           "bsg_decode_step_workspace_bytes", "bsg_decode_step", "bsg_decode_step_gated")
+           "bsg_decode_step_workspace_bytes", "bsg_decode_step", "bsg_decode_step_gated",
+           "bsg_quantize_pages_fp8", "bsg_block_pool_fp8", "bsg_decode_step_fp8")
 
 
 class BsgDims(ctypes.Structure):
@@ -68,6 +69,10 @@ def lib() -> ctypes.CDLL:
             "bsg_decode_step": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, vp, vp], ctypes.c_int),
             "bsg_decode_step_gated": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, i32, vp, vp, vp, vp],
                                       ctypes.c_int),
+            "bsg_quantize_pages_fp8": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "bsg_block_pool_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "bsg_decode_step_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, vp, vp],
+                                    ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -402,4 +407,81 @@ def decode_step_gated(q, kv_lens, block_cache, k_cache, v_cache, page_table, sca
         ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(block_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         float(scale), _ptr(block_idx), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(gate),
         per_dim, _ptr(x), _ptr(out), _ptr(lse), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------- fp8 caches
+def _fp8_pair(codes, scales, name, dev, shape):
+    _req(codes, name + "_codes", torch.uint8, len(shape), dev)
+    _req(scales, name + "_scales", torch.float32, 2, dev)
+    if tuple(codes.shape) != tuple(shape) or tuple(scales.shape) != tuple(shape[:2]):
+        raise ValueError(f"{name}: codes must be {tuple(shape)} uint8 and scales {tuple(shape[:2])} float32")
+
+
+def quantize_pages_fp8(cache, page_table, kv_lens, codes, scales, stream=None):
+    """bsg_quantize_pages_fp8: E4M3 codes + per-(page, head) power-of-two scales of a bf16 paged cache."""
+    _req(cache, "cache", torch.bfloat16, 4)
+    dev = cache.device
+    _tables(page_table, kv_lens, dev)
+    _fp8_pair(codes, scales, "cache", dev, cache.shape)
+    d = dims(cache, page_table, cache.shape[1], 1)
+    _check("bsg_quantize_pages_fp8", lib().bsg_quantize_pages_fp8(
+        ctypes.byref(d), _ptr(cache), _ptr(page_table), _ptr(kv_lens), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def _fp8_dims(k_codes, page_table, num_q_heads, top_k):
+    P, Hkv, bs, D = k_codes.shape
+    B, pts = page_table.shape
+    return BsgDims(B, num_q_heads, Hkv, D, bs, top_k, P, pts, BSG_BF16)
+
+
+def block_pool_fp8(k_codes, k_scales, page_table, kv_lens, rep_codes, rep_scales, blk_begin=None, stream=None):
+    """bsg_block_pool_fp8: the fp8 block cache of the complete blocks from the fp8 key cache."""
+    _req(k_codes, "k_codes", torch.uint8, 4)
+    dev = k_codes.device
+    P, Hkv, bs, D = k_codes.shape
+    _fp8_pair(k_codes, k_scales, "k", dev, k_codes.shape)
+    _tables(page_table, kv_lens, dev)
+    _fp8_pair(rep_codes, rep_scales, "rep", dev, (P, Hkv, D))
+    if blk_begin is not None:
+        _req(blk_begin, "blk_begin", torch.int32, 1, dev)
+        if blk_begin.shape[0] != page_table.shape[0]:
+            raise ValueError("blk_begin must be [B]")
+    d = _fp8_dims(k_codes, page_table, Hkv, 1)
+    _check("bsg_block_pool_fp8", lib().bsg_block_pool_fp8(
+        ctypes.byref(d), _ptr(k_codes), _ptr(k_scales), _ptr(page_table), _ptr(kv_lens), _ptr(blk_begin),
+        _ptr(rep_codes), _ptr(rep_scales), _stream(stream)))
+    return rep_codes, rep_scales
+
+
+def decode_step_fp8(q, kv_lens, rep_codes, rep_scales, k_codes, k_scales, v_codes, v_scales, page_table,
+                    scale: float, block_idx, out, lse=None, workspace=None, stream=None):
+    """bsg_decode_step_fp8: bsg_decode_step over fp8 block, key and value caches (q, out bf16)."""
+    _req(k_codes, "k_codes", torch.uint8, 4)
+    dev = k_codes.device
+    P, Hkv, bs, D = k_codes.shape
+    _fp8_pair(k_codes, k_scales, "k", dev, k_codes.shape)
+    _fp8_pair(v_codes, v_scales, "v", dev, k_codes.shape)
+    _fp8_pair(rep_codes, rep_scales, "rep", dev, (P, Hkv, D))
+    _req(q, "q", torch.bfloat16, 3, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(block_idx, "block_idx", torch.int32, 3, dev)
+    _req(out, "out", torch.bfloat16, 3, dev)
+    B, Hq, D2 = q.shape
+    if out.shape != q.shape or D2 != D or page_table.shape[0] != B or tuple(block_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("shape mismatch between q, out, caches, page_table and block_idx")
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 2, dev)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
+    d = _fp8_dims(k_codes, page_table, Hq, block_idx.shape[2])
+    need = int(lib().bsg_decode_step_workspace_bytes(ctypes.byref(d)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _req(workspace, "workspace", None, None, dev)
+    _check("bsg_decode_step_fp8", lib().bsg_decode_step_fp8(
+        ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(rep_codes), _ptr(rep_scales), _ptr(k_codes), _ptr(k_scales),
+        _ptr(v_codes), _ptr(v_scales), _ptr(page_table), float(scale), _ptr(block_idx), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
     return out

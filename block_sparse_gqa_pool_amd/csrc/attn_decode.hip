@@ -278,12 +278,17 @@ __device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, i
   __syncthreads();
 }
 
-template <int D, int BS, bool FUSED>
+// F8: K and V are OCP E4M3 codes with one scale per (page, head).  Codes become bf16
+// exactly; the K scale multiplies the page's scores and the V scale the page's
+// probabilities before their bf16 rounding (both powers of two, so both products are
+// exact and the result equals the bf16 path on the decoded cache).
+template <int D, int BS, bool FUSED, bool F8>
 __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
-    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
-    const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table, int32_t* __restrict__ block_idx,
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ page_table, int32_t* __restrict__ block_idx,
     const uint64_t* __restrict__ lists, float scale, float* __restrict__ part, int Hq, int Hkv, int top_k,
-    int num_pages, int pt_stride, int nwg, int ppw, int nchunks, int lt) {
+    int num_pages, int pt_stride, int nwg, int ppw, int nchunks, int lt, const float* __restrict__ k_scales,
+    const float* __restrict__ v_scales) {
   constexpr int NDS = D / 32;          // k-steps of the score product
   constexpr int NDT = D / 16;          // 16-wide d tiles of the output
   constexpr int VS = D + DM_VPAD;      // LDS row stride of V (elements)
@@ -339,40 +344,56 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
     const int jj = clampi(j, 0, pt_stride - 1);
     const int p = clampi(page_table[(size_t)b * pt_stride + jj], 0, num_pages - 1);
     const int nk = clampi(pos - jj * BS + 1, 0, BS);
-    const bf16_t* kp = k_cache + (((size_t)p * Hkv + g) * BS) * D;
-    const bf16_t* vp = v_cache + (((size_t)p * Hkv + g) * BS) * D;
+    constexpr int ES = F8 ? 1 : 2;                      // bytes per K/V element
+    const char* kp = reinterpret_cast<const char*>(k_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
+    const char* vp = reinterpret_cast<const char*>(v_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
+    const float sk = F8 ? k_scales[(size_t)p * Hkv + g] : 1.0f;
+    const float sv = F8 ? v_scales[(size_t)p * Hkv + g] : 1.0f;
 #pragma unroll
     for (int h2 = 0; h2 < BS / SUB; h2++) {
       const int kb = h2 * SUB;
       if (kb >= nk) break;
       // V sub-block -> this wave's LDS rows (rows past nk are zero)
       constexpr int PPR = D / 8;
-      uint4 vr[SUB * PPR / 64];
+      uint4 vr[F8 ? 1 : SUB * PPR / 64];
+      uint2 vr8[F8 ? SUB * PPR / 64 : 1];
 #pragma unroll
       for (int i = 0; i < SUB * PPR / 64; i++) {
         const int pc = i * 64 + lane;
         const int r = pc / PPR, c = pc % PPR;
-        vr[i] = (kb + r < nk) ? *reinterpret_cast<const uint4*>(vp + (size_t)(kb + r) * D + 8 * c)
-                              : make_uint4(0, 0, 0, 0);
+        const char* src = vp + ((size_t)(kb + r) * D + 8 * c) * ES;
+        if constexpr (F8)
+          vr8[i] = (kb + r < nk) ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+        else
+          vr[i] = (kb + r < nk) ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
       }
       // scores: S^T tiles of 16 keys
       f32x4_t sacc[SUB / 16];
 #pragma unroll
       for (int T = 0; T < SUB / 16; T++) {
         sacc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        const bf16_t* kr = kp + (size_t)(kb + 16 * T + n) * D + 8 * qd;
+        const char* kr = kp + ((size_t)(kb + 16 * T + n) * D + 8 * qd) * ES;
 #pragma unroll
         for (int s = 0; s < NDS; s++) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(kr + 32 * s);
-          sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(&kv), qb[s], sacc[T],
-                                                              0, 0, 0);
+          bf16x8_t ka;
+          if constexpr (F8) {
+            ka = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(kr + 32 * s));
+          } else {
+            const uint4 kv = *reinterpret_cast<const uint4*>(kr + 64 * s);
+            ka = *reinterpret_cast<const bf16x8_t*>(&kv);
+          }
+          sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], sacc[T], 0, 0, 0);
         }
+        if constexpr (F8) sacc[T] *= sk;
       }
 #pragma unroll
       for (int i = 0; i < SUB * PPR / 64; i++) {
         const int pc = i * 64 + lane;
         const int r = pc / PPR, c = pc % PPR;
-        *reinterpret_cast<uint4*>(Vs + r * VS + 8 * c) = vr[i];
+        if constexpr (F8)
+          *reinterpret_cast<bf16x8_t*>(Vs + r * VS + 8 * c) = e4m3x8_to_bf16(vr8[i]);
+        else
+          *reinterpret_cast<uint4*>(Vs + r * VS + 8 * c) = vr[i];
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -410,8 +431,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
         bf16x8_t pb;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          pb[i] = (__bf16)sacc[2 * k2][i];
-          pb[4 + i] = (__bf16)sacc[2 * k2 + 1][i];
+          pb[i] = (__bf16)(F8 ? sacc[2 * k2][i] * sv : sacc[2 * k2][i]);
+          pb[4 + i] = (__bf16)(F8 ? sacc[2 * k2 + 1][i] * sv : sacc[2 * k2 + 1][i]);
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; dt++) {
@@ -538,13 +559,13 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
     dim3 grid(nwg, d.num_kv_heads, d.batch);
 #define BSG_DM(DD, BB)                                                                                            \
   do {                                                                                                             \
-    auto kfn = attn_decode_mfma_kernel<DD, BB, false>;                                                             \
+    auto kfn = attn_decode_mfma_kernel<DD, BB, false, false>;                                                      \
     hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);  \
     if (ea != hipSuccess) return ea;                                                                               \
     hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache,      \
                        (const bf16_t*)v_cache, page_table, const_cast<int32_t*>(block_idx), nullptr, scale, part,  \
                        d.num_q_heads, d.num_kv_heads, d.top_k, d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d),  \
-                       0, 1);                                                                                      \
+                       0, 1, nullptr, nullptr);                                                                    \
   } while (0)
     if (d.head_dim == 128) {
       if (d.page_size == 64) BSG_DM(128, 64); else BSG_DM(128, 128);
@@ -639,11 +660,12 @@ size_t decode_step_workspace_bytes(const bsg_dims& d) {
 hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
                               const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
                               int32_t* block_idx, void* workspace, void* out, float* lse, hipStream_t stream,
-                              gate_args ga) {
+                              gate_args ga, const float* rep_scales, const float* k_scales, const float* v_scales) {
+  const bool f8 = k_scales != nullptr;
   const size_t a = (decode_select_workspace_bytes(d) + 255) / 256 * 256;
   uint64_t* lists = (uint64_t*)workspace;
   float* part = (float*)((char*)workspace + a);
-  hipError_t e = launch_decode_score_chunks(d, q, kv_lens, block_cache, page_table, lists, stream);
+  hipError_t e = launch_decode_score_chunks(d, q, kv_lens, block_cache, page_table, lists, stream, rep_scales);
   if (e != hipSuccess) return e;
   const int nwg = decode_mfma_nwg(d);
   const int nchunks = decode_select_nchunks(d);
@@ -651,20 +673,26 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
   const size_t smem = decode_step_smem(d, &lt);
   if (smem > 150 * 1024) return hipErrorInvalidValue;
   dim3 grid(nwg, d.num_kv_heads, d.batch);
-#define BSG_DF(DD, BB)                                                                                            \
+#define BSG_DF(DD, BB, F)                                                                                         \
   do {                                                                                                             \
-    auto kfn = attn_decode_mfma_kernel<DD, BB, true>;                                                              \
+    auto kfn = attn_decode_mfma_kernel<DD, BB, true, F>;                                                           \
     hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);  \
     if (ea != hipSuccess) return ea;                                                                               \
-    hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache,      \
-                       (const bf16_t*)v_cache, page_table, block_idx, lists, scale, part, d.num_q_heads,            \
-                       d.num_kv_heads, d.top_k, d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d), nchunks, lt);    \
+    hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, k_cache, v_cache,            \
+                       page_table, block_idx, lists, scale, part, d.num_q_heads, d.num_kv_heads, d.top_k,           \
+                       d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d), nchunks, lt, k_scales, v_scales);         \
+  } while (0)
+#define BSG_DF_F(DD, BB)                 \
+  do {                                   \
+    if (f8) BSG_DF(DD, BB, true);        \
+    else BSG_DF(DD, BB, false);          \
   } while (0)
   if (d.head_dim == 128) {
-    if (d.page_size == 64) BSG_DF(128, 64); else BSG_DF(128, 128);
+    if (d.page_size == 64) BSG_DF_F(128, 64); else BSG_DF_F(128, 128);
   } else {
-    if (d.page_size == 64) BSG_DF(64, 64); else BSG_DF(64, 128);
+    if (d.page_size == 64) BSG_DF_F(64, 64); else BSG_DF_F(64, 128);
   }
+#undef BSG_DF_F
 #undef BSG_DF
   e = hipGetLastError();
   if (e != hipSuccess) return e;

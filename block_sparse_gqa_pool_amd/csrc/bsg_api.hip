@@ -205,4 +205,44 @@ int bsg_decode_step_gated(const bsg_dims* dims, const void* q, const int32_t* kv
                           workspace_bytes, out, lse, stream, {gate, gate_per_dim, x});
 }
 
+int bsg_quantize_pages_fp8(const bsg_dims* dims, const void* src, const int32_t* page_table,
+                           const int32_t* kv_lens, uint8_t* codes, float* scales, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->dtype != BSG_BF16) return BSG_ERR_UNSUPPORTED;
+  if (!src || !page_table || !kv_lens || !codes || !scales) return BSG_ERR_NULL;
+  return to_status(bsg::launch_quantize_pages_fp8(*dims, src, page_table, kv_lens, codes, scales,
+                                                  (hipStream_t)stream));
+}
+
+int bsg_block_pool_fp8(const bsg_dims* dims, const uint8_t* k_codes, const float* k_scales,
+                       const int32_t* page_table, const int32_t* kv_lens, const int32_t* blk_begin,
+                       uint8_t* rep_codes, float* rep_scales, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->dtype != BSG_BF16) return BSG_ERR_UNSUPPORTED;
+  if (!k_codes || !k_scales || !page_table || !kv_lens || !rep_codes || !rep_scales) return BSG_ERR_NULL;
+  return to_status(bsg::launch_block_pool_fp8(*dims, k_codes, k_scales, page_table, kv_lens, blk_begin, rep_codes,
+                                              rep_scales, (hipStream_t)stream));
+}
+
+int bsg_decode_step_fp8(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
+                        const uint8_t* rep_codes, const float* rep_scales, const uint8_t* k_codes,
+                        const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                        const int32_t* page_table, float scale, int32_t* block_idx, void* workspace,
+                        size_t workspace_bytes, void* out, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->dtype != BSG_BF16) return BSG_ERR_UNSUPPORTED;
+  if (!q || !kv_lens || !rep_codes || !rep_scales || !k_codes || !k_scales || !v_codes || !v_scales ||
+      !page_table || !block_idx || !out)
+    return BSG_ERR_NULL;
+  if (!bsg::decode_step_fused_supported(*dims)) return BSG_ERR_UNSUPPORTED;
+  const size_t need = bsg_decode_step_workspace_bytes(dims);
+  if (!workspace || workspace_bytes < need) return BSG_ERR_WORKSPACE;
+  return to_status(bsg::launch_decode_step(*dims, q, kv_lens, rep_codes, k_codes, v_codes, page_table, scale,
+                                           block_idx, workspace, out, lse, (hipStream_t)stream,
+                                           bsg::gate_args{nullptr, 0, nullptr}, rep_scales, k_scales, v_scales));
+}
+
 }  // extern "C"

@@ -34,6 +34,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Eight OCP E4M3 codes (little-endian bytes of two words) -> eight bf16 values, unscaled.
+// Every E4M3 value is exact in bf16; the hardware conversion (v_cvt_pk_f32_fp8) is exact too.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint2 w) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+  bf16x8_t r;
+  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)b[0]; r[3] = (__bf16)b[1];
+  r[4] = (__bf16)c[0]; r[5] = (__bf16)c[1]; r[6] = (__bf16)d[0]; r[7] = (__bf16)d[1];
+  return r;
+}
+
 // Monotone map float -> uint32 (larger float -> larger key); -0.0 is folded onto +0.0.
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s + 0.0f);

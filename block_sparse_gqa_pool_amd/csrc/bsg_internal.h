@@ -47,7 +47,7 @@ hipError_t launch_decode_select(const bsg_dims& d, const void* q, const int32_t*
 int decode_select_nchunks(const bsg_dims& d);
 hipError_t launch_decode_score_chunks(const bsg_dims& d, const void* q, const int32_t* kv_lens,
                                      const void* block_cache, const int32_t* page_table, uint64_t* lists,
-                                     hipStream_t stream);
+                                     hipStream_t stream, const float* rep_scales = nullptr);
 
 // Fused decode step: chunked scoring, then selection + split attention in one kernel, then merge.
 bool decode_step_fused_supported(const bsg_dims& d);
@@ -55,7 +55,15 @@ size_t decode_step_workspace_bytes(const bsg_dims& d);
 hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
                               const void* k_cache, const void* v_cache, const int32_t* page_table, float scale,
                               int32_t* block_idx, void* workspace, void* out, float* lse, hipStream_t stream,
-                              gate_args ga = {nullptr, 0, nullptr});
+                              gate_args ga = {nullptr, 0, nullptr}, const float* rep_scales = nullptr,
+                              const float* k_scales = nullptr, const float* v_scales = nullptr);
+
+// fp8 (OCP E4M3) caches: per-(page, head) power-of-two scales (fp8_cache.hip)
+hipError_t launch_quantize_pages_fp8(const bsg_dims& d, const void* src, const int32_t* page_table,
+                                     const int32_t* kv_lens, uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_block_pool_fp8(const bsg_dims& d, const uint8_t* k_codes, const float* k_scales,
+                                 const int32_t* page_table, const int32_t* kv_lens, const int32_t* blk_begin,
+                                 uint8_t* rep_codes, float* rep_scales, hipStream_t stream);
 
 hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
                                const void* k_cache, const void* v_cache, const int32_t* page_table,

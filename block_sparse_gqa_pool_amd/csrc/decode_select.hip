@@ -27,15 +27,18 @@ constexpr int DS_CH = 64;    // candidate blocks per workgroup of kernel A
 constexpr int DS_NT = 256;
 }  // namespace
 
-template <int D>
+// F8: the block cache holds OCP E4M3 codes with one scale per (page, head) (16 codes per
+// 16-byte piece); the piece sums are then times the representative's scale.
+template <int D, bool F8>
 __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
-    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ block_cache,
-    const int32_t* __restrict__ page_table, uint64_t* __restrict__ lists, int Hq, int Hkv, int bs, int m,
-    int num_pages, int pt_stride, int nchunks, uint32_t ppb_magic) {
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const void* __restrict__ block_cache,
+    const float* __restrict__ rep_scales, const int32_t* __restrict__ page_table, uint64_t* __restrict__ lists,
+    int Hq, int Hkv, int bs, int m, int num_pages, int pt_stride, int nchunks, uint32_t ppb_magic) {
   extern __shared__ __attribute__((aligned(16))) float ds_smem[];
   float* qs = ds_smem;                   // [Hkv][D]
   float* sc = ds_smem + Hkv * D;         // [Hkv][DS_CH]
-  constexpr int SEG = D / 8;             // lanes per (block, group)
+  constexpr int VPP = F8 ? 16 : 8;       // values per 16-byte piece
+  constexpr int SEG = D / VPP;           // lanes per (block, group)
   constexpr int U = 8;                   // 16-byte loads in flight per thread
   const int b = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -63,15 +66,19 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
   static_assert(DS_CH == 64, "one page id per lane");
   const int pid = lane < nloc ? clampi(ptrow[lane], 0, num_pages - 1) : 0;
   uint4 raw[U];
+  float scl[U];                          // F8: the piece's (page, group) scale, segment leaders
+  const char* bc = reinterpret_cast<const char*>(block_cache);
   auto issue = [&](int base) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int pi = base + u * DS_NT + tid;
       const int blk = (int)__umulhi((uint32_t)pi, ppb_magic);   // pi / ppb (exact: pi * ppb < 2^32)
       const int p = __shfl(pid, blk & 63, 64);                  // page of this piece's block
+      const int w = pi - blk * ppb;
       raw[u] = make_uint4(0, 0, 0, 0);
       if (pi < total)
-        raw[u] = *reinterpret_cast<const uint4*>(block_cache + (size_t)p * Hkv * D + (size_t)(pi - blk * ppb) * 8);
+        raw[u] = *reinterpret_cast<const uint4*>(bc + (size_t)p * Hkv * D * (F8 ? 1 : 2) + (size_t)w * 16);
+      if (F8) scl[u] = (pi < total && (lane % SEG) == 0) ? rep_scales[(size_t)p * Hkv + w / SEG] : 0.0f;
     }
   };
   auto consume = [&](int base) {
@@ -80,15 +87,28 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
       const int pi = base + u * DS_NT + tid;
       const int blk = (int)__umulhi((uint32_t)pi, ppb_magic);
       const int w = pi - blk * ppb;
-      const float* qv = qs + (size_t)w * 8;     // (g, d8) of this piece
+      const float* qv = qs + (size_t)w * VPP;   // (g, d-slice) of this piece
       const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
       float s = 0.0f;
+      if constexpr (F8) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        s = fmaf(qv[2 * i], __uint_as_float(wd[i] << 16), s);
-        s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
+        for (int i = 0; i < 4; i++) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], true);
+          s = fmaf(qv[4 * i], lo[0], s);
+          s = fmaf(qv[4 * i + 1], lo[1], s);
+          s = fmaf(qv[4 * i + 2], hi[0], s);
+          s = fmaf(qv[4 * i + 3], hi[1], s);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          s = fmaf(qv[2 * i], __uint_as_float(wd[i] << 16), s);
+          s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
+        }
       }
       s = seg_sum_dpp<SEG>(s);
+      if (F8) s *= scl[u];
       if (pi < total && (lane % SEG) == 0) sc[(w / SEG) * DS_CH + blk] = s;
     }
   };
@@ -218,23 +238,26 @@ bool decode_select_supported(const bsg_dims& d, int q_len) {
 
 hipError_t launch_decode_score_chunks(const bsg_dims& d, const void* q, const int32_t* kv_lens,
                                      const void* block_cache, const int32_t* page_table, uint64_t* lists,
-                                     hipStream_t stream) {
+                                     hipStream_t stream, const float* rep_scales) {
   const int nchunks = decode_select_nchunks(d);
   const int m = d.top_k - 1;
   if (m <= 0) return hipSuccess;
+  const bool f8 = rep_scales != nullptr;
   dim3 grid(nchunks, d.batch);
   const size_t smem = (size_t)(d.num_kv_heads * d.head_dim + d.num_kv_heads * DS_CH) * sizeof(float) +
                       (size_t)(DS_NT / 64) * 64 * sizeof(uint64_t) + (size_t)d.num_q_heads * d.head_dim * 2;
-  const uint32_t ppb = (uint32_t)d.num_kv_heads * (d.head_dim / 8);
-  const uint32_t magic = (uint32_t)((0x100000000ull + ppb - 1) / ppb);   // ceil(2^32 / ppb)
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(decode_score_chunk_kernel<128>, grid, dim3(DS_NT), smem, stream, (const bf16_t*)q, kv_lens,
-                       (const bf16_t*)block_cache, page_table, lists, d.num_q_heads, d.num_kv_heads, d.page_size, m,
-                       d.num_pages, d.pt_stride, nchunks, magic);
-  else
-    hipLaunchKernelGGL(decode_score_chunk_kernel<64>, grid, dim3(DS_NT), smem, stream, (const bf16_t*)q, kv_lens,
-                       (const bf16_t*)block_cache, page_table, lists, d.num_q_heads, d.num_kv_heads, d.page_size, m,
-                       d.num_pages, d.pt_stride, nchunks, magic);
+  const uint32_t ppb = (uint32_t)d.num_kv_heads * (d.head_dim / (f8 ? 16 : 8));   // pieces per block row
+  const uint32_t magic = (uint32_t)((0x100000000ull + ppb - 1) / ppb);             // ceil(2^32 / ppb)
+#define BSG_DSC(DD, F)                                                                                          \
+  hipLaunchKernelGGL((decode_score_chunk_kernel<DD, F>), grid, dim3(DS_NT), smem, stream, (const bf16_t*)q,      \
+                     kv_lens, block_cache, rep_scales, page_table, lists, d.num_q_heads, d.num_kv_heads,         \
+                     d.page_size, m, d.num_pages, d.pt_stride, nchunks, magic)
+  if (d.head_dim == 128) {
+    if (f8) BSG_DSC(128, true); else BSG_DSC(128, false);
+  } else {
+    if (f8) BSG_DSC(64, true); else BSG_DSC(64, false);
+  }
+#undef BSG_DSC
   return hipGetLastError();
 }
 

@@ -245,6 +245,65 @@ int bsg_decode_step_gated(const bsg_dims* dims, const void* q, const int32_t* kv
                           size_t workspace_bytes, const float* gate, int32_t gate_per_dim, const void* x,
                           void* out, float* lse, void* stream);
 
+/*
+ * fp8 KV cache and block cache.  The pages list KV-cache quantisation among the
+ * system-level optimisations that leave the model untouched ("Sparse Attention +
+ * Linear Backbones", section 3) and as a companion of sparse attention ("Sparse
+ * Attention for Long-Context LLMs", section 8); they fix no format.  Format used here:
+ * OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest 448;
+ * no infinities) with one fp32 power-of-two scale per (page, KV head) tile:
+ *     value = decode(code) * scale.
+ * dims describes the bf16 cache the codes stand for (dtype must be BSG_BF16, else
+ * BSG_ERR_UNSUPPORTED); codes use the cache's layout with 1-byte elements.
+ */
+
+/*
+ * bsg_quantize_pages_fp8 -- codes and scales of a bf16 paged cache (K or V).
+ * src: bf16 [P, Hkv, page_size, D].  For every sequence b and every block
+ * j < min(ceil(kv_lens[b] / page_size), pt_stride), with p = page_table[b, j] and
+ * n = min(page_size, kv_lens[b] - j * page_size) valid tokens, and every head g:
+ *     scale[p, g] = 2^e, e the smallest integer with max|src[p, g, :n, :]| <= 448 * 2^e
+ *                   (e = 0 for an all-zero tile; e clamped to [-126, 127]);
+ *     codes[p, g, i, :] = nearest-even E4M3 code of src[p, g, i, :] / 2^e  for i < n,
+ *     codes[p, g, i, :] = 0                                                for i >= n.
+ * codes: uint8 [P, Hkv, page_size, D]; scales: fp32 [P, Hkv].  Tiles of other pages
+ * are not touched.  A page may belong to one sequence only (two sequences sharing a
+ * page would write it concurrently).  Deterministic, bit-exact.
+ */
+int bsg_quantize_pages_fp8(const bsg_dims* dims, const void* src, const int32_t* page_table,
+                           const int32_t* kv_lens, uint8_t* codes, float* scales, void* stream);
+
+/*
+ * bsg_block_pool_fp8 -- fp8 block cache from the fp8 key cache (the block
+ * representative of bsg_block_pool, on the decoded keys).  For each sequence b and each
+ * complete block j in [blk_begin[b], kv_lens[b] / page_size), p = page_table[b, j]:
+ *     mean[g, :] = (sum over tokens i in order, in fp32, of decode(k_codes[p, g, i, :]))
+ *                  * (k_scales[p, g] * (1 / page_size))          (fp32; exact scaling)
+ *     rep_scales[p, g] = 2^e for max|mean[g, :]| as in bsg_quantize_pages_fp8,
+ *     rep_codes[p, g, :] = nearest-even E4M3 codes of mean[g, :] / 2^e.
+ * rep_codes: uint8 [P, Hkv, D]; rep_scales: fp32 [P, Hkv]; blk_begin may be NULL.
+ * Entries of other pages are not touched.  Deterministic, bit-exact.
+ */
+int bsg_block_pool_fp8(const bsg_dims* dims, const uint8_t* k_codes, const float* k_scales,
+                       const int32_t* page_table, const int32_t* kv_lens, const int32_t* blk_begin,
+                       uint8_t* rep_codes, float* rep_scales, void* stream);
+
+/*
+ * bsg_decode_step_fp8 -- bsg_decode_step over fp8 caches: the block scores use the
+ * decoded representatives (rep code * rep scale), attention the decoded keys and values.
+ * The result is the one bsg_decode_step gives on bf16 caches holding the decoded values
+ * (bit for bit: every scale is a power of two, applied exactly).  q and out stay bf16
+ * ([B, Hq, D]); lse fp32 [B, Hq] or NULL; block_idx int32 [B, Hkv, top_k].  Workspace as
+ * bsg_decode_step (bsg_decode_step_workspace_bytes(dims)).  Only the matrix-core decode
+ * path is provided: G <= 16 and the fused selection's limits (bsg_decode_step_workspace_bytes
+ * returns 0 outside them); elsewhere BSG_ERR_UNSUPPORTED.
+ */
+int bsg_decode_step_fp8(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
+                        const uint8_t* rep_codes, const float* rep_scales, const uint8_t* k_codes,
+                        const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                        const int32_t* page_table, float scale, int32_t* block_idx, void* workspace,
+                        size_t workspace_bytes, void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

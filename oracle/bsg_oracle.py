@@ -350,16 +350,22 @@ def e4m3_code(x) -> np.ndarray:
     return (pick | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
 
 
-def fp8_scale_exp(amax: float) -> int:
-    """Smallest integer e with amax <= 448 * 2^e (0 for amax = 0), clamped to [-126, 127].
-    With amax = f * 2^E, 0.5 <= f < 1, and 448 = 0.875 * 2^9: e = E - 9 if f <= 0.875,
-    else E - 8."""
-    amax = float(amax)
-    if amax == 0.0:
-        return 0
-    f, E = math.frexp(amax)
-    e = E - 9 if f <= 0.875 else E - 8
-    return max(-126, min(127, e))
+def fp8_scale_exp(amax):
+    """Smallest integer e with amax <= 448 * 2^e (0 for amax = 0), clamped to [-126, 127];
+    elementwise for arrays.  With amax = f * 2^E, 0.5 <= f < 1, and 448 = 0.875 * 2^9:
+    e = E - 9 if f <= 0.875, else E - 8."""
+    a = np.asarray(amax, np.float64)
+    f, E = np.frexp(a)
+    e = np.where(f <= 0.875, E - 9, E - 8)
+    e = np.clip(np.where(a == 0.0, 0, e), -126, 127).astype(np.int64)
+    return int(e) if e.ndim == 0 else e
+
+
+def _quantize_tiles(x: np.ndarray, axes) -> Tuple[np.ndarray, np.ndarray]:
+    """Codes and exponents of tiles: one scale per index of the axes not in ``axes``."""
+    e = fp8_scale_exp(np.abs(x).max(axis=axes))
+    codes = e4m3_code(x / np.exp2(np.expand_dims(e, axes).astype(np.float64)))
+    return codes, e
 
 
 def quantize_pages_fp8(pages: np.ndarray, page_table: np.ndarray, kv_lens: Sequence[int],
@@ -374,24 +380,28 @@ def quantize_pages_fp8(pages: np.ndarray, page_table: np.ndarray, kv_lens: Seque
     codes = np.zeros((P, Hkv, bs, D), np.uint8)
     scales = np.ones((P, Hkv), np.float32)
     for b, L in enumerate(kv_lens):
-        nblk = min((int(L) + bs - 1) // bs, page_table.shape[1])
-        for j in range(nblk):
-            p = int(page_table[b, j])
-            n = min(bs, int(L) - j * bs)
-            for g in range(Hkv):
-                tile = np.asarray(pages[p, g, :n], np.float64)
-                e = fp8_scale_exp(np.abs(tile).max())
-                codes[p, g, :n] = e4m3_code(tile / 2.0 ** e)
-                codes[p, g, n:] = 0
-                scales[p, g] = 2.0 ** e
+        L = int(L)
+        nblk = min((L + bs - 1) // bs, page_table.shape[1])
+        nfull = min(L // bs, nblk)
+        for j0 in range(0, nfull, 1024):                          # complete pages, in chunks
+            phys = np.asarray(page_table[b, j0:min(nfull, j0 + 1024)], np.int64)
+            c, e = _quantize_tiles(np.asarray(pages[phys], np.float64), (2, 3))
+            codes[phys] = c
+            scales[phys] = np.exp2(e.astype(np.float64))
+        if nblk > nfull:                                          # the partial last page
+            p, n = int(page_table[b, nfull]), L - nfull * bs
+            c, e = _quantize_tiles(np.asarray(pages[p, :, :n], np.float64), (1, 2))
+            codes[p] = 0
+            codes[p, :, :n] = c
+            scales[p] = np.exp2(e.astype(np.float64))
     return codes, scales
 
 
 def fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Decoded values: e4m3_value(code) * scale of the code's (page, head), float64.
-    ``codes`` [P, Hkv, ..., D] and ``scales`` [P, Hkv]."""
+    """Decoded values e4m3_value(code) * scale of the code's (page, head), as float32 (exact:
+    an E4M3 value times a power of two).  ``codes`` [P, Hkv, ..., D], ``scales`` [P, Hkv]."""
     v = e4m3_value(codes)
-    return v * np.asarray(scales, np.float64).reshape(scales.shape + (1,) * (v.ndim - 2))
+    return (v * np.asarray(scales, np.float64).reshape(scales.shape + (1,) * (v.ndim - 2))).astype(np.float32)
 
 
 def block_pool_fp8(k_codes: np.ndarray, k_scales: np.ndarray, page_table: np.ndarray,
@@ -408,14 +418,14 @@ def block_pool_fp8(k_codes: np.ndarray, k_scales: np.ndarray, page_table: np.nda
     for b, L in enumerate(kv_lens):
         begin = 0 if blk_begin is None else int(blk_begin[b])
         end = min(int(L) // bs, page_table.shape[1])
-        for j in range(begin, end):
-            p = int(page_table[b, j])
-            acc = np.zeros((Hkv, D), np.float32)
-            for i in range(bs):                                       # token order
-                acc = acc + e4m3_value(k_codes[p, :, i, :]).astype(np.float32)
-            mean = acc * (np.asarray(k_scales[p], np.float32) * np.float32(1.0 / bs))[:, None]
-            for g in range(Hkv):
-                e = fp8_scale_exp(np.abs(mean[g].astype(np.float64)).max())
-                rc[p, g] = e4m3_code(mean[g].astype(np.float64) / 2.0 ** e)
-                rs[p, g] = 2.0 ** e
+        for j0 in range(begin, end, 1024):
+            phys = np.asarray(page_table[b, j0:min(end, j0 + 1024)], np.int64)
+            vals = e4m3_value(k_codes[phys]).astype(np.float32)           # [n, Hkv, bs, D], exact
+            acc = np.zeros((len(phys), Hkv, D), np.float32)
+            for i in range(bs):                                           # token order
+                acc = acc + vals[:, :, i, :]
+            mean = acc * (np.asarray(k_scales[phys], np.float32) * np.float32(1.0 / bs))[:, :, None]
+            c, e = _quantize_tiles(mean.astype(np.float64), (2,))
+            rc[phys] = c
+            rs[phys] = np.exp2(e.astype(np.float64))
     return rc, rs

@@ -133,3 +133,28 @@ def test_validation_of_gated_calls(L):
     assert ds(BAD, 0, None) == -1
     assert ds(BAD, 3, BAD) == -2
     assert ds(BAD, 1, BAD, need - 1) == -4
+
+
+def test_validation_of_fp8_calls(L):
+    """The fp8 calls reject a non-bf16 dims, NULL pointers and a short workspace before any
+    launch (no device memory is touched: every rejected pointer is a dummy)."""
+    s = None
+    d = ctypes.byref(_dims())
+    df = ctypes.byref(_dims(dtype=_lib.BSG_F32))
+    assert L.bsg_quantize_pages_fp8(df, BAD, BAD, BAD, BAD, BAD, s) == -3
+    assert L.bsg_quantize_pages_fp8(d, None, BAD, BAD, BAD, BAD, s) == -1
+    assert L.bsg_quantize_pages_fp8(d, BAD, BAD, BAD, BAD, None, s) == -1
+    assert L.bsg_block_pool_fp8(df, BAD, BAD, BAD, BAD, None, BAD, BAD, s) == -3
+    assert L.bsg_block_pool_fp8(d, BAD, None, BAD, BAD, None, BAD, BAD, s) == -1
+    need = L.bsg_decode_step_workspace_bytes(d)
+    assert need > 0
+    step = lambda dd, ws, **nul: L.bsg_decode_step_fp8(
+        dd, BAD, BAD, BAD, None if nul.get("rs") else BAD, BAD, BAD, BAD, None if nul.get("vs") else BAD, BAD,
+        0.1, BAD, BAD, ws, BAD, None, s)
+    assert step(df, need) == -3
+    assert step(d, need, rs=True) == -1
+    assert step(d, need, vs=True) == -1
+    assert step(d, need - 1) == -4
+    # outside the matrix-core decode path (G > 16): unsupported
+    dg = ctypes.byref(_dims(num_q_heads=34, num_kv_heads=2))
+    assert step(dg, 1 << 30) == -3
