@@ -283,7 +283,7 @@ __device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, i
 // probabilities before their bf16 rounding (both powers of two, so both products are
 // exact and the result equals the bf16 path on the decoded cache).
 template <int D, int BS, bool FUSED, bool F8>
-__global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ page_table, int32_t* __restrict__ block_idx,
     const uint64_t* __restrict__ lists, float scale, float* __restrict__ part, int Hq, int Hkv, int top_k,
@@ -337,117 +337,170 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
   const int vtr = (16 * 0 + 4 * qd + ((lane & 15) >> 2)) * VS + 4 * (lane & 3);   // tr-read base (key, d)
 
   const int e0 = (blockIdx.x * 4 + wave) * ppw;
-  const int e1 = min(e0 + ppw, top_k);
-  for (int e = e0; e < e1; e++) {
-    const int j = FUSED ? wl[e] : sl[e];
-    if (j < 0) break;
-    const int jj = clampi(j, 0, pt_stride - 1);
-    const int p = clampi(page_table[(size_t)b * pt_stride + jj], 0, num_pages - 1);
-    const int nk = clampi(pos - jj * BS + 1, 0, BS);
-    constexpr int ES = F8 ? 1 : 2;                      // bytes per K/V element
-    const char* kp = reinterpret_cast<const char*>(k_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
-    const char* vp = reinterpret_cast<const char*>(v_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
-    const float sk = F8 ? k_scales[(size_t)p * Hkv + g] : 1.0f;
-    const float sv = F8 ? v_scales[(size_t)p * Hkv + g] : 1.0f;
+  const int e1 = min(e0 + min(ppw, 2), top_k);         // ppw is 1 or 2
+  // the wave's block ids and their pages, fetched together
+  int jv[2], pv[2];
 #pragma unroll
-    for (int h2 = 0; h2 < BS / SUB; h2++) {
-      const int kb = h2 * SUB;
-      if (kb >= nk) break;
-      // V sub-block -> this wave's LDS rows (rows past nk are zero)
-      constexpr int PPR = D / 8;
-      uint4 vr[F8 ? 1 : SUB * PPR / 64];
-      uint2 vr8[F8 ? SUB * PPR / 64 : 1];
+  for (int t = 0; t < 2; t++) {
+    const int e = e0 + t;
+    jv[t] = e < e1 ? (FUSED ? wl[e] : sl[e]) : -1;
+  }
 #pragma unroll
-      for (int i = 0; i < SUB * PPR / 64; i++) {
-        const int pc = i * 64 + lane;
-        const int r = pc / PPR, c = pc % PPR;
-        const char* src = vp + ((size_t)(kb + r) * D + 8 * c) * ES;
-        if constexpr (F8)
-          vr8[i] = (kb + r < nk) ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
-        else
-          vr[i] = (kb + r < nk) ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+  for (int t = 0; t < 2; t++)
+    pv[t] = jv[t] >= 0 ? page_table[(size_t)b * pt_stride + clampi(jv[t], 0, pt_stride - 1)] : 0;
+  constexpr int ES = F8 ? 1 : 2;                        // bytes per K/V element
+  constexpr int NSP = BS / SUB;                         // sub-blocks per page
+  constexpr int PPR = D / 8;                            // 8-element pieces per row
+  constexpr int NV = SUB * PPR / 64;                    // V pieces per lane per sub-block
+  const char* kpg[2];
+  const char* vpg[2];
+  int nkp[2];
+  float skp[2], svp[2];
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int jj = clampi(jv[t], 0, pt_stride - 1);
+    const int p = clampi(pv[t], 0, num_pages - 1);
+    nkp[t] = jv[t] >= 0 ? clampi(pos - jj * BS + 1, 0, BS) : 0;
+    kpg[t] = reinterpret_cast<const char*>(k_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
+    vpg[t] = reinterpret_cast<const char*>(v_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
+    skp[t] = F8 ? k_scales[(size_t)p * Hkv + g] : 1.0f;
+    svp[t] = F8 ? v_scales[(size_t)p * Hkv + g] : 1.0f;
+  }
+  // Raw K/V of one sub-block.  All its loads go out before its first product, so the wave
+  // waits for memory once per sub-block; V rows past nk (inside the page) are loaded too and
+  // zeroed on their way to LDS; K rows past nk give scores that are masked.
+  struct Raw {
+    uint4 v[F8 ? 1 : NV];
+    uint2 v8[F8 ? NV : 1];
+    uint4 k[F8 ? 1 : SUB / 16][NDS];
+    uint2 k8[F8 ? SUB / 16 : 1][NDS];
+  };
+  auto load = [&](int t, int h2, Raw& rw) {
+    const int kb = h2 * SUB;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int pc = i * 64 + lane;
+      const int r = pc / PPR, c = pc % PPR;
+      const char* src = vpg[t] + ((size_t)(kb + r) * D + 8 * c) * ES;
+      if constexpr (F8) rw.v8[i] = *reinterpret_cast<const uint2*>(src);
+      else rw.v[i] = *reinterpret_cast<const uint4*>(src);
+    }
+#pragma unroll
+    for (int T = 0; T < SUB / 16; T++) {
+      const char* kr = kpg[t] + ((size_t)(kb + 16 * T + n) * D + 8 * qd) * ES;
+#pragma unroll
+      for (int s2 = 0; s2 < NDS; s2++) {
+        if constexpr (F8) rw.k8[T][s2] = *reinterpret_cast<const uint2*>(kr + 32 * s2);
+        else rw.k[T][s2] = *reinterpret_cast<const uint4*>(kr + 64 * s2);
       }
-      // scores: S^T tiles of 16 keys
-      f32x4_t sacc[SUB / 16];
+    }
+  };
+  auto compute = [&](int t, int h2, const Raw& rw) {
+    const int kb = h2 * SUB;
+    const int nk = nkp[t];
+    // scores: S^T tiles of 16 keys
+    f32x4_t sacc[SUB / 16];
 #pragma unroll
-      for (int T = 0; T < SUB / 16; T++) {
-        sacc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        const char* kr = kp + ((size_t)(kb + 16 * T + n) * D + 8 * qd) * ES;
+    for (int T = 0; T < SUB / 16; T++) {
+      sacc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int s = 0; s < NDS; s++) {
-          bf16x8_t ka;
-          if constexpr (F8) {
-            ka = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(kr + 32 * s));
-          } else {
-            const uint4 kv = *reinterpret_cast<const uint4*>(kr + 64 * s);
-            ka = *reinterpret_cast<const bf16x8_t*>(&kv);
-          }
-          sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], sacc[T], 0, 0, 0);
-        }
-        if constexpr (F8) sacc[T] *= sk;
+      for (int s2 = 0; s2 < NDS; s2++) {
+        bf16x8_t ka;
+        if constexpr (F8) ka = e4m3x8_to_bf16(rw.k8[T][s2]);
+        else ka = *reinterpret_cast<const bf16x8_t*>(&rw.k[T][s2]);
+        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s2], sacc[T], 0, 0, 0);
+      }
+      if constexpr (F8) sacc[T] *= skp[t];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int pc = i * 64 + lane;
+      const int r = pc / PPR, c = pc % PPR;
+      const bool ok = kb + r < nk;
+      if constexpr (F8) {
+        const bf16x8_t v = e4m3x8_to_bf16(ok ? rw.v8[i] : make_uint2(0, 0));
+        *reinterpret_cast<bf16x8_t*>(Vs + r * VS + 8 * c) = v;
+      } else {
+        *reinterpret_cast<uint4*>(Vs + r * VS + 8 * c) = ok ? rw.v[i] : make_uint4(0, 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < SUB / 16; T++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int key = kb + 16 * T + 4 * qd + i;
+        const float sc = key < nk ? sacc[T][i] : -INFINITY;
+        sacc[T][i] = sc;
+        mx = fmaxf(mx, sc);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+    m_run = m_new;
+    float rs = 0.0f;
+#pragma unroll
+    for (int T = 0; T < SUB / 16; T++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float pe = __builtin_amdgcn_exp2f((sacc[T][i] - m_use) * c2);
+        sacc[T][i] = pe;
+        rs += pe;
+      }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int i = 0; i < NDT; i++) o[i] *= alpha;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k2 = 0; k2 < SUB / 32; k2++) {
+      bf16x8_t pb;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        pb[i] = (__bf16)(F8 ? sacc[2 * k2][i] * svp[t] : sacc[2 * k2][i]);
+        pb[4 + i] = (__bf16)(F8 ? sacc[2 * k2 + 1][i] * svp[t] : sacc[2 * k2 + 1][i]);
       }
 #pragma unroll
-      for (int i = 0; i < SUB * PPR / 64; i++) {
-        const int pc = i * 64 + lane;
-        const int r = pc / PPR, c = pc % PPR;
-        if constexpr (F8)
-          *reinterpret_cast<bf16x8_t*>(Vs + r * VS + 8 * c) = e4m3x8_to_bf16(vr8[i]);
-        else
-          *reinterpret_cast<uint4*>(Vs + r * VS + 8 * c) = vr[i];
+      for (int dt = 0; dt < NDT; dt++) {
+        const bf16_t* vb = Vs + vtr + (32 * k2) * VS + 16 * dt;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb + 16 * VS));
+        bf16x8_t va;
+        *reinterpret_cast<s16x4_t*>(&va) = lo;
+        *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[dt], 0, 0, 0);
       }
-      float mx = -INFINITY;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // units u = (page u / NSP, sub-block u % NSP); a unit exists if its first key is valid
+  auto valid = [&](int u) { return (u % NSP) * SUB < nkp[u / NSP]; };
+  if constexpr (F8 && NSP == 1) {
+    // fp8 sub-blocks take half the registers: with one sub-block per page the next page's
+    // loads are in flight while this one is computed
+    Raw rw[2];
+    if (valid(0)) load(0, 0, rw[0]);
 #pragma unroll
-      for (int T = 0; T < SUB / 16; T++)
+    for (int u = 0; u < 2 * NSP; u++) {
+      if (u + 1 < 2 * NSP && valid(u + 1)) load((u + 1) / NSP, (u + 1) % NSP, rw[(u + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (valid(u)) compute(u / NSP, u % NSP, rw[u & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int key = kb + 16 * T + 4 * qd + i;
-          const float sv = key < nk ? sacc[T][i] : -INFINITY;
-          sacc[T][i] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-      m_run = m_new;
-      float rs = 0.0f;
-#pragma unroll
-      for (int T = 0; T < SUB / 16; T++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const float pe = __builtin_amdgcn_exp2f((sacc[T][i] - m_use) * c2);
-          sacc[T][i] = pe;
-          rs += pe;
-        }
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int i = 0; i < NDT; i++) o[i] *= alpha;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int k2 = 0; k2 < SUB / 32; k2++) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          pb[i] = (__bf16)(F8 ? sacc[2 * k2][i] * sv : sacc[2 * k2][i]);
-          pb[4 + i] = (__bf16)(F8 ? sacc[2 * k2 + 1][i] * sv : sacc[2 * k2 + 1][i]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; dt++) {
-          const bf16_t* vb = Vs + vtr + (32 * k2) * VS + 16 * dt;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb + 16 * VS));
-          bf16x8_t va;
-          *reinterpret_cast<s16x4_t*>(&va) = lo;
-          *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[dt], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int u = 0; u < 2 * NSP; u++) {
+      if (!valid(u)) continue;
+      Raw rw;
+      load(u / NSP, u % NSP, rw);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(u / NSP, u % NSP, rw);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (FUSED && blockIdx.x == 0) {  // the selection, ascending, to block_idx (own block last)
