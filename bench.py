@@ -268,22 +268,29 @@ def cpu_baseline_prefill(spec, seed, n_tokens):
 # ------------------------------------------------------------------------------------
 # HBM traffic from rocprofv3 counters
 TRAFFIC_KERNELS = {
-    # key: (kernel-name substring, source files, workload)
+    # key: (kernel-name substring, source files, workload); the fp8 instantiations carry F8 = true
     "sparse_attn_prefill_s131072": ("attn_prefill_mfma", ["attn_prefill.hip"], "prefill_bf16_s131072"),
-    "decode_attn_b32_ctx131072": ("attn_decode_mfma_kernel", ["attn_decode.hip"], "decode_bf16_b32_ctx131072"),
-    "decode_scan_b32_ctx131072": ("decode_score_chunk_kernel", ["decode_select.hip"], "decode_bf16_b32_ctx131072"),
+    "decode_attn_b32_ctx131072": ("attn_decode_mfma_kernel<128, 64, true, false>", ["attn_decode.hip"],
+                                  "decode_bf16_b32_ctx131072"),
+    "decode_scan_b32_ctx131072": ("decode_score_chunk_kernel<128, false>", ["decode_select.hip"],
+                                  "decode_bf16_b32_ctx131072"),
+    "decode_fp8_attn_b32_ctx131072": ("attn_decode_mfma_kernel<128, 64, true, true>", ["attn_decode.hip"],
+                                      "decode_bf16_b32_ctx131072 in fp8"),
+    "decode_fp8_scan_b32_ctx131072": ("decode_score_chunk_kernel<128, true>", ["decode_select.hip"],
+                                      "decode_bf16_b32_ctx131072 in fp8"),
 }
 CALIB_BYTES = 1 << 30
 
 
 def traffic_run():
-    """One prefill step, one decode step, then a calibration copy of CALIB_BYTES (run under rocprofv3 --pmc)."""
+    """One prefill step, bf16 and fp8 decode steps, then a calibration copy of CALIB_BYTES (run under rocprofv3 --pmc)."""
     import torch
     from workloads import spec_by_name, SPECS
     sp = spec_by_name("prefill_bf16_s131072")
     run_prefill(sp, SPECS.index(sp), 1, 0)
     sd = spec_by_name("decode_bf16_b32_ctx131072")
     run_decode(sd, SPECS.index(sd), 4, 0, graph_replay=False)
+    run_decode(sd, SPECS.index(sd), 4, 0, graph_replay=False, fp8=True)
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -400,13 +407,16 @@ def main():
                                        "traffic": (tr_a + tr_s) if (tr_a and tr_s) else None},
                           "wall_us_per_step": d["wall_us_per_step"]}
         d8 = run_decode(dspec, SPECS.index(dspec), max(args.steps, 40), args.warmup, fp8=True)
+        tr_a8 = _traffic("decode_fp8_attn_b32_ctx131072", ["attn_decode.hip"])
+        tr_s8 = _traffic("decode_fp8_scan_b32_ctx131072", ["decode_select.hip"])
         gbs8 = d8["bytes"] / (d8["us_per_step"] / 1e6) / 1e9
         line["decode_fp8"] = {"workload": dspec.name + " (K, V and block cache in fp8 E4M3)",
                               "us_per_step": d8["us_per_step"], "api": "bsg_decode_step_fp8", "steps": d8["steps"],
                               "timing": "8 steps per HIP graph replay, HIP events",
                               "roofline": {"bound": "hbm", "achieved": gbs8, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                            "frac": gbs8 / PEAK_HBM_GBS, "bytes_per_step": d8["bytes"],
-                                           "bytes_parts": d8["bytes_parts"], "traffic": None},
+                                           "bytes_parts": d8["bytes_parts"],
+                                           "traffic": (tr_a8 + tr_s8) if (tr_a8 and tr_s8) else None},
                               "wall_us_per_step": d8["wall_us_per_step"]}
     else:
         d = run_decode(spec, seed, args.steps, args.warmup)
