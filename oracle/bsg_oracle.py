@@ -49,6 +49,20 @@ What is computed, with the passage each step follows:
    scale / page_size, quantised the same way per (page, head).  Attention and
    scores then run on the decoded values (code value times scale), exactly as
    steps 2-4 on a float cache.
+7. Token-level selection (optional; "Sparse Attention + Linear Backbones",
+   sections 5.1-5.3 and the pseudocode of 5.5: an indexer scores every
+   earlier position, the 2048 highest-scoring positions are kept per query,
+   attention runs over those; the indexer uses no positional encoding).  The
+   learned indexer is absent, so the index is the identity one: the score of
+   token s for the query heads of group g is the sum over the group's heads of
+   q . k_s (the block score of step 2 at granularity one).  Candidates are the
+   tokens at or before the query's position; the top K are kept by (score,
+   lower index first), sorted ascending, padded with -1; attention is exact
+   over the kept tokens.
+8. Two-level selection (optional; "Sparse Attention for Long-Context LLMs",
+   section 8: coarse filtering followed by fine filtering): the block top-k of
+   step 3, then the token top-K of step 7 among the tokens of the kept blocks
+   (causal inside the own block), then attention over the kept tokens.
 
 Precision: attention and scores are computed in float64.  Two results are
 codes decided by floating point, and those decisions are taken in the
@@ -69,6 +83,7 @@ __all__ = [
     "query_positions", "group_scores", "select_blocks",
     "sparse_attention", "prefill_reference", "decode_reference", "gated_fusion",
     "e4m3_value", "e4m3_code", "fp8_scale_exp", "quantize_pages_fp8", "fp8_dequant", "block_pool_fp8",
+    "token_scores", "select_tokens", "token_attention", "decode_tokens_reference", "two_level_decode_reference",
 ]
 
 
@@ -429,3 +444,120 @@ def block_pool_fp8(k_codes: np.ndarray, k_scales: np.ndarray, page_table: np.nda
             rc[phys] = c
             rs[phys] = np.exp2(e.astype(np.float64))
     return rc, rs
+
+
+# ----------------------------------------------------------------------------
+# 7. token-level selection, 8. two-level selection
+# ----------------------------------------------------------------------------
+def token_scores(q: np.ndarray, k_pages: np.ndarray, page_table: np.ndarray, kv_lens: Sequence[int],
+                 t_idx: Optional[Sequence[int]] = None, block_idx: Optional[np.ndarray] = None) -> np.ndarray:
+    """Scores [B, Hkv, T, L_max] in float64 (L_max = longest sequence): for query t of group g
+    at position p, scores[.., s] = sum over the group's heads h of q[h, t] . k[s] for the
+    candidate tokens s, -inf elsewhere.  Candidates: s <= p; with ``block_idx``
+    [B, Hkv, T, k] (two-level selection) only the tokens of the listed blocks."""
+    B, Hq, q_len, D = q.shape
+    _, Hkv, bs, _ = k_pages.shape
+    G = Hq // Hkv
+    tsel = np.arange(q_len) if t_idx is None else np.asarray(t_idx, dtype=np.int64)
+    T = len(tsel)
+    Lmax = int(max(kv_lens))
+    out = np.full((B, Hkv, T, Lmax), -np.inf, np.float64)
+    for b in range(B):
+        L = int(kv_lens[b])
+        keys = gather_tokens(k_pages, page_table[b], L).astype(np.float64)      # [Hkv, L, D]
+        pos = query_positions(L, q_len, tsel)
+        for g in range(Hkv):
+            qs = np.asarray(q[b, g * G:(g + 1) * G][:, tsel], np.float64).sum(axis=0)   # [T, D]
+            sc = qs @ keys[g].T                                                    # [T, L]
+            cand = np.arange(L)[None, :] <= pos[:, None]
+            if block_idx is not None:
+                inblk = np.zeros((T, L), bool)
+                for ti in range(T):
+                    for j in block_idx[b, g, ti]:
+                        if j >= 0:
+                            inblk[ti, int(j) * bs:min(L, (int(j) + 1) * bs)] = True
+                cand &= inblk
+            out[b, g, :, :L] = np.where(cand, sc, -np.inf)
+    return out
+
+
+def select_tokens(scores: np.ndarray, top_k: int) -> np.ndarray:
+    """Kept tokens [B, Hkv, T, top_k] (int32, ascending, -1 padded): the top_k candidates
+    (finite scores) by score, higher first, equal scores lower index first, decided on the
+    float32 rounding of the scores."""
+    B, Hkv, T, L = scores.shape
+    s32 = scores.astype(np.float32)
+    out = np.full((B, Hkv, T, top_k), -1, np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            for t in range(T):
+                row = s32[b, g, t]
+                cand = np.nonzero(np.isfinite(row))[0]
+                order = cand[np.lexsort((cand, -row[cand]))]                        # score desc, index asc
+                keep = np.sort(order[:top_k])
+                out[b, g, t, :len(keep)] = keep
+    return out
+
+
+def token_attention(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, page_table: np.ndarray,
+                    kv_lens: Sequence[int], token_idx: np.ndarray, scale: float,
+                    t_idx: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(out [B, Hq, T, D], lse [B, Hq, T]) in float64: softmax((q . k_s) * scale) over the
+    kept tokens s of ``token_idx`` [B, Hkv, T, K] (the query's group), times v_s."""
+    B, Hq, q_len, D = q.shape
+    _, Hkv, bs, _ = k_pages.shape
+    G = Hq // Hkv
+    tsel = np.arange(q_len) if t_idx is None else np.asarray(t_idx, dtype=np.int64)
+    T = len(tsel)
+    out = np.zeros((B, Hq, T, D), np.float64)
+    lse = np.full((B, Hq, T), -np.inf, np.float64)
+    for b in range(B):
+        L = int(kv_lens[b])
+        keys = gather_tokens(k_pages, page_table[b], L).astype(np.float64)
+        vals = gather_tokens(v_pages, page_table[b], L).astype(np.float64)
+        for g in range(Hkv):
+            for ti in range(T):
+                sel = np.asarray([int(x) for x in token_idx[b, g, ti] if x >= 0], np.int64)
+                if sel.size == 0:
+                    continue
+                qh = np.asarray(q[b, g * G:(g + 1) * G, tsel[ti]], np.float64)      # [G, D]
+                z = (qh @ keys[g, sel].T) * scale
+                m = z.max(axis=1, keepdims=True)
+                w = np.exp(z - m)
+                l = w.sum(axis=1, keepdims=True)
+                out[b, g * G:(g + 1) * G, ti] = (w @ vals[g, sel]) / l
+                lse[b, g * G:(g + 1) * G, ti] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def decode_tokens_reference(q, k_pages, v_pages, page_table, kv_lens, top_k_tokens: int,
+                            scale: Optional[float] = None):
+    """Token-level decode step (q_len = 1): token scores -> token top-K -> attention.
+    Returns dict(scores, token_idx, out, lse)."""
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    sc = token_scores(q, k_pages, page_table, kv_lens)
+    idx = select_tokens(sc, top_k_tokens)
+    out, lse = token_attention(q, k_pages, v_pages, page_table, kv_lens, idx, scale)
+    return dict(scores=sc, token_idx=idx, out=out, lse=lse)
+
+
+def two_level_decode_reference(q, k_pages, v_pages, page_table, kv_lens, page_size, top_k_blocks: int,
+                               top_k_tokens: int, cache_dtype, scale: Optional[float] = None, block_cache=None):
+    """Two-level decode step (q_len = 1): block scores -> block top-k (steps 1-3) -> token
+    scores over the kept blocks' tokens -> token top-K -> attention.  Returns dict(block_cache,
+    block_scores, block_idx, scores, token_idx, out, lse)."""
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    Hkv = k_pages.shape[1]
+    if block_cache is None:
+        block_cache = block_pool(k_pages, page_table, kv_lens, cache_dtype)
+    bsc = group_scores(q, block_cache, page_table, kv_lens, Hkv, page_size)
+    bidx = select_blocks(bsc, kv_lens, 1, page_size, top_k_blocks)
+    sc = token_scores(q, k_pages, page_table, kv_lens, block_idx=bidx)
+    idx = select_tokens(sc, top_k_tokens)
+    out, lse = token_attention(q, k_pages, v_pages, page_table, kv_lens, idx, scale)
+    return dict(block_cache=block_cache, block_scores=bsc, block_idx=bidx, scores=sc, token_idx=idx, out=out,
+                lse=lse)

@@ -594,3 +594,91 @@ def test_block_pool_fp8_closed_forms():
     # untouched pages keep their entries; blk_begin skips earlier blocks
     rc3, rs3 = O.block_pool_fp8(codes, scales, pt, kv, blk_begin=[2, 1])
     assert np.all(rc3[int(pt[0, 0])] == 0) and np.array_equal(rc3[int(pt[0, 2])], rc1[int(pt[0, 2])])
+
+
+# ----------------------------------------------------------------------------
+# token-level and two-level selection: scores against torch einsum, the selection's
+# threshold property by brute force, reductions to dense and to block-level attention
+# ----------------------------------------------------------------------------
+def _decode_case(seed, B=2, L=(64 * 5 + 9, 64 * 3 + 40), Hq=8, Hkv=2, D=64, shuffle=True):
+    spec = SPECS[2].replace(batch=B, ctx_len=0, ctx_range=(min(L), max(L)), num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim=D, dtype="f32", shuffle_pages=shuffle)
+    w = make_workload(spec, seed)
+    q, kp, vp, pt, kv = _np(w)
+    return spec, q, kp, vp, pt, kv
+
+
+def test_token_scores_match_einsum_and_causality():
+    spec, q, kp, vp, pt, kv = _decode_case(31)
+    sc = O.token_scores(q, kp, pt, kv)
+    G = spec.num_q_heads // spec.num_kv_heads
+    for b, L in enumerate(kv):
+        K = torch.from_numpy(O.gather_tokens(kp, pt[b], L).astype(np.float64))        # [Hkv, L, D]
+        qt = torch.from_numpy(q[b, :, 0].astype(np.float64)).view(spec.num_kv_heads, G, -1)
+        ref = torch.einsum("ghd,gsd->gs", qt, K).numpy()
+        np.testing.assert_allclose(sc[b, :, 0, :L], ref, rtol=1e-12, atol=1e-12)
+        assert np.all(np.isneginf(sc[b, :, 0, L:]))
+    # prefill-shaped queries: tokens after the query's position are not candidates
+    spec2 = SPECS[0].replace(seq_len=200)
+    w = make_workload(spec2, 32)
+    q2, kp2, vp2, pt2, kv2 = _np(w)
+    s2 = O.token_scores(q2, kp2, pt2, kv2, t_idx=[0, 63, 64, 199])
+    for ti, t in enumerate([0, 63, 64, 199]):
+        assert np.all(np.isfinite(s2[0, :, ti, :t + 1])) and np.all(np.isneginf(s2[0, :, ti, t + 1:]))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_select_tokens_threshold_property(seed):
+    rng = np.random.default_rng(seed)
+    sc = np.round(rng.standard_normal((2, 3, 2, 300)) * 4) / 4              # many exact ties
+    sc[..., 250:] = -np.inf                                                 # not candidates
+    sc[1, 0, 1, 7:] = -np.inf                                               # fewer candidates than K
+    K = 40
+    idx = O.select_tokens(sc, K)
+    for b, g, t in itertools.product(range(2), range(3), range(2)):
+        row = sc[b, g, t].astype(np.float32)
+        cand = np.nonzero(np.isfinite(row))[0]
+        kept = [int(x) for x in idx[b, g, t] if x >= 0]
+        assert kept == sorted(set(kept)) and len(kept) == min(K, len(cand))
+        assert np.all(idx[b, g, t, len(kept):] == -1)
+        dropped = sorted(set(cand.tolist()) - set(kept))
+        for i in kept:                                   # every kept token beats every dropped one
+            for j in dropped:
+                assert row[i] > row[j] or (row[i] == row[j] and i < j)
+
+
+def test_token_topk_of_all_tokens_is_dense_gqa():
+    spec, q, kp, vp, pt, kv = _decode_case(33)
+    r = O.decode_tokens_reference(q, kp, vp, pt, kv, top_k_tokens=max(kv))
+    G = spec.num_q_heads // spec.num_kv_heads
+    for b, L in enumerate(kv):
+        K = O.gather_tokens(kp, pt[b], L).astype(np.float64)
+        V = O.gather_tokens(vp, pt[b], L).astype(np.float64)
+        ref = _sdpa_dense(q[b:b + 1].astype(np.float64), np.repeat(K, G, axis=0)[None],
+                          np.repeat(V, G, axis=0)[None], scale=1.0 / math.sqrt(q.shape[-1]))
+        np.testing.assert_allclose(r["out"][b], ref[0], rtol=1e-10, atol=1e-12)
+
+
+def test_two_level_reduces_to_block_and_to_token_selection():
+    spec, q, kp, vp, pt, kv = _decode_case(34)
+    bs, kb = spec.page_size, 3
+    # every token of the kept blocks kept -> the block-level decode step
+    r2 = O.two_level_decode_reference(q, kp, vp, pt, kv, bs, kb, kb * bs, "f32")
+    rb = O.decode_reference(q, kp, vp, pt, kv, bs, kb, "f32")
+    assert np.array_equal(r2["block_idx"], rb["block_idx"])
+    np.testing.assert_allclose(r2["out"], rb["out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r2["lse"], rb["lse"], rtol=1e-12, atol=1e-12)
+    # every block kept -> the token-level step
+    nb = max((L + bs - 1) // bs for L in kv)
+    Kt = 50
+    r3 = O.two_level_decode_reference(q, kp, vp, pt, kv, bs, nb + 1, Kt, "f32")
+    rt = O.decode_tokens_reference(q, kp, vp, pt, kv, Kt)
+    assert np.array_equal(r3["token_idx"], rt["token_idx"])
+    np.testing.assert_allclose(r3["out"], rt["out"], rtol=1e-12, atol=1e-12)
+    # the kept tokens lie in the kept blocks and are the best of those blocks' tokens
+    r4 = O.two_level_decode_reference(q, kp, vp, pt, kv, bs, kb, 70, "f32")
+    for b in range(len(kv)):
+        for g in range(spec.num_kv_heads):
+            blocks = set(int(j) for j in r4["block_idx"][b, g, 0] if j >= 0)
+            toks = [int(s) for s in r4["token_idx"][b, g, 0] if s >= 0]
+            assert len(toks) == 70 and all(s // bs in blocks for s in toks)
