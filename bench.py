@@ -87,6 +87,74 @@ def decode_bytes(block_idx, kv_lens, page_size, Hkv, D, elem=2):
     return kv + reps + pt + sc, dict(selected_kv=kv, block_cache=reps, page_table=pt, scales=sc)
 
 
+def run_decode_tokens(spec, seed, steps, warmup, top_k_tokens, two_level):
+    """Token-level (two_level False) or two-level decode steps, graph-replayed like run_decode.
+    Algorithmic bytes: token level reads every key once (the identity indexer scores all
+    tokens) plus the kept tokens' values and the page table; two level reads the block cache
+    of every candidate, the keys of the kept blocks, and the kept tokens' values."""
+    import torch
+    import block_sparse_gqa_pool_amd as bsg
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    w = make_workload(spec, seed, device=dev)
+    B, Hq, _, D = w.q.shape
+    Hkv, bs, k = spec.num_kv_heads, spec.page_size, spec.top_k
+    scale = 1.0 / math.sqrt(D)
+    q1 = w.q[:, :, 0].contiguous()
+    out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=dev)
+    tok = torch.empty(B, Hkv, top_k_tokens, dtype=torch.int32, device=dev)
+    cache = bidx = None
+    if two_level:
+        cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
+        bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+        bidx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+    d = bsg.dims(w.k_cache, w.page_table, Hq, k if two_level else 1)
+    import ctypes
+    need = int(bsg.lib().bsg_decode_step_tokens_workspace_bytes(ctypes.byref(d), top_k_tokens, int(two_level)))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bsg.decode_step_tokens(q1, w.kv_lens, w.k_cache, w.v_cache, w.page_table, scale, tok, out,
+                               block_cache=cache, block_idx=bidx, workspace=ws)
+
+    PER_GRAPH = 4
+    for _ in range(max(warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(PER_GRAPH):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, (steps + PER_GRAPH - 1) // PER_GRAPH)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_rep):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    steps = n_rep * PER_GRAPH
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    L = w.kv_lens.long()
+    kept = float((tok >= 0).sum().item())
+    v_bytes = kept * D * 2
+    pt = float(((L + bs - 1) // bs).sum().item()) * 4
+    if two_level:
+        own = (L - 1) // bs
+        reps = float(own.sum().item()) * Hkv * D * 2
+        nb = float((bidx >= 0).sum().item())
+        parts = dict(block_cache=reps, kept_block_keys=nb * bs * D * 2, kept_token_values=v_bytes, page_table=pt)
+    else:
+        parts = dict(all_keys=float(L.sum().item()) * Hkv * D * 2, kept_token_values=v_bytes, page_table=pt)
+    nbytes = sum(parts.values())
+    del graph, w, cache, bidx, tok, out, ws
+    torch.cuda.empty_cache()
+    return dict(us_per_step=us, bytes=nbytes, bytes_parts=parts, steps=steps)
+
+
 # ------------------------------------------------------------------------------------
 def run_prefill(spec, seed, steps, warmup):
     import torch
@@ -418,6 +486,16 @@ def main():
                                            "bytes_parts": d8["bytes_parts"],
                                            "traffic": (tr_a8 + tr_s8) if (tr_a8 and tr_s8) else None},
                               "wall_us_per_step": d8["wall_us_per_step"]}
+        for key, K, two in (("decode_tokens", 2048, False), ("decode_two_level", 512, True)):
+            dt = run_decode_tokens(dspec, SPECS.index(dspec), max(args.steps, 16), args.warmup, K, two)
+            gbt = dt["bytes"] / (dt["us_per_step"] / 1e6) / 1e9
+            line[key] = {"workload": dspec.name + (f" (block top-{dspec.top_k}, then token top-{K})" if two
+                                                   else f" (token top-{K})"),
+                         "us_per_step": dt["us_per_step"], "api": "bsg_decode_step_tokens", "steps": dt["steps"],
+                         "timing": "4 steps per HIP graph replay, HIP events",
+                         "roofline": {"bound": "hbm", "achieved": gbt, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": gbt / PEAK_HBM_GBS, "bytes_per_step": dt["bytes"],
+                                      "bytes_parts": dt["bytes_parts"], "traffic": None}}
     else:
         d = run_decode(spec, seed, args.steps, args.warmup)
         gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9

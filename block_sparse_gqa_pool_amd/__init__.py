@@ -6,7 +6,8 @@ only marshals torch tensors into its calls.  Build it with
 """
 from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, BsgDims, BsgError, block_pool, block_pool_fp8, decode_step, decode_step_fp8, decode_step_gated,
-    decode_step_workspace_bytes, decode_workspace_bytes, dims, group_score, quantize_pages_fp8,
+    decode_step_tokens, decode_step_workspace_bytes, decode_workspace_bytes, dims, group_score, quantize_pages_fp8,
+    sparse_attn_decode_tokens, token_topk,
     group_score_topk, group_score_topk_workspace_bytes, lib, sparse_attn_decode, sparse_attn_prefill,
     sparse_attn_prefill_gated, topk_blocks,
 )

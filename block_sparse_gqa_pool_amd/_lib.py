@@ -25,7 +25,9 @@ EXPORTS = ("bsg_version", "bsg_status_str", "bsg_block_pool", "bsg_group_score",
            "bsg_group_score_topk_workspace_bytes", "bsg_group_score_topk", "bsg_sparse_attn_prefill",
            "bsg_sparse_attn_prefill_gated", "bsg_decode_workspace_bytes", "bsg_sparse_attn_decode",
            "bsg_decode_step_workspace_bytes", "bsg_decode_step", "bsg_decode_step_gated",
-           "bsg_quantize_pages_fp8", "bsg_block_pool_fp8", "bsg_decode_step_fp8")
+           "bsg_quantize_pages_fp8", "bsg_block_pool_fp8", "bsg_decode_step_fp8",
+           "bsg_token_topk_workspace_bytes", "bsg_token_topk", "bsg_decode_tokens_workspace_bytes",
+           "bsg_sparse_attn_decode_tokens", "bsg_decode_step_tokens_workspace_bytes", "bsg_decode_step_tokens")
 
 
 class BsgDims(ctypes.Structure):
@@ -73,6 +75,13 @@ def lib() -> ctypes.CDLL:
             "bsg_block_pool_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "bsg_decode_step_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, vp, vp],
                                     ctypes.c_int),
+            "bsg_token_topk_workspace_bytes": ([dp, i32], sz),
+            "bsg_token_topk": ([dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp], ctypes.c_int),
+            "bsg_decode_tokens_workspace_bytes": ([dp, i32], sz),
+            "bsg_sparse_attn_decode_tokens": ([dp, vp, vp, vp, vp, vp, vp, i32, f32, vp, sz, vp, vp, vp], ctypes.c_int),
+            "bsg_decode_step_tokens_workspace_bytes": ([dp, i32, i32], sz),
+            "bsg_decode_step_tokens": ([dp, vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, sz, vp, vp, vp],
+                                       ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -483,5 +492,103 @@ def decode_step_fp8(q, kv_lens, rep_codes, rep_scales, k_codes, k_scales, v_code
     _check("bsg_decode_step_fp8", lib().bsg_decode_step_fp8(
         ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(rep_codes), _ptr(rep_scales), _ptr(k_codes), _ptr(k_scales),
         _ptr(v_codes), _ptr(v_scales), _ptr(page_table), float(scale), _ptr(block_idx), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------- token-level selection
+def _ws(workspace, need, dev):
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _req(workspace, "workspace", None, None, dev)
+    return workspace
+
+
+def token_topk(q, kv_lens, k_cache, page_table, token_idx, block_idx=None, workspace=None, stream=None):
+    """bsg_token_topk: q [B, Hq, D] -> token_idx [B, Hkv, K] (K = token_idx.shape[2]);
+    block_idx [B, Hkv, k] makes it two-level."""
+    _req(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _req(q, "q", torch.bfloat16, 3, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(token_idx, "token_idx", torch.int32, 3, dev)
+    P, Hkv, bs, D = k_cache.shape
+    B, Hq, _ = q.shape
+    if tuple(token_idx.shape[:2]) != (B, Hkv) or q.shape[2] != D:
+        raise ValueError("shape mismatch between q, k_cache and token_idx")
+    kb = 1
+    if block_idx is not None:
+        _req(block_idx, "block_idx", torch.int32, 3, dev)
+        if tuple(block_idx.shape[:2]) != (B, Hkv):
+            raise ValueError("block_idx must be [B, Hkv, k]")
+        kb = block_idx.shape[2]
+    d = dims(k_cache, page_table, Hq, kb)
+    workspace = _ws(workspace, int(lib().bsg_token_topk_workspace_bytes(ctypes.byref(d), int(block_idx is not None))),
+                    dev)
+    _check("bsg_token_topk", lib().bsg_token_topk(
+        ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(k_cache), _ptr(page_table), _ptr(block_idx),
+        token_idx.shape[2], _ptr(token_idx), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return token_idx
+
+
+def sparse_attn_decode_tokens(q, kv_lens, k_cache, v_cache, page_table, token_idx, scale: float, out, lse=None,
+                              workspace=None, stream=None):
+    """bsg_sparse_attn_decode_tokens: attention of q [B, Hq, D] over token_idx [B, Hkv, K]."""
+    _req(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _req(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _req(q, "q", torch.bfloat16, 3, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(token_idx, "token_idx", torch.int32, 3, dev)
+    _req(out, "out", torch.bfloat16, 3, dev)
+    B, Hq, D = q.shape
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or tuple(token_idx.shape[:2]) != (B, k_cache.shape[1]):
+        raise ValueError("shape mismatch between q, out, caches and token_idx")
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 2, dev)
+    K = token_idx.shape[2]
+    d = dims(k_cache, page_table, Hq, 1)
+    workspace = _ws(workspace, int(lib().bsg_decode_tokens_workspace_bytes(ctypes.byref(d), K)), dev)
+    _check("bsg_sparse_attn_decode_tokens", lib().bsg_sparse_attn_decode_tokens(
+        ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(token_idx), K,
+        float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _stream(stream)))
+    return out
+
+
+def decode_step_tokens(q, kv_lens, k_cache, v_cache, page_table, scale: float, token_idx, out, lse=None,
+                       block_cache=None, block_idx=None, workspace=None, stream=None):
+    """bsg_decode_step_tokens: token-level step, or two-level when block_cache and block_idx
+    [B, Hkv, k] are given (the block selection is written to block_idx)."""
+    _req(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _req(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _req(q, "q", torch.bfloat16, 3, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(token_idx, "token_idx", torch.int32, 3, dev)
+    _req(out, "out", torch.bfloat16, 3, dev)
+    B, Hq, D = q.shape
+    P, Hkv, bs, _ = k_cache.shape
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or tuple(token_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("shape mismatch between q, out, caches and token_idx")
+    two = block_idx is not None
+    kb = 1
+    if two:
+        if block_cache is None:
+            raise ValueError("two-level steps need block_cache")
+        _req(block_cache, "block_cache", torch.bfloat16, 3, dev)
+        _req(block_idx, "block_idx", torch.int32, 3, dev)
+        if tuple(block_idx.shape[:2]) != (B, Hkv) or tuple(block_cache.shape) != (P, Hkv, D):
+            raise ValueError("block_idx must be [B, Hkv, k] and block_cache [P, Hkv, D]")
+        kb = block_idx.shape[2]
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 2, dev)
+    K = token_idx.shape[2]
+    d = dims(k_cache, page_table, Hq, kb)
+    workspace = _ws(workspace, int(lib().bsg_decode_step_tokens_workspace_bytes(ctypes.byref(d), K, int(two))), dev)
+    _check("bsg_decode_step_tokens", lib().bsg_decode_step_tokens(
+        ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(block_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        K, int(two), float(scale), _ptr(block_idx), _ptr(token_idx), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
     return out

@@ -562,6 +562,255 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Attention over a token list (token-level and two-level selection): the decode kernel above
+// with its 64-key sub-blocks taken from consecutive entries of the row's ascending token list
+// instead of one page.  Each lane looks up the page of one entry; a key row's address then
+// reaches the lanes that read it by shuffle.  Entries are kept tokens followed by -1 padding,
+// so the valid keys of a sub-block are a prefix of it.
+template <int D, int BS>
+__global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
+    const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ token_idx, int Kt, float scale, float* __restrict__ part, int Hq, int Hkv,
+    int num_pages, int pt_stride, int nwg, int ppw) {
+  constexpr int NDS = D / 32;
+  constexpr int NDT = D / 16;
+  constexpr int VS = D + DM_VPAD;
+  constexpr int SUB = 64;
+  constexpr int PPR = D / 8;
+  constexpr int NV = SUB * PPR / 64;
+  extern __shared__ __attribute__((aligned(16))) unsigned char dm_smem[];
+  const int G = Hq / Hkv;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, qd = lane >> 4;
+  bf16_t* Vs = reinterpret_cast<bf16_t*>(dm_smem) + (size_t)wave * SUB * VS;
+  const float c2 = scale * 1.4426950408889634f;
+  const int32_t* trow = token_idx + ((size_t)b * Hkv + g) * Kt;
+  (void)kv_lens;
+
+  bf16x8_t qb[NDS];
+  {
+    const bool hv = n < G;
+    const bf16_t* qp = q + ((size_t)b * Hq + (size_t)g * G + (hv ? n : 0)) * D + 8 * qd;
+#pragma unroll
+    for (int s = 0; s < NDS; s++) {
+      uint4 v = hv ? *reinterpret_cast<const uint4*>(qp + 32 * s) : make_uint4(0, 0, 0, 0);
+      qb[s] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; i++) o[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int vtr = (4 * qd + ((lane & 15) >> 2)) * VS + 4 * (lane & 3);
+
+  // this wave's (at most two) sub-blocks of the list: tokens, then their pages, together
+  const int u0 = (blockIdx.x * 4 + wave) * min(ppw, 2);
+  int tok[2];
+  long long rb[2];
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int e = (u0 + t) * SUB + lane;
+    tok[t] = (t < ppw && e < Kt) ? trow[e] : -1;
+  }
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int pid = tok[t] >= 0 ? clampi(page_table[(size_t)b * pt_stride + min(tok[t] / BS, pt_stride - 1)], 0,
+                                         num_pages - 1)
+                                : 0;
+    rb[t] = tok[t] >= 0 ? ((((long long)pid * Hkv + g) * BS + tok[t] % BS) * D) : 0;
+  }
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int nk = __popcll(__ballot(tok[t] >= 0));     // valid keys: a prefix of the sub-block
+    if (nk == 0) break;
+    uint4 vr[NV];
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int pc = i * 64 + lane;
+      const long long base = __shfl(rb[t], pc / PPR, 64);
+      vr[i] = *reinterpret_cast<const uint4*>(v_cache + base + 8 * (pc % PPR));
+    }
+    uint4 kr[SUB / 16][NDS];
+#pragma unroll
+    for (int T = 0; T < SUB / 16; T++) {
+      const long long base = __shfl(rb[t], 16 * T + n, 64);
+#pragma unroll
+      for (int s2 = 0; s2 < NDS; s2++) kr[T][s2] = *reinterpret_cast<const uint4*>(k_cache + base + 8 * qd + 32 * s2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t sacc[SUB / 16];
+#pragma unroll
+    for (int T = 0; T < SUB / 16; T++) {
+      sacc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s2 = 0; s2 < NDS; s2++)
+        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(&kr[T][s2]), qb[s2],
+                                                            sacc[T], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int pc = i * 64 + lane;
+      const int r = pc / PPR, c = pc % PPR;
+      *reinterpret_cast<uint4*>(Vs + r * VS + 8 * c) = r < nk ? vr[i] : make_uint4(0, 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < SUB / 16; T++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int key = 16 * T + 4 * qd + i;
+        const float sc = key < nk ? sacc[T][i] : -INFINITY;
+        sacc[T][i] = sc;
+        mx = fmaxf(mx, sc);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+    m_run = m_new;
+    float rs = 0.0f;
+#pragma unroll
+    for (int T = 0; T < SUB / 16; T++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float pe = __builtin_amdgcn_exp2f((sacc[T][i] - m_use) * c2);
+        sacc[T][i] = pe;
+        rs += pe;
+      }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int i = 0; i < NDT; i++) o[i] *= alpha;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k2 = 0; k2 < SUB / 32; k2++) {
+      bf16x8_t pb;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        pb[i] = (__bf16)sacc[2 * k2][i];
+        pb[4 + i] = (__bf16)sacc[2 * k2 + 1][i];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++) {
+        const bf16_t* vb = Vs + vtr + (32 * k2) * VS + 16 * dt;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb + 16 * VS));
+        bf16x8_t va;
+        *reinterpret_cast<s16x4_t*>(&va) = lo;
+        *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[dt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float l_h = l_run + __shfl_xor(l_run, 16, 64);
+  l_h += __shfl_xor(l_h, 32, 64);
+  __syncthreads();
+  float* mrg = reinterpret_cast<float*>(dm_smem);               // [4][16][D + 2]
+  {
+    float* mw = mrg + ((size_t)wave * 16 + n) * (D + 2);
+    if (qd == 0) {
+      mw[0] = m_run;
+      mw[1] = l_h;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mw[2 + 16 * dt + 4 * qd + i] = o[dt][i];
+  }
+  __syncthreads();
+  const size_t pstride = (size_t)G * (D + 2);
+  float* myp = part + (((size_t)b * Hkv + g) * nwg + blockIdx.x) * pstride;
+  for (int e = tid; e < G * D; e += 256) {
+    const int h = e / D, d = e % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; w++) mm = fmaxf(mm, mrg[((size_t)w * 16 + h) * (D + 2)]);
+    float ll = 0.0f, oo = 0.0f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const float* mw = mrg + ((size_t)w * 16 + h) * (D + 2);
+        if (mw[0] == -INFINITY) continue;
+        const float sc = __builtin_amdgcn_exp2f((mw[0] - mm) * c2);
+        ll += mw[1] * sc;
+        oo += mw[2 + d] * sc;
+      }
+    }
+    myp[h * (D + 2) + 2 + d] = oo;
+    if (d == 0) {
+      myp[h * (D + 2)] = mm == -INFINITY ? -INFINITY : mm * scale;
+      myp[h * (D + 2) + 1] = ll;
+    }
+  }
+}
+
+static int token_attn_ppw(const bsg_dims& d, int Kt) {
+  const long long units = (Kt + 63) / 64;
+  const long long wg2 = (long long)d.batch * d.num_kv_heads * ((units + 7) / 8);
+  return wg2 >= 512 ? 2 : 1;
+}
+
+static int token_attn_nwg(const bsg_dims& d, int Kt) {
+  const int ppw = token_attn_ppw(d, Kt);
+  const int units = (Kt + 63) / 64;
+  return (units + 4 * ppw - 1) / (4 * ppw);
+}
+
+bool token_attn_supported(const bsg_dims& d) {
+  return d.dtype == BSG_BF16 && d.num_q_heads / d.num_kv_heads <= 16;
+}
+
+size_t token_attn_workspace_bytes(const bsg_dims& d, int Kt) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  return (size_t)d.batch * d.num_kv_heads * token_attn_nwg(d, Kt) * G * (d.head_dim + 2) * sizeof(float);
+}
+
+hipError_t launch_attn_decode_tokens(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
+                                     const void* v_cache, const int32_t* page_table, const int32_t* token_idx, int Kt,
+                                     float scale, void* workspace, void* out, float* lse, hipStream_t stream) {
+  const int nwg = token_attn_nwg(d, Kt);
+  const int ppw = token_attn_ppw(d, Kt);
+  float* part = (float*)workspace;
+  const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
+  const size_t smem_m = (size_t)4 * 16 * (d.head_dim + 2) * sizeof(float);
+  const size_t smem = smem_v > smem_m ? smem_v : smem_m;
+  dim3 grid(nwg, d.num_kv_heads, d.batch);
+#define BSG_DT(DD, BB)                                                                                            \
+  do {                                                                                                             \
+    auto kfn = attn_decode_tokens_kernel<DD, BB>;                                                                  \
+    hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);  \
+    if (ea != hipSuccess) return ea;                                                                               \
+    hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache,      \
+                       (const bf16_t*)v_cache, page_table, token_idx, Kt, scale, part, d.num_q_heads,              \
+                       d.num_kv_heads, d.num_pages, d.pt_stride, nwg, ppw);                                        \
+  } while (0)
+  if (d.head_dim == 128) {
+    if (d.page_size == 64) BSG_DT(128, 64); else BSG_DT(128, 128);
+  } else {
+    if (d.page_size == 64) BSG_DT(64, 64); else BSG_DT(64, 128);
+  }
+#undef BSG_DT
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 mgrid(d.batch * d.num_q_heads);
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 128>), mgrid, dim3(128), 0, stream, part, (bf16_t*)out, lse,
+                       d.num_q_heads, d.num_kv_heads, nwg, gate_args{nullptr, 0, nullptr});
+  else
+    hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
+                       d.num_q_heads, d.num_kv_heads, nwg, gate_args{nullptr, 0, nullptr});
+  return hipGetLastError();
+}
+
 static bool decode_mfma_path(const bsg_dims& d) {
   const int G = d.num_q_heads / d.num_kv_heads;
   return d.dtype == BSG_BF16 && G <= 16;

@@ -245,4 +245,81 @@ int bsg_decode_step_fp8(const bsg_dims* dims, const void* q, const int32_t* kv_l
                                            bsg::gate_args{nullptr, 0, nullptr}, rep_scales, k_scales, v_scales));
 }
 
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t bsg_token_topk_workspace_bytes(const bsg_dims* dims, int32_t two_level) {
+  if (check_dims(dims)) return 0;
+  return bsg::token_topk_workspace_bytes(*dims, two_level != 0);
+}
+
+int bsg_token_topk(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* k_cache,
+                   const int32_t* page_table, const int32_t* block_idx, int32_t top_k_tokens, int32_t* token_idx,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->dtype != BSG_BF16) return BSG_ERR_UNSUPPORTED;
+  if (!q || !kv_lens || !k_cache || !page_table || !token_idx) return BSG_ERR_NULL;
+  if (top_k_tokens < 1) return BSG_ERR_SHAPE;
+  const size_t need = bsg::token_topk_workspace_bytes(*dims, block_idx != nullptr);
+  if (!workspace || workspace_bytes < need) return BSG_ERR_WORKSPACE;
+  return to_status(bsg::launch_token_topk(*dims, q, kv_lens, k_cache, page_table, block_idx, top_k_tokens,
+                                          token_idx, workspace, (hipStream_t)stream));
+}
+
+size_t bsg_decode_tokens_workspace_bytes(const bsg_dims* dims, int32_t top_k_tokens) {
+  if (check_dims(dims) || top_k_tokens < 1) return 0;
+  return bsg::token_attn_workspace_bytes(*dims, top_k_tokens);
+}
+
+int bsg_sparse_attn_decode_tokens(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* k_cache,
+                                  const void* v_cache, const int32_t* page_table, const int32_t* token_idx,
+                                  int32_t top_k_tokens, float scale, void* workspace, size_t workspace_bytes,
+                                  void* out, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!bsg::token_attn_supported(*dims)) return BSG_ERR_UNSUPPORTED;
+  if (!q || !kv_lens || !k_cache || !v_cache || !page_table || !token_idx || !out) return BSG_ERR_NULL;
+  if (top_k_tokens < 1) return BSG_ERR_SHAPE;
+  if (!workspace || workspace_bytes < bsg::token_attn_workspace_bytes(*dims, top_k_tokens)) return BSG_ERR_WORKSPACE;
+  return to_status(bsg::launch_attn_decode_tokens(*dims, q, kv_lens, k_cache, v_cache, page_table, token_idx,
+                                                  top_k_tokens, scale, workspace, out, lse, (hipStream_t)stream));
+}
+
+size_t bsg_decode_step_tokens_workspace_bytes(const bsg_dims* dims, int32_t top_k_tokens, int32_t two_level) {
+  if (check_dims(dims) || top_k_tokens < 1) return 0;
+  const size_t sel = two_level ? align256(bsg_group_score_topk_workspace_bytes(dims, 1)) : 0;
+  return sel + align256(bsg::token_topk_workspace_bytes(*dims, two_level != 0)) +
+         bsg::token_attn_workspace_bytes(*dims, top_k_tokens);
+}
+
+int bsg_decode_step_tokens(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* block_cache,
+                           const void* k_cache, const void* v_cache, const int32_t* page_table,
+                           int32_t top_k_tokens, int32_t two_level, float scale, int32_t* block_idx,
+                           int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                           void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->dtype != BSG_BF16 || !bsg::token_attn_supported(*dims)) return BSG_ERR_UNSUPPORTED;
+  if (!q || !kv_lens || !k_cache || !v_cache || !page_table || !token_idx || !out) return BSG_ERR_NULL;
+  if (two_level && (!block_cache || !block_idx)) return BSG_ERR_NULL;
+  if (top_k_tokens < 1) return BSG_ERR_SHAPE;
+  const size_t need = bsg_decode_step_tokens_workspace_bytes(dims, top_k_tokens, two_level);
+  if (!workspace || workspace_bytes < need) return BSG_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  size_t off = 0;
+  if (two_level) {
+    const size_t a = align256(bsg_group_score_topk_workspace_bytes(dims, 1));
+    st = bsg_group_score_topk(dims, q, 1, kv_lens, block_cache, page_table, block_idx, ws, a, stream);
+    if (st) return st;
+    off = a;
+  }
+  const size_t b = align256(bsg::token_topk_workspace_bytes(*dims, two_level != 0));
+  hipError_t e = bsg::launch_token_topk(*dims, q, kv_lens, k_cache, page_table, two_level ? block_idx : nullptr,
+                                        top_k_tokens, token_idx, ws + off, s);
+  if (e != hipSuccess) return BSG_ERR_HIP;
+  return to_status(bsg::launch_attn_decode_tokens(*dims, q, kv_lens, k_cache, v_cache, page_table, token_idx,
+                                                  top_k_tokens, scale, ws + off + b, out, lse, s));
+}
+
 }  // extern "C"

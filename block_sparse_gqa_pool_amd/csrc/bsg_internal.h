@@ -58,6 +58,17 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
                               gate_args ga = {nullptr, 0, nullptr}, const float* rep_scales = nullptr,
                               const float* k_scales = nullptr, const float* v_scales = nullptr);
 
+// Token-level / two-level selection (token_select.hip) and attention over token lists.
+size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level);
+hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
+                             const int32_t* page_table, const int32_t* block_idx, int top_k_tokens,
+                             int32_t* token_idx, void* workspace, hipStream_t stream);
+bool token_attn_supported(const bsg_dims& d);
+size_t token_attn_workspace_bytes(const bsg_dims& d, int Kt);
+hipError_t launch_attn_decode_tokens(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
+                                     const void* v_cache, const int32_t* page_table, const int32_t* token_idx, int Kt,
+                                     float scale, void* workspace, void* out, float* lse, hipStream_t stream);
+
 // fp8 (OCP E4M3) caches: per-(page, head) power-of-two scales (fp8_cache.hip)
 hipError_t launch_quantize_pages_fp8(const bsg_dims& d, const void* src, const int32_t* page_table,
                                      const int32_t* kv_lens, uint8_t* codes, float* scales, hipStream_t stream);

@@ -304,6 +304,65 @@ int bsg_decode_step_fp8(const bsg_dims* dims, const void* q, const int32_t* kv_l
                         const int32_t* page_table, float scale, int32_t* block_idx, void* workspace,
                         size_t workspace_bytes, void* out, float* lse, void* stream);
 
+/*
+ * Token-level and two-level selection for decode (q_len = 1, bf16).
+ *
+ * Token level follows "Sparse Attention + Linear Backbones", sections 5.1-5.3 and the
+ * pseudocode of 5.5: an indexer scores every earlier position, the top_k_tokens
+ * highest-scoring positions are kept per query, attention runs over those; the indexer
+ * uses no positional encoding.  The learned indexer is absent, so the index is the identity
+ * one: for the query heads of group g,
+ *     score(s) = sum over the group's heads h of q[b, h, :] . K[token s, g, :]   (fp32)
+ * over the candidates s <= kv_lens[b] - 1.  Two level follows "Sparse Attention for
+ * Long-Context LLMs", section 8 (coarse filtering, then fine filtering): the candidates are
+ * the tokens of the row's selected blocks, block_idx [B, Hkv, dims.top_k] (ascending, -1
+ * padded, as bsg_topk_blocks writes it).  The top top_k_tokens candidates are kept by
+ * (score, lower token first) and written ascending to token_idx [B, Hkv, top_k_tokens],
+ * padded with -1 when there are fewer candidates.
+ */
+
+/*
+ * bsg_token_topk -- token scores and exact top-K.  block_idx NULL: token level (every
+ * token is a candidate; this reads the whole K cache of the batch); else two level.
+ * workspace (device, no initialisation) >= bsg_token_topk_workspace_bytes(dims, two_level)
+ * bytes: the fp32 scores, B * Hkv * (pt_stride * page_size, or top_k * page_size) of them.
+ * dtype must be BSG_BF16.
+ */
+size_t bsg_token_topk_workspace_bytes(const bsg_dims* dims, int32_t two_level);
+int bsg_token_topk(const bsg_dims* dims, const void* q, const int32_t* kv_lens, const void* k_cache,
+                   const int32_t* page_table, const int32_t* block_idx, int32_t top_k_tokens,
+                   int32_t* token_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bsg_sparse_attn_decode_tokens -- exact attention over the kept tokens of token_idx
+ * [B, Hkv, top_k_tokens] (the group's list; -1 entries are skipped):
+ *     out[b, h] = sum_s softmax_s(q[b, h] . k_s * scale) v_s,  lse = log sum_s exp(...),
+ * split over workgroups with the log-sum-exp merge of bsg_sparse_attn_decode.  bf16 with
+ * G = Hq / Hkv <= 16 (else BSG_ERR_UNSUPPORTED).  workspace >=
+ * bsg_decode_tokens_workspace_bytes(dims, top_k_tokens) bytes.
+ */
+size_t bsg_decode_tokens_workspace_bytes(const bsg_dims* dims, int32_t top_k_tokens);
+int bsg_sparse_attn_decode_tokens(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
+                                  const void* k_cache, const void* v_cache, const int32_t* page_table,
+                                  const int32_t* token_idx, int32_t top_k_tokens, float scale,
+                                  void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                  void* stream);
+
+/*
+ * bsg_decode_step_tokens -- a whole token-level (two_level = 0) or two-level (two_level = 1)
+ * decode step: [block scores + block top-k into block_idx, as bsg_group_score_topk with
+ * q_len = 1,] token top-K into token_idx, attention into out / lse.  block_cache and
+ * block_idx are used (and required) for two_level only.  workspace >=
+ * bsg_decode_step_tokens_workspace_bytes(dims, top_k_tokens, two_level) bytes.
+ */
+size_t bsg_decode_step_tokens_workspace_bytes(const bsg_dims* dims, int32_t top_k_tokens,
+                                              int32_t two_level);
+int bsg_decode_step_tokens(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
+                           const void* block_cache, const void* k_cache, const void* v_cache,
+                           const int32_t* page_table, int32_t top_k_tokens, int32_t two_level,
+                           float scale, int32_t* block_idx, int32_t* token_idx, void* workspace,
+                           size_t workspace_bytes, void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

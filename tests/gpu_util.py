@@ -125,3 +125,29 @@ def mini_pool(w, seqs: Sequence[int]):
     q = to_np(w.q[list(seqs)])
     kv = [w.kv_lens_host[b] for b in seqs]
     return q, kp, vp, ptm, kv
+
+
+def compare_token_selection(gpu_idx: np.ndarray, ora_idx: np.ndarray, scores64: np.ndarray, top_k: int):
+    """Token selection parity with the tie exemption (as compare_selection, for token lists).
+
+    gpu_idx, ora_idx: [B, Hkv, T, K] ascending, -1 padded; scores64: oracle float64 scores
+    [B, Hkv, T, L] (-inf for non-candidates).  A differing row is exempt only if the
+    oracle's K-th and (K+1)-th candidates score within TIE_REL of each other and every token
+    in the difference scores within that window of the boundary.  Returns (bad, exempt)."""
+    bad, exempt = [], []
+    diff = np.nonzero((gpu_idx != ora_idx).any(-1))
+    for b, g, t in zip(*diff):
+        row = scores64[b, g, t]
+        gi = [int(x) for x in gpu_idx[b, g, t] if x >= 0]
+        oi = [int(x) for x in ora_idx[b, g, t] if x >= 0]
+        cand = np.nonzero(np.isfinite(row))[0]
+        ok = (len(gi) == len(oi) and gi == sorted(gi) and len(set(gi)) == len(gi)
+              and all(np.isfinite(row[j]) for j in gi) and len(cand) > top_k)
+        if ok:
+            order = cand[np.lexsort((cand, -row[cand].astype(np.float32)))]
+            sa, sb = row[order[top_k - 1]], row[order[top_k]]
+            win = TIE_REL * max(abs(sa), abs(sb))
+            ok = abs(sa - sb) <= win and all(abs(row[j] - sa) <= win or abs(row[j] - sb) <= win
+                                             for j in set(gi) ^ set(oi))
+        (exempt if ok else bad).append((int(b), int(g), int(t)))
+    return bad, exempt

@@ -158,3 +158,29 @@ def test_validation_of_fp8_calls(L):
     # outside the matrix-core decode path (G > 16): unsupported
     dg = ctypes.byref(_dims(num_q_heads=34, num_kv_heads=2))
     assert step(dg, 1 << 30) == -3
+
+
+def test_validation_of_token_calls(L):
+    """Token-level calls reject f32 dims, NULL pointers, K < 1 and short workspaces before any
+    launch (dummy pointers only)."""
+    s = None
+    d = ctypes.byref(_dims())
+    df = ctypes.byref(_dims(dtype=_lib.BSG_F32))
+    need = L.bsg_token_topk_workspace_bytes(d, 0)
+    assert need == 2 * 2 * 32 * 64 * 4 and L.bsg_token_topk_workspace_bytes(d, 1) == 2 * 2 * 8 * 64 * 4
+    assert L.bsg_token_topk(df, BAD, BAD, BAD, BAD, None, 16, BAD, BAD, need, s) == -3
+    assert L.bsg_token_topk(d, None, BAD, BAD, BAD, None, 16, BAD, BAD, need, s) == -1
+    assert L.bsg_token_topk(d, BAD, BAD, BAD, BAD, None, 0, BAD, BAD, need, s) == -2
+    assert L.bsg_token_topk(d, BAD, BAD, BAD, BAD, None, 16, BAD, BAD, need - 1, s) == -4
+    na = L.bsg_decode_tokens_workspace_bytes(d, 2048)
+    assert na > 0
+    attn = lambda dd, ws, tok=BAD: L.bsg_sparse_attn_decode_tokens(dd, BAD, BAD, BAD, BAD, BAD, tok, 2048, 0.1, BAD,
+                                                                   ws, BAD, None, s)
+    assert attn(df, na) == -3 and attn(d, na, None) == -1 and attn(d, na - 1) == -4
+    dg = ctypes.byref(_dims(num_q_heads=34, num_kv_heads=2))
+    assert attn(dg, 1 << 30) == -3
+    ns = L.bsg_decode_step_tokens_workspace_bytes(d, 64, 1)
+    assert ns > 0 and L.bsg_decode_step_tokens_workspace_bytes(d, 64, 0) > 0
+    step = lambda two, ws, bc=BAD: L.bsg_decode_step_tokens(d, BAD, BAD, bc, BAD, BAD, BAD, 64, two, 0.1, BAD, BAD,
+                                                            BAD, ws, BAD, None, s)
+    assert step(1, ns, None) == -1 and step(1, ns - 1) == -4
