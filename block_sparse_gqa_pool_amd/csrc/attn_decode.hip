@@ -10,6 +10,7 @@
 // The work is HBM-bound: each selected (page, head) K and V tile is read exactly once.
 #include "bsg_device.h"
 #include "bsg_internal.h"
+#include "decode_prologue.h"
 
 namespace bsg {
 
@@ -192,91 +193,6 @@ constexpr int DM_VPAD = 16;
 }
 
 typedef __attribute__((address_space(3))) s16x4_t* dm_lds_s16x4_ptr;
-
-// Selection prologue of the fused decode step (one workgroup, all threads).  `lists` holds,
-// per chunk of candidate blocks, the chunk's best m = top_k - 1 keys sorted descending (0 =
-// none).  The cnt-th largest of the chunks' first T keys is a lower bound `tau` of the
-// cnt-th largest key overall (at least cnt keys reach it), so the kept keys are among the
-// list keys >= tau -- typically little more than cnt of them.  Those survivors are ranked
-// against each other; ranks below cnt are kept.  wl receives the kept block ids ascending.
-// Number of keys in a[0, n) that are larger than key; a is 16-byte aligned and read two
-// keys per 16-byte load, 16 keys per batch.
-__device__ __forceinline__ int count_above(const uint64_t* a, int n, uint64_t key) {
-  int rank = 0, i = 0;
-  for (; i + 16 <= n; i += 16) {
-    ulonglong2 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; u++) v[u] = reinterpret_cast<const ulonglong2*>(a + i)[u];
-#pragma unroll
-    for (int u = 0; u < 8; u++) rank += (v[u].x > key ? 1 : 0) + (v[u].y > key ? 1 : 0);
-  }
-  for (; i < n; i++) rank += a[i] > key ? 1 : 0;
-  return rank;
-}
-
-// Selection prologue of the fused decode step (one workgroup, all threads).  `lists` holds,
-// per chunk of candidate blocks, the chunk's best m = top_k - 1 keys sorted descending (0 =
-// none).  The cnt-th largest of the chunks' first T keys is a lower bound `tau` of the
-// cnt-th largest key overall (at least cnt keys reach it), so the kept keys are among the
-// list keys >= tau -- a prefix of every list, typically little more than cnt keys in all.
-// Those survivors are ranked against each other; sel[r] receives the block id of rank r
-// (r < cnt, largest score first).
-__device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, int nchunks, int m, int lt, int cnt,
-                                       uint64_t* L, uint64_t* S, int* sel, int* counter, uint64_t* tau_s) {
-  const int tid = threadIdx.x;
-  const int T = 1 << lt;                      // leading keys taken from every chunk list
-  const int NT = nchunks << lt;
-  const int NL = nchunks * m;
-  uint64_t* tops = S;                         // [NT], reused for the survivors afterwards
-  if (tid == 0) {
-    *counter = 0;
-    *tau_s = 1ull;
-  }
-  for (int e0 = 0; e0 < NL; e0 += 4 * 256) {  // lists -> LDS, 4 loads in flight per thread
-    uint64_t v[4];
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int e = e0 + u * 256 + tid;
-      v[u] = e < NL ? lists_row[e] : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int e = e0 + u * 256 + tid;
-      if (e < NL) L[e] = v[u];
-    }
-  }
-  __syncthreads();
-  int nvalid = 0;
-  for (int e0 = 0; e0 < NT; e0 += 256) {
-    const int e = e0 + tid;
-    const int i = e & (T - 1);                // position in the chunk's list (T may exceed m)
-    const uint64_t key = (e < NT && i < m) ? L[(e >> lt) * m + i] : 0ull;
-    if (e < NT) tops[e] = key;
-    nvalid += __syncthreads_count(key != 0ull);
-  }
-  if (nvalid >= cnt) {
-    for (int e = tid; e < NT; e += 256) {
-      const uint64_t key = tops[e];
-      if (key != 0ull && count_above(tops, NT, key) == cnt - 1) *tau_s = key;
-    }
-  }
-  __syncthreads();
-  const uint64_t tau = *tau_s;
-  for (int c = tid; c < nchunks; c += 256) {   // this chunk's keys >= tau, appended as one run
-    int nc = 0;
-    while (nc < m && L[c * m + nc] >= tau) nc++;
-    const int at = nc > 0 ? atomicAdd(counter, nc) : 0;
-    for (int i = 0; i < nc; i++) S[at + i] = L[c * m + i];
-  }
-  __syncthreads();
-  const int ns = *counter;
-  for (int e = tid; e < ns; e += 256) {
-    const uint64_t key = S[e];
-    const int rank = count_above(S, ns, key);
-    if (rank < cnt) sel[rank] = sel_key_index(key);
-  }
-  __syncthreads();
-}
 
 // F8: K and V are OCP E4M3 codes with one scale per (page, head).  Codes become bf16
 // exactly; the K scale multiplies the page's scores and the V scale the page's
@@ -937,13 +853,10 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
 static size_t decode_step_smem(const bsg_dims& d, int* lt_out) {
   const int nchunks = decode_select_nchunks(d);
   const int m = d.top_k - 1;
-  int lt = 0;                                   // tops: 2^lt leading keys of every list, >= 2 m of them
-  while (m > 0 && (nchunks << lt) < 2 * m && (1 << lt) < m) lt++;
+  const int lt = decode_prologue_lt(nchunks, m);
   const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
   const size_t smem_m = (size_t)4 * 16 * (d.head_dim + 2) * sizeof(float);
-  const size_t nl = (size_t)nchunks * (m > 0 ? m : 1);
-  const size_t nt = (size_t)nchunks << lt;
-  const size_t smem_s = (((nl + 1) & ~(size_t)1) + (nl > nt ? nl : nt)) * sizeof(uint64_t);   // S 16-byte aligned
+  const size_t smem_s = decode_prologue_smem_bytes(nchunks, m, lt);
   size_t smem = smem_v > smem_m ? smem_v : smem_m;
   if (lt_out) *lt_out = lt;
   return smem > smem_s ? smem : smem_s;

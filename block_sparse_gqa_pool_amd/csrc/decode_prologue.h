@@ -1,0 +1,104 @@
+// Exact top-(k-1) selection from per-chunk sorted key lists (decode), shared by the fused
+// decode step (inside the attention kernel) and the stand-alone decode selection kernel.
+#pragma once
+
+#include "bsg_device.h"
+
+namespace bsg {
+
+// Number of keys in a[0, n) that are larger than key; a is 16-byte aligned and read two
+// keys per 16-byte load, 16 keys per batch.
+__device__ __forceinline__ int count_above(const uint64_t* a, int n, uint64_t key) {
+  int rank = 0, i = 0;
+  for (; i + 16 <= n; i += 16) {
+    ulonglong2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) v[u] = reinterpret_cast<const ulonglong2*>(a + i)[u];
+#pragma unroll
+    for (int u = 0; u < 8; u++) rank += (v[u].x > key ? 1 : 0) + (v[u].y > key ? 1 : 0);
+  }
+  for (; i < n; i++) rank += a[i] > key ? 1 : 0;
+  return rank;
+}
+
+// Selection prologue of the fused decode step (one workgroup, all threads).  `lists` holds,
+// per chunk of candidate blocks, the chunk's best m = top_k - 1 keys sorted descending (0 =
+// none).  The cnt-th largest of the chunks' first T keys is a lower bound `tau` of the
+// cnt-th largest key overall (at least cnt keys reach it), so the kept keys are among the
+// list keys >= tau -- a prefix of every list, typically little more than cnt keys in all.
+// Those survivors are ranked against each other; sel[r] receives the block id of rank r
+// (r < cnt, largest score first).
+__device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, int nchunks, int m, int lt, int cnt,
+                                       uint64_t* L, uint64_t* S, int* sel, int* counter, uint64_t* tau_s) {
+  const int tid = threadIdx.x;
+  const int T = 1 << lt;                      // leading keys taken from every chunk list
+  const int NT = nchunks << lt;
+  const int NL = nchunks * m;
+  uint64_t* tops = S;                         // [NT], reused for the survivors afterwards
+  if (tid == 0) {
+    *counter = 0;
+    *tau_s = 1ull;
+  }
+  for (int e0 = 0; e0 < NL; e0 += 4 * 256) {  // lists -> LDS, 4 loads in flight per thread
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = e0 + u * 256 + tid;
+      v[u] = e < NL ? lists_row[e] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = e0 + u * 256 + tid;
+      if (e < NL) L[e] = v[u];
+    }
+  }
+  __syncthreads();
+  int nvalid = 0;
+  for (int e0 = 0; e0 < NT; e0 += 256) {
+    const int e = e0 + tid;
+    const int i = e & (T - 1);                // position in the chunk's list (T may exceed m)
+    const uint64_t key = (e < NT && i < m) ? L[(e >> lt) * m + i] : 0ull;
+    if (e < NT) tops[e] = key;
+    nvalid += __syncthreads_count(key != 0ull);
+  }
+  if (nvalid >= cnt) {
+    for (int e = tid; e < NT; e += 256) {
+      const uint64_t key = tops[e];
+      if (key != 0ull && count_above(tops, NT, key) == cnt - 1) *tau_s = key;
+    }
+  }
+  __syncthreads();
+  const uint64_t tau = *tau_s;
+  for (int c = tid; c < nchunks; c += 256) {   // this chunk's keys >= tau, appended as one run
+    int nc = 0;
+    while (nc < m && L[c * m + nc] >= tau) nc++;
+    const int at = nc > 0 ? atomicAdd(counter, nc) : 0;
+    for (int i = 0; i < nc; i++) S[at + i] = L[c * m + i];
+  }
+  __syncthreads();
+  const int ns = *counter;
+  for (int e = tid; e < ns; e += 256) {
+    const uint64_t key = S[e];
+    const int rank = count_above(S, ns, key);
+    if (rank < cnt) sel[rank] = sel_key_index(key);
+  }
+  __syncthreads();
+}
+
+
+// Leading keys (2^lt) the prologue takes from every chunk list: chunks * 2^lt >= 2 (k - 1),
+// and no more than the list length.
+inline int decode_prologue_lt(int nchunks, int m) {
+  int lt = 0;
+  while (m > 0 && (nchunks << lt) < 2 * m && (1 << lt) < m) lt++;
+  return lt;
+}
+
+// LDS of the prologue: the lists, then the tops / survivors (16-byte aligned).
+inline size_t decode_prologue_smem_bytes(int nchunks, int m, int lt) {
+  const size_t nl = (size_t)nchunks * (m > 0 ? m : 1);
+  const size_t nt = (size_t)nchunks << lt;
+  return (((nl + 1) & ~(size_t)1) + (nl > nt ? nl : nt)) * sizeof(uint64_t);
+}
+
+}  // namespace bsg

@@ -14,11 +14,13 @@
 //     (no page-table round trip between them).  Then one wave per group ranks the chunk's
 //     64 keys (score, lower-index-first; rank = number of larger keys) and writes its best
 //     top_k - 1 keys, sorted descending.
-//  B. decode_select_kernel, one workgroup per (sequence, group): exact selection from the
-//     sorted chunk lists by pruning and ranking (see the kernel), then the kept ids are
-//     written ascending, the own block appended and the row padded with -1.
+//  B. decode_select_kernel, one workgroup per (sequence, group): the exact selection of the
+//     fused decode step's prologue (decode_prologue.h: a lower bound from the lists' leading
+//     keys, the survivors above it, their ranks), then the kept ids are written ascending,
+//     the own block appended and the row padded with -1.
 #include "bsg_device.h"
 #include "bsg_internal.h"
+#include "decode_prologue.h"
 
 namespace bsg {
 
@@ -166,54 +168,22 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
 __global__ __launch_bounds__(256) void decode_select_kernel(const uint64_t* __restrict__ lists,
                                                             const int32_t* __restrict__ kv_lens,
                                                             int32_t* __restrict__ block_idx, int Hkv, int bs,
-                                                            int top_k, int nchunks, int pt_stride) {
-  extern __shared__ uint64_t dsel_smem[];   // [nchunks][m] keys, then [nchunks] prefix lengths
+                                                            int top_k, int nchunks, int pt_stride, int lt) {
+  extern __shared__ __attribute__((aligned(16))) uint64_t dsel_smem[];
   __shared__ int kept[64];
+  __shared__ int counter_s;
   __shared__ uint64_t tau_s;
   const int row = blockIdx.x;
   const int b = row / Hkv;
   const int tid = threadIdx.x;
   const int m = top_k - 1;
   const int own = max(kv_lens[b] - 1, 0) / bs;
-  const int ncand = min(own, pt_stride);
-  const int cnt = min(m, ncand);
+  const int cnt = min(m, min(own, pt_stride));
   int32_t* out = block_idx + (size_t)row * top_k;
   if (cnt > 0) {
-    uint64_t* L = dsel_smem;
-    int* plen = reinterpret_cast<int*>(dsel_smem + (size_t)nchunks * m);
-    const uint64_t* src = lists + (size_t)row * nchunks * m;
-    for (int e = tid; e < nchunks * m; e += 256) L[e] = src[e];
-    if (tid == 0) tau_s = 0ull;
-    __syncthreads();
-    for (int c = tid; c < nchunks; c += 256) atomicMax((unsigned long long*)&tau_s, (unsigned long long)L[c * m + m - 1]);
-    __syncthreads();
-    const uint64_t tau = tau_s > 0ull ? tau_s : 1ull;       // keys are >= 1 when valid
-    for (int c = tid; c < nchunks; c += 256) {              // prefix of keys >= tau
-      int lo = 0, hi = m;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (L[c * m + mid] >= tau) lo = mid + 1; else hi = mid;
-      }
-      plen[c] = lo;
-    }
-    __syncthreads();
-    for (int e = tid; e < nchunks * m; e += 256) {
-      const int c = e / m, pidx = e % m;
-      if (pidx >= plen[c]) continue;
-      const uint64_t key = L[e];
-      int rank = 0;
-      for (int c2 = 0; c2 < nchunks && rank < cnt; c2++) {  // keys above `key` in list c2
-        int lo = 0, hi = plen[c2];
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (L[c2 * m + mid] > key) lo = mid + 1; else hi = mid;
-        }
-        rank += lo;
-      }
-      if (rank < cnt) kept[rank] = sel_key_index(key);
-    }
-    __syncthreads();
-    if (tid < cnt) {
+    decode_select_prologue(lists + (size_t)row * nchunks * m, nchunks, m, lt, cnt, dsel_smem,
+                           dsel_smem + (((size_t)nchunks * m + 1) & ~(size_t)1), kept, &counter_s, &tau_s);
+    if (tid < cnt) {                                         // ascending
       const int ji = kept[tid];
       int r2 = 0;
       for (int i = 0; i < cnt; i++) r2 += kept[i] < ji ? 1 : 0;
@@ -233,7 +203,9 @@ size_t decode_select_workspace_bytes(const bsg_dims& d) {
 
 bool decode_select_supported(const bsg_dims& d, int q_len) {
   const int nchunks = decode_select_nchunks(d);
-  return q_len == 1 && d.dtype == BSG_BF16 && (size_t)nchunks * (d.top_k - 1) * 8 + nchunks * 4 <= 120 * 1024;
+  const int m = d.top_k - 1;
+  return q_len == 1 && d.dtype == BSG_BF16 &&
+         decode_prologue_smem_bytes(nchunks, m, decode_prologue_lt(nchunks, m)) <= 150 * 1024;
 }
 
 hipError_t launch_decode_score_chunks(const bsg_dims& d, const void* q, const int32_t* kv_lens,
@@ -268,14 +240,15 @@ hipError_t launch_decode_select(const bsg_dims& d, const void* q, const int32_t*
   uint64_t* lists = (uint64_t*)workspace;
   hipError_t e = launch_decode_score_chunks(d, q, kv_lens, block_cache, page_table, lists, stream);
   if (e != hipSuccess) return e;
-  const size_t smem2 = (size_t)nchunks * (m > 0 ? m : 1) * sizeof(uint64_t) + (size_t)nchunks * sizeof(int);
+  const int lt = decode_prologue_lt(nchunks, m);
+  const size_t smem2 = decode_prologue_smem_bytes(nchunks, m, lt);
   if (smem2 > 64 * 1024) {
     hipError_t ea = hipFuncSetAttribute((const void*)decode_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                         (int)smem2);
     if (ea != hipSuccess) return ea;
   }
   hipLaunchKernelGGL(decode_select_kernel, dim3(d.batch * d.num_kv_heads), dim3(256), smem2, stream, lists, kv_lens,
-                     block_idx, d.num_kv_heads, d.page_size, d.top_k, nchunks, d.pt_stride);
+                     block_idx, d.num_kv_heads, d.page_size, d.top_k, nchunks, d.pt_stride, lt);
   return hipGetLastError();
 }
 

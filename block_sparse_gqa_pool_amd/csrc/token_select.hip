@@ -7,16 +7,19 @@
 // granularity one.  Two level ("Sparse Attention for Long-Context LLMs", section 8: coarse
 // then fine filtering): the candidates are the tokens of the row's selected blocks.
 //
-//  * token_score_kernel: one workgroup per (64 candidates, group, sequence).  The group-summed
-//    query is built in LDS; the 64 key rows (one page, D bf16 each) are read with 16-byte
-//    loads, SEG = D/8 lanes per row, and reduced with DPP moves.  Candidates past the query's
+//  * token_score_kernel: one workgroup per (64 candidates, 4 groups, sequence).  The
+//    group-summed queries are built in LDS; each group's 64 key rows (one page, D bf16 each)
+//    are read with 16-byte loads, SEG = D/8 lanes per row, all loads of the workgroup in
+//    flight together, and reduced with DPP moves.  Candidates past the query's
 //    position (or in an unused block slot) get -inf.  HBM-bound: at token level it reads the
 //    whole K cache of the sequence once (the pages' caveat: sparse attention cuts compute,
 //    not necessarily memory traffic).
 //  * token_topk_kernel: one workgroup of 1024 threads per (sequence, group) selects the top K
 //    of the row's candidates exactly, by (score, lower index first).  A three-level radix
-//    select on the 32-bit order key (11 + 11 + 10 bits, LDS histograms, equal bins merged
-//    within a wave before the LDS atomic) finds the K-th key tau; a compaction pass in index
+//    select on the 32-bit order key (11 + 11 + 10 bits; LDS histograms: the first level, where
+//    every candidate falls into a few crowded bins, in 16 copies picked by lane; the later
+//    levels, with few keys under the chosen prefix, merge equal bins within a wave before the
+//    LDS atomic) finds the K-th key tau; a compaction pass in index
 //    order keeps every key above tau and the first K - #above keys equal to tau, and writes
 //    the kept tokens ascending (-1 padded).
 #include "bsg_device.h"
@@ -26,9 +29,12 @@ namespace bsg {
 
 namespace {
 constexpr int TS_CH = 64;      // candidates per score workgroup
+constexpr int TS_HPW = 4;      // KV heads per score workgroup
 constexpr int TK_NT = 1024;    // threads of the selection workgroup
 constexpr int TK_NW = TK_NT / 64;
 constexpr int TK_BINS = 2048;  // radix bins per level (11 bits)
+constexpr int TK_UNR = 8;      // row tiles (4 scores per thread each) loaded per batch
+constexpr int TK_COPIES = 16;  // level-1 histogram copies (lane % 16): few lanes meet on one entry
 }  // namespace
 
 // Token of candidate c of row (b, g): two level, slot c % BS of block block_idx[c / BS];
@@ -50,37 +56,59 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     float* __restrict__ scores, int nc, int Hq, int Hkv, int num_pages, int pt_stride) {
   static_assert(BS % TS_CH == 0, "a chunk lies in one page");
   constexpr int SEG = D / 8;                       // lanes per key row
-  constexpr int NP = TS_CH * SEG / 256;            // 16-byte pieces per thread
-  __shared__ float qs[D];
-  const int c0 = blockIdx.x * TS_CH, g = blockIdx.y, b = blockIdx.z;
+  constexpr int PPH = TS_CH * SEG;                 // 16-byte pieces per head
+  constexpr int NP = TS_HPW * PPH / 256;           // pieces per thread
+  __shared__ float qs[TS_HPW][D];
+  const int c0 = blockIdx.x * TS_CH, g0 = blockIdx.y * TS_HPW, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int G = Hq / Hkv;
   const int pos = kv_lens[b] - 1;
-  const int32_t* brow = TWO ? block_idx + ((size_t)b * Hkv + g) * kblk : nullptr;
-  const int tok0 = cand_token<BS, TWO>(c0, brow);  // a chunk is 64 consecutive tokens of one block
-  const int j = tok0 >= 0 ? tok0 / BS : -1;
-  const bool live = j >= 0 && j < pt_stride && tok0 <= pos;
-  const int p = live ? clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1) : 0;
-  const bf16_t* rows = k_cache + (((size_t)p * Hkv + g) * BS + (live ? tok0 % BS : 0)) * D;
+  // per head of this workgroup: the chunk's first token and key rows (a chunk is 64
+  // consecutive tokens of one block; at token level the same block for every head)
+  int tok0[TS_HPW];
+  const bf16_t* rows[TS_HPW];
+#pragma unroll
+  for (int hh = 0; hh < TS_HPW; hh++) {
+    const int g = g0 + hh;
+    const int32_t* brow = TWO ? block_idx + ((size_t)b * Hkv + min(g, Hkv - 1)) * kblk : nullptr;
+    const int t0 = g < Hkv ? cand_token<BS, TWO>(c0, brow) : -1;
+    const int j = t0 >= 0 ? t0 / BS : -1;
+    const bool live = j >= 0 && j < pt_stride && t0 <= pos;
+    const int p = live ? clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1) : 0;
+    tok0[hh] = live ? t0 : -1;
+    rows[hh] = k_cache + (((size_t)p * Hkv + (live ? g : 0)) * BS + (live ? t0 % BS : 0)) * D;
+  }
   uint4 raw[NP];
 #pragma unroll
   for (int u = 0; u < NP; u++) {
     const int pi = u * 256 + tid;
-    raw[u] = live ? *reinterpret_cast<const uint4*>(rows + (size_t)pi * 8) : make_uint4(0, 0, 0, 0);
+    const int hh = pi / PPH;
+    raw[u] = tok0[hh] >= 0 ? *reinterpret_cast<const uint4*>(rows[hh] + (size_t)(pi % PPH) * 8)
+                           : make_uint4(0, 0, 0, 0);
   }
-  // group-summed query (fp32, heads in order)
-  for (int d = tid; d < D; d += 256) {
-    float s = 0.0f;
-    for (int h = 0; h < G; h++) s += bf16_to_f32(q[((size_t)b * Hq + g * G + h) * D + d]);
-    qs[d] = s;
+  // group-summed queries (fp32, heads in order), 8 dims per thread from 16-byte loads
+  if (tid < TS_HPW * (D / 8)) {
+    const int hh = tid / (D / 8), d0 = 8 * (tid % (D / 8)), g = g0 + hh;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (g < Hkv)
+      for (int h = 0; h < G; h++) {
+        const uint4 v = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + g * G + h) * D + d0);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          acc[2 * i] += __uint_as_float(wd[i] << 16);
+          acc[2 * i + 1] += __uint_as_float(wd[i] & 0xffff0000u);
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < 8; i++) qs[hh][d0 + i] = acc[i];
   }
   __syncthreads();
-  float* srow = scores + ((size_t)b * Hkv + g) * nc + c0;
 #pragma unroll
   for (int u = 0; u < NP; u++) {
     const int pi = u * 256 + tid;
-    const int r = pi / SEG, w = pi % SEG;
-    const float* qv = qs + w * 8;
+    const int hh = pi / PPH, r = (pi % PPH) / SEG, w = pi % SEG;
+    const float* qv = &qs[hh][w * 8];
     const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
     float s = 0.0f;
 #pragma unroll
@@ -89,7 +117,9 @@ __global__ __launch_bounds__(256) void token_score_kernel(
       s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
     }
     s = seg_sum_dpp<SEG>(s);
-    if ((lane % SEG) == 0) srow[r] = (live && tok0 + r <= pos) ? s : -INFINITY;
+    const int g = g0 + hh;
+    if ((lane % SEG) == 0 && g < Hkv)
+      scores[((size_t)b * Hkv + g) * nc + c0 + r] = (tok0[hh] >= 0 && tok0[hh] + r <= pos) ? s : -INFINITY;
   }
 }
 
@@ -138,6 +168,7 @@ template <int BS, bool TWO>
 __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restrict__ scores, int nc, int K,
                                                           const int32_t* __restrict__ block_idx, int kblk,
                                                           int32_t* __restrict__ token_idx, int Hkv) {
+  extern __shared__ uint32_t hcopy[];              // level 1: TK_BINS bins x TK_COPIES copies
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t red[TK_NW + 1];
   __shared__ uint32_t sel_s[3];                    // digit, count above the digit, count in it
@@ -146,6 +177,15 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
   const float* row = scores + ((size_t)b * Hkv + g) * nc;
   const int32_t* brow = TWO ? block_idx + ((size_t)b * Hkv + g) * kblk : nullptr;
   int32_t* orow = token_idx + ((size_t)b * Hkv + g) * K;
+  // TK_UNR tiles of the row from cb on, 4 scores per thread per tile, all loads in flight
+  // together (-inf past the row; nc is a multiple of 64)
+  auto load_batch = [&](int cb, float4* v) {
+#pragma unroll
+    for (int u = 0; u < TK_UNR; u++) {
+      const int c = cb + u * 4 * TK_NT + 4 * tid;
+      v[u] = c < nc ? *reinterpret_cast<const float4*>(row + c) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+  };
   // ---- radix select of the K-th largest key (levels of 11, 11 and 10 bits)
   uint32_t prefix = 0, pmask = 0;
   uint32_t above = 0, m_eq = 0;
@@ -153,22 +193,52 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
   for (int lv = 0; lv < 3; lv++) {
     const int shift = lv == 0 ? 21 : (lv == 1 ? 10 : 0);
     const int nbits = lv == 2 ? 10 : 11;
-    for (int i = tid; i < TK_BINS; i += TK_NT) hist[i] = 0u;
-    __syncthreads();
     const uint32_t dmask = (1u << nbits) - 1u;
-    for (int c0 = 0; c0 < nc; c0 += 4 * TK_NT) {
-      const int c = c0 + 4 * tid;
-      float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (c < nc) v = *reinterpret_cast<const float4*>(row + c);   // nc is a multiple of 64
-      const float vv[4] = {v.x, v.y, v.z, v.w};
+    if (lv == 0) {
+      // every candidate takes part: spread the (few, crowded) top-digit bins over copies
+      for (int i = tid; i < TK_BINS * TK_COPIES; i += TK_NT) hcopy[i] = 0u;
+      __syncthreads();
+      const uint32_t cp = threadIdx.x & (TK_COPIES - 1);
+      for (int cb = 0; cb < nc; cb += TK_UNR * 4 * TK_NT) {
+        float4 v[TK_UNR];
+        load_batch(cb, v);
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const uint32_t key = tk_key(vv[e]);
-        const bool act = (key & pmask) == prefix && (lv > 0 || key != 0u);
-        tk_hist_add(hist, (int)((key >> shift) & dmask), act);
+        for (int u = 0; u < TK_UNR; u++) {
+          const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const uint32_t key = tk_key(vv[e]);
+            if (key != 0u) atomicAdd(&hcopy[((key >> shift) & dmask) * TK_COPIES + cp], 1u);
+          }
+        }
       }
+      __syncthreads();
+      for (int i = tid; i < TK_BINS; i += TK_NT) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int k = 0; k < TK_COPIES; k++) t += hcopy[i * TK_COPIES + k];
+        hist[i] = t;
+      }
+      __syncthreads();
+    } else {
+      // only the keys under the chosen prefix take part: few, and spread over the bins
+      for (int i = tid; i < TK_BINS; i += TK_NT) hist[i] = 0u;
+      __syncthreads();
+      for (int cb = 0; cb < nc; cb += TK_UNR * 4 * TK_NT) {
+        float4 v[TK_UNR];
+        load_batch(cb, v);
+#pragma unroll
+        for (int u = 0; u < TK_UNR; u++) {
+          const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const uint32_t key = tk_key(vv[e]);
+            tk_hist_add(hist, (int)((key >> shift) & dmask), (key & pmask) == prefix);
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // digit holding the (K - above)-th largest remaining key: suffix sums from the top bin
     const uint32_t need = (uint32_t)K - above;
     const int nb = 1 << nbits;
@@ -204,37 +274,41 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
   const uint32_t take_eq = all ? 0u : (uint32_t)K - above;
   const bool rank_eq = !all && take_eq < m_eq;     // ties at tau split by index
   uint32_t out_base = 0, eq_base = 0;
-  for (int c0 = 0; c0 < nc; c0 += 4 * TK_NT) {
-    const int c = c0 + 4 * tid;
-    float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (c < nc) v = *reinterpret_cast<const float4*>(row + c);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-    uint32_t key[4];
-    uint32_t n_eq = 0;
+  for (int cb = 0; cb < nc; cb += TK_UNR * 4 * TK_NT) {
+    float4 vb[TK_UNR];
+    load_batch(cb, vb);
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-      key[e] = tk_key(vv[e]);
-      n_eq += (!all && key[e] == tau) ? 1u : 0u;
+    for (int u = 0; u < TK_UNR; u++) {
+      const int c = cb + u * 4 * TK_NT + 4 * tid;
+      if (cb + u * 4 * TK_NT >= nc) break;
+      const float vv[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+      uint32_t key[4];
+      uint32_t n_eq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        key[e] = tk_key(vv[e]);
+        n_eq += (!all && key[e] == tau) ? 1u : 0u;
+      }
+      uint32_t eq_off = 0, eq_tot = 0;
+      if (rank_eq) eq_off = tk_scan(n_eq, red, &eq_tot);
+      bool keep[4];
+      uint32_t n_keep = 0, r = eq_base + eq_off;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const bool gt = all ? key[e] >= tau : key[e] > tau;
+        const bool eq = !all && key[e] == tau;
+        keep[e] = gt || (eq && (!rank_eq || r < take_eq));
+        r += eq ? 1u : 0u;
+        n_keep += keep[e] ? 1u : 0u;
+      }
+      uint32_t ktot;
+      uint32_t o = out_base + tk_scan(n_keep, red, &ktot);
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        if (keep[e] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c + e, brow);
+      out_base += ktot;
+      eq_base += eq_tot;
     }
-    uint32_t eq_off = 0, eq_tot = 0;
-    if (rank_eq) eq_off = tk_scan(n_eq, red, &eq_tot);
-    bool keep[4];
-    uint32_t n_keep = 0, r = eq_base + eq_off;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const bool gt = all ? key[e] >= tau : key[e] > tau;
-      const bool eq = !all && key[e] == tau;
-      keep[e] = gt || (eq && (!rank_eq || r < take_eq));
-      r += eq ? 1u : 0u;
-      n_keep += keep[e] ? 1u : 0u;
-    }
-    uint32_t ktot;
-    uint32_t o = out_base + tk_scan(n_keep, red, &ktot);
-#pragma unroll
-    for (int e = 0; e < 4; e++)
-      if (keep[e] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c + e, brow);
-    out_base += ktot;
-    eq_base += eq_tot;
   }
   for (int i = (int)out_base + tid; i < K; i += TK_NT) orow[i] = -1;
 }
@@ -250,7 +324,7 @@ hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv
   const bool two = block_idx != nullptr;
   const int nc = two ? d.top_k * d.page_size : d.pt_stride * d.page_size;
   float* scores = (float*)workspace;
-  dim3 g1(nc / TS_CH, d.num_kv_heads, d.batch);
+  dim3 g1(nc / TS_CH, (d.num_kv_heads + TS_HPW - 1) / TS_HPW, d.batch);
 #define BSG_TS(DD, BB, TW)                                                                                     \
   hipLaunchKernelGGL((token_score_kernel<DD, BB, TW>), g1, dim3(256), 0, stream, (const bf16_t*)q, kv_lens,     \
                      (const bf16_t*)k_cache, page_table, block_idx, d.top_k, scores, nc, d.num_q_heads,         \
@@ -270,9 +344,15 @@ hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(d.num_kv_heads, d.batch);
+  const size_t smem = (size_t)TK_BINS * TK_COPIES * sizeof(uint32_t);
 #define BSG_TK(BB, TW)                                                                                         \
-  hipLaunchKernelGGL((token_topk_kernel<BB, TW>), g2, dim3(TK_NT), 0, stream, scores, nc, top_k_tokens,          \
-                     block_idx, d.top_k, token_idx, d.num_kv_heads)
+  do {                                                                                                          \
+    auto kfn = token_topk_kernel<BB, TW>;                                                                       \
+    hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
+    if (ea != hipSuccess) return ea;                                                                            \
+    hipLaunchKernelGGL(kfn, g2, dim3(TK_NT), smem, stream, scores, nc, top_k_tokens, block_idx, d.top_k,        \
+                       token_idx, d.num_kv_heads);                                                              \
+  } while (0)
   if (d.page_size == 64) {
     if (two) BSG_TK(64, true); else BSG_TK(64, false);
   } else {
