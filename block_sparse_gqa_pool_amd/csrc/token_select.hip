@@ -21,7 +21,9 @@
 //    levels, with few keys under the chosen prefix, merge equal bins within a wave before the
 //    LDS atomic) finds the K-th key tau; a compaction pass in index
 //    order keeps every key above tau and the first K - #above keys equal to tau, and writes
-//    the kept tokens ascending (-1 padded).
+//    the kept tokens ascending (-1 padded).  Rows of at most 4096 candidates (the two-level
+//    rows) take token_topk_small_kernel: the same steps with 256 threads holding the keys in
+//    registers and one histogram.
 #include "bsg_device.h"
 #include "bsg_internal.h"
 
@@ -35,6 +37,7 @@ constexpr int TK_NW = TK_NT / 64;
 constexpr int TK_BINS = 2048;  // radix bins per level (11 bits)
 constexpr int TK_UNR = 8;      // row tiles (4 scores per thread each) loaded per batch
 constexpr int TK_COPIES = 16;  // level-1 histogram copies (lane % 16): few lanes meet on one entry
+constexpr int TKS_NT = 256;    // threads of the short-row selection workgroup
 }  // namespace
 
 // Token of candidate c of row (b, g): two level, slot c % BS of block block_idx[c / BS];
@@ -140,8 +143,9 @@ __device__ __forceinline__ void tk_hist_add(uint32_t* hist, int bin, bool active
   }
 }
 
-// Exclusive prefix sum over the workgroup (thread order); returns this thread's offset and
-// the total in *tot.  Uses red[TK_NW + 1].
+// Exclusive prefix sum over the workgroup of NW waves (thread order); returns this thread's
+// offset and the total in *tot.  Uses red[NW + 1].
+template <int NW>
 __device__ __forceinline__ uint32_t tk_scan(uint32_t v, uint32_t* red, uint32_t* tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t incl = v;
@@ -154,7 +158,7 @@ __device__ __forceinline__ uint32_t tk_scan(uint32_t v, uint32_t* red, uint32_t*
   __syncthreads();
   uint32_t base = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < TK_NW; w++) {
+  for (int w = 0; w < NW; w++) {
     const uint32_t t = red[w];
     base += w < wave ? t : 0u;
     all += t;
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
     uint32_t mine = 0;
     for (int k = 0; k < per; k++) mine += hist[nb - 1 - (tid * per + k)];
     uint32_t tot;
-    const uint32_t before = tk_scan(mine, red, &tot);   // keys in higher bins than this thread's
+    const uint32_t before = tk_scan<TK_NW>(mine, red, &tot);   // keys in higher bins than this thread's
     if (lv == 0 && tot <= (uint32_t)K) {
       all = true;
       break;
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
         n_eq += (!all && key[e] == tau) ? 1u : 0u;
       }
       uint32_t eq_off = 0, eq_tot = 0;
-      if (rank_eq) eq_off = tk_scan(n_eq, red, &eq_tot);
+      if (rank_eq) eq_off = tk_scan<TK_NW>(n_eq, red, &eq_tot);
       bool keep[4];
       uint32_t n_keep = 0, r = eq_base + eq_off;
 #pragma unroll
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
         n_keep += keep[e] ? 1u : 0u;
       }
       uint32_t ktot;
-      uint32_t o = out_base + tk_scan(n_keep, red, &ktot);
+      uint32_t o = out_base + tk_scan<TK_NW>(n_keep, red, &ktot);
 #pragma unroll
       for (int e = 0; e < 4; e++)
         if (keep[e] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c + e, brow);
@@ -311,6 +315,102 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
     }
   }
   for (int i = (int)out_base + tid; i < K; i += TK_NT) orow[i] = -1;
+}
+
+// The same selection for short rows (nc <= 256 * PER, e.g. the two-level rows of top_k
+// blocks): one workgroup of 256 threads, each holding PER consecutive candidates' keys in
+// registers for all three levels and the compaction, with one LDS histogram.
+template <int BS, bool TWO, int PER>
+__global__ __launch_bounds__(TKS_NT) void token_topk_small_kernel(const float* __restrict__ scores, int nc, int K,
+                                                                  const int32_t* __restrict__ block_idx, int kblk,
+                                                                  int32_t* __restrict__ token_idx, int Hkv) {
+  constexpr int NW = TKS_NT / 64;
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t red[NW + 1];
+  __shared__ uint32_t sel_s[3];
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* row = scores + ((size_t)b * Hkv + g) * nc;
+  const int32_t* brow = TWO ? block_idx + ((size_t)b * Hkv + g) * kblk : nullptr;
+  int32_t* orow = token_idx + ((size_t)b * Hkv + g) * K;
+  const int c0 = tid * PER;
+  uint32_t key[PER];
+#pragma unroll
+  for (int u = 0; u < PER / 4; u++) {
+    const int c = c0 + 4 * u;
+    const float4 v = c < nc ? *reinterpret_cast<const float4*>(row + c)
+                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    key[4 * u] = tk_key(v.x);
+    key[4 * u + 1] = tk_key(v.y);
+    key[4 * u + 2] = tk_key(v.z);
+    key[4 * u + 3] = tk_key(v.w);
+  }
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t above = 0, m_eq = 0;
+  bool all = false;
+  for (int lv = 0; lv < 3; lv++) {
+    const int shift = lv == 0 ? 21 : (lv == 1 ? 10 : 0);
+    const int nbits = lv == 2 ? 10 : 11;
+    const uint32_t dmask = (1u << nbits) - 1u;
+    for (int i = tid; i < TK_BINS; i += TKS_NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; u++)
+      if (key[u] != 0u && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & dmask], 1u);
+    __syncthreads();
+    const uint32_t need = (uint32_t)K - above;
+    const int nb = 1 << nbits;
+    const int per = nb / TKS_NT;
+    uint32_t mine = 0;
+    for (int k = 0; k < per; k++) mine += hist[nb - 1 - (tid * per + k)];
+    uint32_t tot;
+    const uint32_t before = tk_scan<NW>(mine, red, &tot);
+    if (lv == 0 && tot <= (uint32_t)K) {
+      all = true;
+      break;
+    }
+    uint32_t run = before;
+    for (int k = 0; k < per; k++) {
+      const int bin = nb - 1 - (tid * per + k);
+      const uint32_t h = hist[bin];
+      if (run < need && need <= run + h) {
+        sel_s[0] = (uint32_t)bin;
+        sel_s[1] = run;
+        sel_s[2] = h;
+      }
+      run += h;
+    }
+    __syncthreads();
+    prefix |= sel_s[0] << shift;
+    pmask |= dmask << shift;
+    above += sel_s[1];
+    m_eq = sel_s[2];
+    __syncthreads();
+  }
+  const uint32_t tau = all ? 1u : prefix;
+  const uint32_t take_eq = all ? 0u : (uint32_t)K - above;
+  const bool rank_eq = !all && take_eq < m_eq;
+  uint32_t n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < PER; u++) n_eq += (!all && key[u] == tau) ? 1u : 0u;
+  uint32_t eq_off = 0, eq_tot = 0;
+  if (rank_eq) eq_off = tk_scan<NW>(n_eq, red, &eq_tot);
+  bool keep[PER];
+  uint32_t n_keep = 0, r = eq_off;
+#pragma unroll
+  for (int u = 0; u < PER; u++) {
+    const bool gt = all ? key[u] >= tau : key[u] > tau;
+    const bool eq = !all && key[u] == tau;
+    keep[u] = gt || (eq && (!rank_eq || r < take_eq));
+    r += eq ? 1u : 0u;
+    n_keep += keep[u] ? 1u : 0u;
+  }
+  uint32_t ktot;
+  uint32_t o = tk_scan<NW>(n_keep, red, &ktot);
+#pragma unroll
+  for (int u = 0; u < PER; u++)
+    if (keep[u] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c0 + u, brow);
+  for (int i = (int)ktot + tid; i < K; i += TKS_NT) orow[i] = -1;
 }
 
 size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level) {
@@ -344,6 +444,24 @@ hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(d.num_kv_heads, d.batch);
+  if (nc <= TKS_NT * 16) {                         // short rows: keys in registers
+#define BSG_TKS(BB, TW, PP)                                                                                    \
+  hipLaunchKernelGGL((token_topk_small_kernel<BB, TW, PP>), g2, dim3(TKS_NT), 0, stream, scores, nc, top_k_tokens, \
+                     block_idx, d.top_k, token_idx, d.num_kv_heads)
+#define BSG_TKS_P(BB, TW)                                    \
+  do {                                                       \
+    if (nc <= TKS_NT * 8) BSG_TKS(BB, TW, 8);                \
+    else BSG_TKS(BB, TW, 16);                                \
+  } while (0)
+    if (d.page_size == 64) {
+      if (two) BSG_TKS_P(64, true); else BSG_TKS_P(64, false);
+    } else {
+      if (two) BSG_TKS_P(128, true); else BSG_TKS_P(128, false);
+    }
+#undef BSG_TKS_P
+#undef BSG_TKS
+    return hipGetLastError();
+  }
   const size_t smem = (size_t)TK_BINS * TK_COPIES * sizeof(uint32_t);
 #define BSG_TK(BB, TW)                                                                                         \
   do {                                                                                                          \

@@ -33,8 +33,9 @@ CASES = [
                       num_kv_heads=2, top_k=5), 300),                                         # bs 128, D 64, G 16
     (SPECS[2].replace(batch=2, ctx_len=64 * 5 + 3), 2048),                                    # K above every length
     (SPECS[2].replace(batch=2, ctx_len=64 * 20), 1),                                          # K = 1
+    (SPECS[2].replace(batch=2, ctx_len=64 * 90 + 5), 700),                                    # rows > 4096
 ]
-IDS = ["g8_bs64", "ragged", "bs128_d64_g16", "k_all", "k1"]
+IDS = ["g8_bs64", "ragged", "bs128_d64_g16", "k_all", "k1", "long_rows"]
 
 
 @pytest.mark.parametrize("spec,K", CASES, ids=IDS)
