@@ -289,7 +289,7 @@ def test_decode_end_to_end(name, api):
 
 
 @pytest.mark.parametrize("case", [
-    dict(top_k=1), dict(top_k=2), dict(top_k=64), dict(top_k=33),
+    dict(top_k=1), dict(top_k=2), dict(top_k=64), dict(top_k=33), dict(top_k=8), dict(top_k=16, head_dim=64),
     dict(num_q_heads=4, num_kv_heads=4), dict(num_q_heads=16, num_kv_heads=4), dict(num_q_heads=24, num_kv_heads=4),
     dict(head_dim=64), dict(page_size=128, top_k=5), dict(q_len=333), dict(batch=3), dict(seq_len=64 * 3 + 1),
 ])
@@ -418,3 +418,48 @@ def test_decode_step_graph_replay_matches_eager():
                         workspace=ws)
         torch.cuda.synchronize()
     check_decode(w, idx_e, out_e, lse_e)
+
+
+@pytest.mark.parametrize("top_k", [2, 8, 16, 33, 64])
+def test_fused_selection_exact_ties(top_k):
+    """Fused score + top-k with a block cache whose representatives repeat three patterns, so
+    most candidates tie exactly with many others: the kept blocks must be the lowest-indexed
+    ones of the best pattern(s), as in the oracle, bit for bit.  (Identical representatives
+    give identical scores on both sides; rows whose boundary falls between two different
+    patterns closer than 1e-4 relative are left out.)"""
+    spec = SPECS[1].replace(seq_len=64 * 200 + 13, top_k=top_k)
+    note(f"[case] fused selection with exact ties, top_k={top_k}")
+    w = make_workload(spec, 9).to(DEV)
+    q, kp, vp, pt, kv = np_inputs(w)
+    P, Hkv, D = kp.shape[0], spec.num_kv_heads, spec.head_dim
+    rng = np.random.default_rng(5)
+    pats = torch.from_numpy(rng.standard_normal((3, Hkv, D)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    which = (np.arange(P)[:, None] * 5 + np.arange(Hkv)[None, :]) % 3          # [P, Hkv]
+    cache = pats[which, np.arange(Hkv)[None, :]]                                # [P, Hkv, D]
+    sc = O.group_scores(q, cache, pt, kv, Hkv, spec.page_size)
+    ref = O.select_blocks(sc, kv, w.q.shape[2], spec.page_size, top_k)
+    dcache = torch.from_numpy(cache).to(torch.bfloat16).to(DEV)
+    B, Hq, ql, _ = w.q.shape
+    idx = torch.empty(B, Hkv, ql, top_k, dtype=torch.int32, device=DEV)
+    bsg.group_score_topk(w.q, w.kv_lens, dcache, w.page_table, idx, page_size=spec.page_size)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    s32 = np.sort(sc.astype(np.float32), axis=-1)[..., ::-1]                   # descending
+    m = top_k - 1
+    nb = s32.shape[-1]
+    if m == 0 or m >= nb:
+        ok = np.ones(got.shape[:-1], bool)
+        ties = 0
+    else:
+        x, y = s32[..., m - 1], s32[..., m]
+        with np.errstate(invalid="ignore"):
+            tie = (x == y) & np.isfinite(y)
+            far = ~np.isfinite(y) | (np.abs(x - y) > 1e-4 * np.maximum(np.maximum(np.abs(x), np.abs(y)), 1e-30))
+        ok = tie | far
+        ties = int(tie.sum())
+    same = (got == ref).all(-1)
+    bad = np.argwhere(ok & ~same)
+    checked = int(ok.sum())
+    note(f"  rows checked {checked} of {ok.size}, exact ties at the boundary {ties}, mismatches {len(bad)}")
+    assert len(bad) == 0, [(tuple(i), got[tuple(i)], ref[tuple(i)]) for i in bad[:3]]
+    assert ties > 0 and checked > 0.9 * ok.size
