@@ -148,12 +148,17 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    int rank = 0;                            // distinct ranks: equal (zero) keys ordered by lane
+    // rank = number of larger keys.  Keys of real blocks are distinct and nonzero (they hold
+    // the block index), so only the empty slots (key 0, lanes nloc..63) tie; they take their
+    // lane as rank, which keeps every rank distinct.
+    int rank = 0;
+    const ulonglong2* kb2 = reinterpret_cast<const ulonglong2*>(kbuf);
 #pragma unroll 8
-    for (int i = 0; i < 64; i++) {
-      const uint64_t o = kbuf[i];
-      rank += (o > key || (o == key && i < lane)) ? 1 : 0;
+    for (int i = 0; i < 32; i++) {
+      const ulonglong2 o = kb2[i];
+      rank += (o.x > key ? 1 : 0) + (o.y > key ? 1 : 0);
     }
+    if (key == 0ull) rank = lane;
     uint64_t* dst = lists + (((size_t)b * Hkv + g) * nchunks + c) * m;
     if (rank < m) dst[rank] = key;
     __builtin_amdgcn_wave_barrier();
