@@ -25,12 +25,13 @@ __device__ __forceinline__ int count_above(const uint64_t* a, int n, uint64_t ke
 // per chunk of candidate blocks, the chunk's best m = top_k - 1 keys sorted descending (0 =
 // none).  The cnt-th largest of the chunks' first T keys is a lower bound `tau` of the
 // cnt-th largest key overall (at least cnt keys reach it), so the kept keys are among the
-// list keys >= tau -- a prefix of every list, typically little more than cnt keys in all.
-// Those survivors are ranked against each other; sel[r] receives the block id of rank r
-// (r < cnt, largest score first).
+// list keys >= tau, typically little more than cnt keys in all.  Those survivors are
+// ranked against each other; sel[r] receives the block id of rank r (r < cnt, largest
+// score first).
 __device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, int nchunks, int m, int lt, int cnt,
                                        uint64_t* L, uint64_t* S, int* sel, int* counter, uint64_t* tau_s) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int T = 1 << lt;                      // leading keys taken from every chunk list
   const int NT = nchunks << lt;
   const int NL = nchunks * m;
@@ -39,7 +40,8 @@ __device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, i
     *counter = 0;
     *tau_s = 1ull;
   }
-  for (int e0 = 0; e0 < NL; e0 += 4 * 256) {  // lists -> LDS, 4 loads in flight per thread
+  // lists -> LDS, 4 loads in flight per thread; a list's first T keys also go to tops
+  for (int e0 = 0; e0 < NL; e0 += 4 * 256) {
     uint64_t v[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
@@ -49,31 +51,38 @@ __device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, i
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       const int e = e0 + u * 256 + tid;
-      if (e < NL) L[e] = v[u];
+      if (e < NL) {
+        L[e] = v[u];
+        const int c = e / m, i = e - c * m;
+        if (i < T) tops[(c << lt) + i] = v[u];
+      }
     }
   }
+  if (T > m)                                  // positions past the list length hold no key
+    for (int e = tid; e < NT; e += 256)
+      if ((e & (T - 1)) >= m) tops[e] = 0ull;
   __syncthreads();
-  int nvalid = 0;
-  for (int e0 = 0; e0 < NT; e0 += 256) {
-    const int e = e0 + tid;
-    const int i = e & (T - 1);                // position in the chunk's list (T may exceed m)
-    const uint64_t key = (e < NT && i < m) ? L[(e >> lt) * m + i] : 0ull;
-    if (e < NT) tops[e] = key;
-    nvalid += __syncthreads_count(key != 0ull);
-  }
-  if (nvalid >= cnt) {
-    for (int e = tid; e < NT; e += 256) {
-      const uint64_t key = tops[e];
-      if (key != 0ull && count_above(tops, NT, key) == cnt - 1) *tau_s = key;
-    }
+  // tau = the cnt-th largest top.  With fewer than cnt tops set, no set top has cnt - 1
+  // above it, and tau stays 1: every key survives.
+  for (int e = tid; e < NT; e += 256) {
+    const uint64_t key = tops[e];
+    if (key != 0ull && count_above(tops, NT, key) == cnt - 1) *tau_s = key;
   }
   __syncthreads();
   const uint64_t tau = *tau_s;
-  for (int c = tid; c < nchunks; c += 256) {   // this chunk's keys >= tau, appended as one run
-    int nc = 0;
-    while (nc < m && L[c * m + nc] >= tau) nc++;
-    const int at = nc > 0 ? atomicAdd(counter, nc) : 0;
-    for (int i = 0; i < nc; i++) S[at + i] = L[c * m + i];
+  // survivors: the list keys >= tau (tau >= 1, so no empty slot), compacted per wave; their
+  // order does not matter
+  for (int e0 = 0; e0 < NL; e0 += 256) {
+    const int e = e0 + tid;
+    const uint64_t key = e < NL ? L[e] : 0ull;
+    const bool keep = key >= tau;
+    const uint64_t bal = __ballot(keep);
+    if (bal != 0ull) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(counter, __popcll(bal));
+      base = __shfl(base, 0, 64);
+      if (keep) S[base + __popcll(bal & ((1ull << lane) - 1ull))] = key;
+    }
   }
   __syncthreads();
   const int ns = *counter;
