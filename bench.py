@@ -1,21 +1,32 @@
 """Benchmark: block-sparse GQA attention at 128K context on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only PARTS]
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  prefill workload: block_pool -> group_score_topk -> sparse_attn_prefill
-  decode workload:  decode_step = group scores + top-k + sparse attention (block cache built beforehand),
-                    captured (8 steps per HIP graph) and replayed: the step is three short kernels
-Inputs are generated on the GPU and resident in HBM before timing starts.  The default
-workload is the 128K prefill (B=1, S=131072, Hq=64, Hkv=8, D=128, 128-token blocks,
-top-16); the 128K decode step (B=32, context 131072, Hq=32, Hkv=4, 64-token pages,
-top-32) is measured in the same run and reported under "decode".
+  prefill: block_pool -> group_score_topk -> sparse_attn_prefill
+  decode:  decode_step = group scores + top-k + sparse attention (the block cache is built beforehand,
+           as at the end of a prefill); the step is three short kernels, so 8 steps are captured per
+           HIP graph and the graph is replayed
+Inputs are generated on the GPU and resident in HBM before timing starts.
 
-Prints ONE JSON line.  `value` is prefill tokens/s (or decode steps/s-free us/step for
---workload decode).  `roofline` covers the dominant kernel of the step, timed with HIP
-events on the stream the library launches on; its algorithmic work is counted from the
-actual selection (4*D FLOPs per selected, causally valid key per query head for prefill;
-selected K+V bytes + block-cache bytes + page-table bytes for decode).
+The headline workload is the 128K prefill (B=1, S=131072, Hq=64, Hkv=8, D=128, 128-token blocks, top-16);
+`value` is its tokens/s.  The same run also reports, as sub-objects:
+  prefill_s32768      32K prefill (Hq=32, Hkv=4, 64-token blocks, top-32): per-token random plantings
+  decode              128K decode step (B=32, Hq=32, Hkv=4, 64-token shuffled pages, top-32), warm (the same
+                      step replayed) and cold (four disjoint workloads in rotation, so that a step's bytes
+                      were last touched 3 steps = ~590 MB earlier, beyond the 256 MB Infinity Cache)
+  decode_ragged_1m    ragged decode toward 1M (B=4, L ~ U[512K, 1M], Hq=64, Hkv=8, top-32), warm and cold
+  decode_fp8, decode_tokens, decode_two_level   the fp8-cache, token-level and two-level decode steps
+Kernel times are HIP events on the stream the library launches on, one pair per launch; the JSON gives the
+mean (what `ms_per_step` and the roofline use) and the median.
+
+`roofline` covers the dominant kernel (prefill attention): algorithmic FLOPs per launch (4*D per selected,
+causally valid key per query head, counted from the actual selection) over the mean launch time.  Its
+`traffic` and `mfma_util` come from committed rocprofv3 counter summaries under profiles/ and are null
+when the kernel source has changed since they were taken.
+
+`cpu_baseline` is the CPU oracle on the host's cores (a process pool, one worker per core of the affinity
+mask, at most 16), timed on bounded samples of the same workloads and extrapolated linearly.
 """
 from __future__ import annotations
 
@@ -24,7 +35,9 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +47,7 @@ METRIC = "block-sparse GQA attn: prefill tok/s + decode µs/step at 128K, % roof
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+PER_GRAPH = 8               # decode steps captured per HIP graph
 
 
 def _kernel_hash(*files) -> str:
@@ -44,19 +58,28 @@ def _kernel_hash(*files) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_key: str, src_files) -> float | None:
-    """HBM bytes per launch from a committed counter summary, if it matches the current source."""
-    path = os.path.join(PROFILE_DIR, f"{kernel_key}_traffic.json")
+def _profile_record(name: str, src_files):
+    """A committed counter summary (profiles/<name>.json) if it matches the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"{name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_hash") != _kernel_hash(*src_files):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
-# ------------------------------------------------------------------------------------
+def _traffic(kernel_key: str, src_files):
+    rec = _profile_record(f"{kernel_key}_traffic", src_files)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def _stats(xs):
+    return dict(mean=sum(xs) / len(xs), median=statistics.median(xs), min=min(xs), n=len(xs))
+
+
+# ------------------------------------------------------------------------------------ work counts
 def prefill_flops(block_idx, kv_lens, q_len, page_size, G, D):
     """4*D FLOPs per (query head, selected key at a position <= the query)."""
     import torch
@@ -66,6 +89,56 @@ def prefill_flops(block_idx, kv_lens, q_len, page_size, G, D):
     n = torch.clamp(pos - j * page_size + 1, min=0, max=page_size)
     n = torch.where(j >= 0, n, torch.zeros_like(n))
     return float(n.sum().item()) * G * 4 * D
+
+
+def prefill_tile_stats(block_idx, kv_lens, q_len, page_size, G, D):
+    """What the matrix-core prefill kernel processes for this selection.
+
+    A workgroup takes 256 query rows = TT tokens x HG heads of one group (HG = largest power of two
+    dividing G, at most 32) and streams the union of its tokens' blocks once; each wave takes 32 rows
+    (WT = 32 / HG tokens) and runs every 64-key sub-block that one of its rows attends to.  Returns the
+    mean union size per workgroup, the K/V bytes the unions stream, and the FLOPs the waves issue
+    (32 rows x 64 keys x 4 D per processed sub-block) against the algorithmic count."""
+    import torch
+    B, Hkv, T, k = block_idx.shape
+    HG = 1
+    while HG < 32 and G % (HG * 2) == 0:
+        HG *= 2
+    TT, WT = 256 // HG, 32 // HG
+    dev = block_idx.device
+    nb = int(block_idx.max().item()) + 1
+    pos = kv_lens.view(B, 1, 1).long() - q_len + torch.arange(T, device=dev).view(1, 1, T)     # [B,1,T]
+    unions, issued_sub = 0, 0
+    for b in range(B):
+        for g in range(Hkv):
+            idx = block_idx[b, g].long()                                                    # [T, k]
+            p = pos[b, 0].view(T, 1).expand(T, k)
+            Tp = (T + TT - 1) // TT * TT
+            idxp = torch.full((Tp, k), -1, dtype=torch.long, device=dev)
+            idxp[:T] = idx
+            pp = torch.full((Tp, k), -1, dtype=torch.long, device=dev)
+            pp[:T] = p
+            # union per workgroup tile
+            tiles = idxp.view(Tp // TT, TT * k)
+            mask = torch.zeros(Tp // TT, nb + 1, dtype=torch.bool, device=dev)
+            mask.scatter_(1, tiles.clamp(min=-1) + 1, True)
+            unions += int(mask[:, 1:].sum().item())
+            # per wave: for each selected block the furthest query position among the wave's rows
+            w_idx = idxp.view(Tp // WT, WT * k)
+            w_pos = pp.view(Tp // WT, WT * k)
+            mx = torch.full((Tp // WT, nb + 1), -1, dtype=torch.long, device=dev)
+            mx.scatter_reduce_(1, w_idx + 1, w_pos, reduce="amax")
+            mx = mx[:, 1:]
+            jb = torch.arange(nb, device=dev).view(1, nb) * page_size
+            nsub = torch.clamp((mx - jb) // 64 + 1, min=0, max=page_size // 64)
+            nsub = torch.where(mx >= 0, nsub, torch.zeros_like(nsub))
+            issued_sub += int(nsub.sum().item())
+    n_tiles = B * Hkv * ((T + TT - 1) // TT) * (G // HG)
+    issued = float(issued_sub) * (G // HG) * HG * (32 // HG) * 64 * 4 * D
+    return dict(rows_per_workgroup=256, tokens_per_workgroup=TT, tokens_per_wave=WT,
+                mean_union_blocks=unions * (G // HG) / n_tiles,
+                union_kv_bytes=float(unions) * (G // HG) * page_size * D * 2 * 2,
+                issued_flops=issued)
 
 
 def decode_bytes(block_idx, kv_lens, page_size, Hkv, D, elem=2):
@@ -87,76 +160,8 @@ def decode_bytes(block_idx, kv_lens, page_size, Hkv, D, elem=2):
     return kv + reps + pt + sc, dict(selected_kv=kv, block_cache=reps, page_table=pt, scales=sc)
 
 
-def run_decode_tokens(spec, seed, steps, warmup, top_k_tokens, two_level):
-    """Token-level (two_level False) or two-level decode steps, graph-replayed like run_decode.
-    Algorithmic bytes: token level reads every key once (the identity indexer scores all
-    tokens) plus the kept tokens' values and the page table; two level reads the block cache
-    of every candidate, the keys of the kept blocks, and the kept tokens' values."""
-    import torch
-    import block_sparse_gqa_pool_amd as bsg
-    from workloads import make_workload
-
-    dev = torch.device("cuda:0")
-    w = make_workload(spec, seed, device=dev)
-    B, Hq, _, D = w.q.shape
-    Hkv, bs, k = spec.num_kv_heads, spec.page_size, spec.top_k
-    scale = 1.0 / math.sqrt(D)
-    q1 = w.q[:, :, 0].contiguous()
-    out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=dev)
-    tok = torch.empty(B, Hkv, top_k_tokens, dtype=torch.int32, device=dev)
-    cache = bidx = None
-    if two_level:
-        cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
-        bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
-        bidx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
-    d = bsg.dims(w.k_cache, w.page_table, Hq, k if two_level else 1)
-    import ctypes
-    need = int(bsg.lib().bsg_decode_step_tokens_workspace_bytes(ctypes.byref(d), top_k_tokens, int(two_level)))
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        bsg.decode_step_tokens(q1, w.kv_lens, w.k_cache, w.v_cache, w.page_table, scale, tok, out,
-                               block_cache=cache, block_idx=bidx, workspace=ws)
-
-    PER_GRAPH = 4
-    for _ in range(max(warmup, 1)):
-        step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(PER_GRAPH):
-            step()
-    graph.replay()
-    torch.cuda.synchronize()
-    n_rep = max(1, (steps + PER_GRAPH - 1) // PER_GRAPH)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(n_rep):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    steps = n_rep * PER_GRAPH
-    us = 1e3 * e0.elapsed_time(e1) / steps
-    L = w.kv_lens.long()
-    kept = float((tok >= 0).sum().item())
-    v_bytes = kept * D * 2
-    pt = float(((L + bs - 1) // bs).sum().item()) * 4
-    if two_level:
-        own = (L - 1) // bs
-        reps = float(own.sum().item()) * Hkv * D * 2
-        nb = float((bidx >= 0).sum().item())
-        parts = dict(block_cache=reps, kept_block_keys=nb * bs * D * 2, kept_token_values=v_bytes, page_table=pt)
-    else:
-        parts = dict(all_keys=float(L.sum().item()) * Hkv * D * 2, kept_token_values=v_bytes, page_table=pt)
-    nbytes = sum(parts.values())
-    del graph, w, cache, bidx, tok, out, ws
-    torch.cuda.empty_cache()
-    return dict(us_per_step=us, bytes=nbytes, bytes_parts=parts, steps=steps)
-
-
-# ------------------------------------------------------------------------------------
-def run_prefill(spec, seed, steps, warmup):
+# ------------------------------------------------------------------------------------ prefill
+def run_prefill(spec, seed, steps, warmup, tile_stats=False):
     import torch
     import block_sparse_gqa_pool_amd as bsg
     from workloads import make_workload
@@ -196,20 +201,152 @@ def run_prefill(spec, seed, steps, warmup):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(3)]
+    names = ("block_pool", "group_score_topk", "sparse_attn_prefill")
+    stage = {n: _stats([e[i].elapsed_time(e[i + 1]) for e in evs]) for i, n in enumerate(names)}
     step_ms = [e[0].elapsed_time(e[3]) for e in evs]
     flops = prefill_flops(idx, w.kv_lens, S, bs, spec.group_size, D)
-    res = dict(
-        tokens=B * S, wall_s=wall, ms_per_step=sum(step_ms) / steps, wall_ms_per_step=1e3 * wall / steps,
-        stage_ms={n: sum(v) / steps for n, v in zip(("block_pool", "group_score_topk", "sparse_attn_prefill"), stage)},
-        attn_flops=flops,
-    )
+    res = dict(tokens=B * S, wall_s=wall, ms_per_step=sum(step_ms) / steps, wall_ms_per_step=1e3 * wall / steps,
+               stage=stage, attn_flops=flops)
+    if tile_stats:
+        res["tiles"] = prefill_tile_stats(idx, w.kv_lens, S, bs, spec.group_size, D)
     del w, cache, idx, out, ws
     torch.cuda.empty_cache()
     return res
 
 
-def run_decode(spec, seed, steps, warmup, graph_replay=True, fp8=False):
+def prefill_line(spec, r):
+    attn = r["stage"]["sparse_attn_prefill"]
+    achieved = r["attn_flops"] / (attn["mean"] / 1e3) / 1e12
+    d = {"workload": spec.name, "tok_per_s": r["tokens"] / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+         "stages_ms": {n: {"mean": s["mean"], "median": s["median"]} for n, s in r["stage"].items()},
+         "roofline": {"kernel": "sparse_attn_prefill", "bound": "mfma", "achieved": achieved,
+                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                      "flops_per_launch": r["attn_flops"], "avg_launch_ms": attn["mean"],
+                      "median_launch_ms": attn["median"], "launches": attn["n"]},
+         "pipeline_mfma_frac": (r["attn_flops"] / (r["ms_per_step"] / 1e3) / 1e12) / PEAK_BF16_TFLOPS}
+    if "tiles" in r:
+        t = r["tiles"]
+        d["tiles"] = dict(t, selected_over_issued=r["attn_flops"] / t["issued_flops"])
+    return d
+
+
+# ------------------------------------------------------------------------------------ decode
+def _decode_setup(spec, seed, dev, fp8=False):
+    """One decode workload on the device with its block cache built (as at the end of a prefill)."""
+    import torch
+    import block_sparse_gqa_pool_amd as bsg
+    from workloads import make_workload
+
+    w = make_workload(spec, seed, device=dev)
+    B, Hq, _, D = w.q.shape
+    Hkv, bs, k = spec.num_kv_heads, spec.page_size, spec.top_k
+    s = dict(w=w, q1=w.q[:, :, 0].contiguous(), idx=torch.empty(B, Hkv, k, dtype=torch.int32, device=dev),
+             out=torch.empty(B, Hq, D, dtype=w.q.dtype, device=dev),
+             ws=torch.empty(bsg.decode_step_workspace_bytes(w.k_cache, w.page_table, Hq, k), dtype=torch.uint8,
+                            device=dev))
+    if not fp8:
+        cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
+        bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+        s["cache"] = cache
+        return s
+    # fp8 caches, quantised from the bf16 ones at prefill; the bf16 caches are freed
+    P = w.k_cache.shape[0]
+    kc = torch.zeros(P, Hkv, bs, D, dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    ks = torch.ones(P, Hkv, dtype=torch.float32, device=dev)
+    vs = torch.ones_like(ks)
+    bsg.quantize_pages_fp8(w.k_cache, w.page_table, w.kv_lens, kc, ks)
+    bsg.quantize_pages_fp8(w.v_cache, w.page_table, w.kv_lens, vc, vs)
+    rc = torch.zeros(P, Hkv, D, dtype=torch.uint8, device=dev)
+    rs = torch.ones(P, Hkv, dtype=torch.float32, device=dev)
+    bsg.block_pool_fp8(kc, ks, w.page_table, w.kv_lens, rc, rs)
+    w.k_cache = w.v_cache = None
+    s.update(kc=kc, ks=ks, vc=vc, vs=vs, rc=rc, rs=rs)
+    return s
+
+
+def _decode_call(s, scale, fp8):
+    import block_sparse_gqa_pool_amd as bsg
+    w = s["w"]
+    if fp8:
+        bsg.decode_step_fp8(s["q1"], w.kv_lens, s["rc"], s["rs"], s["kc"], s["ks"], s["vc"], s["vs"], w.page_table,
+                            scale, s["idx"], s["out"], workspace=s["ws"])
+    else:
+        bsg.decode_step(s["q1"], w.kv_lens, s["cache"], w.k_cache, w.v_cache, w.page_table, scale, s["idx"],
+                        s["out"], workspace=s["ws"])
+
+
+def run_decode(spec, seed, steps, warmup, fp8=False, rotate=1, graph_replay=True):
+    """Decode steps captured PER_GRAPH to a HIP graph and replayed; with rotate = R > 1 the steps cycle
+    through R workloads of different seeds (disjoint caches and queries), so every step finds its bytes
+    evicted from the last-level cache by the R - 1 steps before it."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    sets = [_decode_setup(spec, seed + 1000 * r, dev, fp8) for r in range(rotate)]
+    D = spec.head_dim
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(warmup, 1)):
+        for s in sets:
+            _decode_call(s, scale, fp8)
+    torch.cuda.synchronize()
+    if not graph_replay:                      # eager steps (counter collection)
+        for i in range(steps):
+            _decode_call(sets[i % rotate], scale, fp8)
+        torch.cuda.synchronize()
+        del sets
+        torch.cuda.empty_cache()
+        return None
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(PER_GRAPH):
+            _decode_call(sets[i % rotate], scale, fp8)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, (steps + PER_GRAPH - 1) // PER_GRAPH)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [1e3 * a.elapsed_time(b) / PER_GRAPH for a, b in evs]      # us
+    parts = [decode_bytes(s["idx"], s["w"].kv_lens, spec.page_size, spec.num_kv_heads, D, elem=1 if fp8 else 2)
+             for s in sets]
+    nbytes = sum(p[0] for p in parts) / rotate
+    res = dict(us=_stats(per_step), wall_us_per_step=1e6 * wall / (n_rep * PER_GRAPH), bytes=nbytes,
+               bytes_parts=parts[0][1], steps=n_rep * PER_GRAPH)
+    del graph, sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_line(spec, d, api, traffic=None, cold=None):
+    def roof(r):
+        us = r["us"]["mean"]
+        gbs = r["bytes"] / (us / 1e6) / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "bytes_per_step": r["bytes"]}
+    line = {"workload": spec.name, "api": api, "us_per_step": d["us"]["mean"], "us_per_step_median": d["us"]["median"],
+            "steps": d["steps"], "timing": f"{PER_GRAPH} steps per HIP graph replay, HIP events per replay",
+            "roofline": dict(roof(d), bytes_parts=d["bytes_parts"], traffic=traffic)}
+    if cold is not None:
+        line["cold"] = {"us_per_step": cold["us"]["mean"], "us_per_step_median": cold["us"]["median"],
+                        "steps": cold["steps"], "rotation": "4 workloads of different seeds, cycled step by step",
+                        "roofline": roof(cold)}
+    return line
+
+
+def run_decode_tokens(spec, seed, steps, warmup, top_k_tokens, two_level):
+    """Token-level (two_level False) or two-level decode steps, graph-replayed like run_decode.
+    Algorithmic bytes: token level reads every key once (the identity indexer scores all
+    tokens) plus the kept tokens' values and the page table; two level reads the block cache
+    of every candidate, the keys of the kept blocks, and the kept tokens' values."""
+    import ctypes
     import torch
     import block_sparse_gqa_pool_amd as bsg
     from workloads import make_workload
@@ -219,122 +356,239 @@ def run_decode(spec, seed, steps, warmup, graph_replay=True, fp8=False):
     B, Hq, _, D = w.q.shape
     Hkv, bs, k = spec.num_kv_heads, spec.page_size, spec.top_k
     scale = 1.0 / math.sqrt(D)
-    cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
-    bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)        # built at prefill (untimed)
-    idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
     q1 = w.q[:, :, 0].contiguous()
     out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=dev)
-    ws = torch.empty(bsg.decode_step_workspace_bytes(w.k_cache, w.page_table, Hq, k), dtype=torch.uint8, device=dev)
+    tok = torch.empty(B, Hkv, top_k_tokens, dtype=torch.int32, device=dev)
+    cache = bidx = None
+    if two_level:
+        cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
+        bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+        bidx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+    d = bsg.dims(w.k_cache, w.page_table, Hq, k if two_level else 1)
+    need = int(bsg.lib().bsg_decode_step_tokens_workspace_bytes(ctypes.byref(d), top_k_tokens, int(two_level)))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
-        bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table, scale, idx, out, workspace=ws)
+        bsg.decode_step_tokens(q1, w.kv_lens, w.k_cache, w.v_cache, w.page_table, scale, tok, out,
+                               block_cache=cache, block_idx=bidx, workspace=ws)
 
-    if fp8:
-        # fp8 caches, quantised from the bf16 ones at prefill (untimed); the bf16 caches are freed
-        P = w.k_cache.shape[0]
-        kc = torch.zeros(P, Hkv, bs, D, dtype=torch.uint8, device=dev)
-        vc = torch.zeros_like(kc)
-        ks = torch.ones(P, Hkv, dtype=torch.float32, device=dev)
-        vs = torch.ones_like(ks)
-        bsg.quantize_pages_fp8(w.k_cache, w.page_table, w.kv_lens, kc, ks)
-        bsg.quantize_pages_fp8(w.v_cache, w.page_table, w.kv_lens, vc, vs)
-        rc = torch.zeros(P, Hkv, D, dtype=torch.uint8, device=dev)
-        rs = torch.ones(P, Hkv, dtype=torch.float32, device=dev)
-        bsg.block_pool_fp8(kc, ks, w.page_table, w.kv_lens, rc, rs)
-        w.k_cache = w.v_cache = None
-        cache = None
-        torch.cuda.empty_cache()
-
-        def step():
-            bsg.decode_step_fp8(q1, w.kv_lens, rc, rs, kc, ks, vc, vs, w.page_table, scale, idx, out, workspace=ws)
-
-    # the step is three short kernels, faster than Python can launch them: capture
-    # PER_GRAPH whole steps in one HIP graph and replay it, so the timed region measures
-    # back-to-back GPU work rather than host launch cost
-    PER_GRAPH = 8
+    per = 4
     for _ in range(max(warmup, 1)):
         step()
     torch.cuda.synchronize()
-    if not graph_replay:                     # eager steps (counter collection)
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        del w, cache, idx, out, ws
-        torch.cuda.empty_cache()
-        return None
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for _ in range(PER_GRAPH):
+        for _ in range(per):
             step()
-    torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
-    n_rep = max(1, (steps + PER_GRAPH - 1) // PER_GRAPH)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(n_rep):
+    n_rep = max(1, (steps + per - 1) // per)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
+    for a, b in evs:
+        a.record(stream)
         graph.replay()
-    e1.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    steps = n_rep * PER_GRAPH
-    step_ms = e0.elapsed_time(e1) / steps
-    nbytes, parts = decode_bytes(idx, w.kv_lens, bs, Hkv, D, elem=1 if fp8 else 2)
-    res = dict(us_per_step=1e3 * step_ms, wall_us_per_step=1e6 * wall / steps, bytes=nbytes, bytes_parts=parts,
-               steps=steps)
-    del graph, w, cache, idx, out, ws
+    us = _stats([1e3 * a.elapsed_time(b) / per for a, b in evs])
+    L = w.kv_lens.long()
+    kept = float((tok >= 0).sum().item())
+    v_bytes = kept * D * 2
+    pt = float(((L + bs - 1) // bs).sum().item()) * 4
+    if two_level:
+        own = (L - 1) // bs
+        reps = float(own.sum().item()) * Hkv * D * 2
+        nb = float((bidx >= 0).sum().item())
+        parts = dict(block_cache=reps, kept_block_keys=nb * bs * D * 2, kept_token_values=v_bytes, page_table=pt)
+    else:
+        parts = dict(all_keys=float(L.sum().item()) * Hkv * D * 2, kept_token_values=v_bytes, page_table=pt)
+    nbytes = sum(parts.values())
+    del graph, w, cache, bidx, tok, out, ws
     torch.cuda.empty_cache()
-    return res
+    gbt = nbytes / (us["mean"] / 1e6) / 1e9
+    return {"us_per_step": us["mean"], "us_per_step_median": us["median"], "api": "bsg_decode_step_tokens",
+            "steps": n_rep * per, "timing": f"{per} steps per HIP graph replay, HIP events per replay",
+            "roofline": {"bound": "hbm", "achieved": gbt, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbt / PEAK_HBM_GBS, "bytes_per_step": nbytes, "bytes_parts": parts,
+                         "traffic": None}}
 
 
-# ------------------------------------------------------------------------------------
-def cpu_baseline_prefill(spec, seed, n_tokens):
-    """The CPU oracle on a bounded sample of the same workload (one BLAS thread)."""
+# ------------------------------------------------------------------------------------ CPU oracle
+# The oracle runs in spawned worker processes (one per core, no GPU); the paged pools reach them as
+# memory-mapped float32 files, queries and tables as task arguments.
+_ORACLE = {}
+
+
+def _oracle_worker_init(paths):
+    import numpy as np
+    try:                                   # one BLAS thread per worker: the pool supplies the parallelism
+        from threadpoolctl import threadpool_limits
+        _ORACLE["blas"] = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        pass
+    for name, (path, shape) in paths.items():
+        _ORACLE[name] = np.memmap(path, dtype=np.float32, mode="r", shape=tuple(shape))
+
+
+def _oracle_noop(_):
+    return os.getpid()
+
+
+def _oracle_prefill_range(args):
+    """Oracle scores, top-k and attention for the queries [t0, t0 + n) of a prefill: the chunk of a
+    prefill whose queries end at position t0 + n - 1, i.e. kv_len = t0 + n, q_len = n."""
+    import oracle as O
+    q_rows, pt, t0, Hkv, bs, k, scale = args
+    n = q_rows.shape[2]
+    kv = [t0 + n]
+    sc = O.group_scores(q_rows, _ORACLE["cache"], pt, kv, Hkv, bs)
+    idx = O.select_blocks(sc, kv, n, bs, k)
+    O.sparse_attention(q_rows, _ORACLE["k"], _ORACLE["v"], pt, kv, idx, scale)
+    return n
+
+
+def _oracle_decode_seq(args):
+    """Oracle decode step (scores, top-k, attention) of one sequence; the block cache is given."""
+    import oracle as O
+    q1, pt, kv, Hkv, bs, k, scale = args
+    sc = O.group_scores(q1, _ORACLE["cache"], pt, kv, Hkv, bs)
+    idx = O.select_blocks(sc, kv, 1, bs, k)
+    O.sparse_attention(q1, _ORACLE["k"], _ORACLE["v"], pt, kv, idx, scale)
+    return 1
+
+
+def _host_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _memmaps(tmp, arrays):
+    import numpy as np
+    paths = {}
+    for name, a in arrays.items():
+        path = os.path.join(tmp, name + ".f32")
+        mm = np.memmap(path, dtype=np.float32, mode="w+", shape=a.shape)
+        mm[:] = a
+        mm.flush()
+        del mm
+        paths[name] = (path, list(a.shape))
+    return paths
+
+
+def _pool(paths, n):
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    ex = cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"), initializer=_oracle_worker_init,
+                                initargs=(paths,))
+    list(ex.map(_oracle_noop, range(4 * n)))      # start every worker before timing
+    return ex
+
+
+def cpu_baseline_prefill(spec, seed, n_ranges=32, range_len=192):
+    """The oracle on the host's cores: the block pool over all blocks (one process, vectorised), then
+    scores + top-k + attention for n_ranges query ranges of range_len tokens spread over the sequence,
+    extrapolated linearly to all tokens."""
     import numpy as np
     import torch
     import oracle as O
     from workloads import make_workload
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
     w = make_workload(spec, seed, device="cuda:0" if torch.cuda.is_available() else "cpu")
-    q = w.q.float().cpu().numpy()
     kp = w.k_cache.float().cpu().numpy()
     vp = w.v_cache.float().cpu().numpy()
     pt = w.page_table.cpu().numpy()
     kv = list(w.kv_lens_host)
+    S = w.q.shape[2]
+    starts = np.linspace(0, S - range_len, n_ranges).astype(np.int64)
+    q_rows = [w.q[:, :, t0:t0 + range_len].float().cpu().numpy() for t0 in starts]
     del w
     torch.cuda.empty_cache()
-    S = q.shape[2]
-    rng = np.random.default_rng(0)
-    tsel = np.sort(rng.choice(S, size=n_tokens, replace=False))
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
-        t0 = time.perf_counter()
-        cache = O.block_pool(kp, pt, kv, spec.dtype)
-        t1 = time.perf_counter()
-        sc = O.group_scores(q, cache, pt, kv, spec.num_kv_heads, spec.page_size, tsel)
-        idx = O.select_blocks(sc, kv, S, spec.page_size, spec.top_k, tsel)
-        O.sparse_attention(q, kp, vp, pt, kv, idx, 1.0 / math.sqrt(spec.head_dim), tsel)
-        t2 = time.perf_counter()
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    per_tok = (t2 - t1) / n_tokens
-    est = (t1 - t0) + per_tok * S
-    return dict(value=S / est, unit="tok/s", cores=1, kind="oracle",
-                sample=(f"block_pool over all {pt.shape[1]} blocks ({t1 - t0:.1f} s) + scores, top-k and "
-                        f"attention for {n_tokens} random query tokens ({t2 - t1:.1f} s), extrapolated "
-                        f"linearly to all {S} tokens: {est:.0f} s per prefill"),
-                seconds=t2 - t0)
+    t0 = time.perf_counter()
+    cache = O.block_pool(kp, pt, kv, spec.dtype)
+    t_pool = time.perf_counter() - t0
+    nw = _host_workers()
+    scale = 1.0 / math.sqrt(spec.head_dim)
+    with tempfile.TemporaryDirectory() as tmp:
+        paths = _memmaps(tmp, dict(k=kp, v=vp, cache=cache))
+        del kp, vp
+        ex = _pool(paths, nw)
+        try:
+            t1 = time.perf_counter()
+            done = sum(ex.map(_oracle_prefill_range, [(q, pt, int(s), spec.num_kv_heads, spec.page_size, spec.top_k,
+                                                       scale) for q, s in zip(q_rows, starts)]))
+            t_att = time.perf_counter() - t1
+        finally:
+            ex.shutdown()
+    est = t_pool + t_att / done * S
+    return dict(value=S / est, unit="tok/s", cores=nw, kind="oracle",
+                sample=(f"block_pool over all {pt.shape[1]} blocks ({t_pool:.1f} s, one process) + scores, top-k and "
+                        f"attention for {n_ranges} query ranges of {range_len} tokens spread over the sequence "
+                        f"({done} tokens, {t_att:.1f} s wall on {nw} worker processes), extrapolated linearly to all "
+                        f"{S} tokens: {est:.0f} s per prefill"),
+                seconds=t_pool + t_att)
 
 
-# ------------------------------------------------------------------------------------
-# HBM traffic from rocprofv3 counters
+def cpu_baseline_decode(spec, seed, n_sample=8, n_steps=5):
+    """The oracle decode step on the host's cores: the pages of n_sample sequences are taken from the
+    workload, their block cache built beforehand (as on the GPU); one step = all B sequences, each a
+    task (sequence b runs sample b mod n_sample); median of n_steps steps."""
+    import numpy as np
+    import torch
+    import oracle as O
+    from workloads import make_workload
+
+    w = make_workload(spec, seed, device="cuda:0" if torch.cuda.is_available() else "cpu")
+    B = w.q.shape[0]
+    bs = spec.page_size
+    seqs = list(range(min(n_sample, B)))
+    pt_full = w.page_table.cpu().numpy()
+    rows, pages = [], []
+    for b in seqs:
+        n = (w.kv_lens_host[b] + bs - 1) // bs
+        rows.append((len(pages), n))
+        pages.extend(pt_full[b, :n].tolist())
+    sel = torch.tensor(pages, dtype=torch.int64, device=w.k_cache.device)
+    kp = w.k_cache.index_select(0, sel).float().cpu().numpy()
+    vp = w.v_cache.index_select(0, sel).float().cpu().numpy()
+    q = [w.q[b:b + 1].float().cpu().numpy() for b in seqs]
+    kvs = [w.kv_lens_host[b] for b in seqs]
+    del w, sel
+    torch.cuda.empty_cache()
+    pts = []
+    for o, n in rows:
+        pts.append(np.arange(o, o + n, dtype=np.int32)[None, :])
+    cache = np.zeros((kp.shape[0], spec.num_kv_heads, spec.head_dim), np.float32)
+    for i in range(len(seqs)):
+        cache = O.block_pool(kp, pts[i], [kvs[i]], spec.dtype, block_cache=cache)
+    nw = _host_workers()
+    scale = 1.0 / math.sqrt(spec.head_dim)
+    tasks = [(q[b % len(seqs)], pts[b % len(seqs)], [kvs[b % len(seqs)]], spec.num_kv_heads, bs, spec.top_k, scale)
+             for b in range(B)]
+    with tempfile.TemporaryDirectory() as tmp:
+        paths = _memmaps(tmp, dict(k=kp, v=vp, cache=cache))
+        del kp, vp
+        ex = _pool(paths, nw)
+        try:
+            times = []
+            for _ in range(n_steps):
+                t1 = time.perf_counter()
+                list(ex.map(_oracle_decode_seq, tasks))
+                times.append(time.perf_counter() - t1)
+        finally:
+            ex.shutdown()
+    med = statistics.median(times)
+    return dict(value=1e6 * med, unit="us/step", cores=nw, kind="oracle",
+                sample=(f"one step = all {B} sequences (sequence b replays sampled sequence b mod {len(seqs)}: "
+                        f"their pages and block cache, built beforehand), {B} tasks on {nw} worker processes; "
+                        f"median of {n_steps} steps"),
+                seconds=sum(times))
+
+
+# ------------------------------------------------------------------------------------ counters
+# HBM traffic (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) and matrix-core utilisation of the kernels
 TRAFFIC_KERNELS = {
     # key: (kernel-name substring, source files, workload); the fp8 instantiations carry F8 = true
     "sparse_attn_prefill_s131072": ("attn_prefill_mfma", ["attn_prefill.hip"], "prefill_bf16_s131072"),
@@ -348,6 +602,11 @@ TRAFFIC_KERNELS = {
                                       "decode_bf16_b32_ctx131072 in fp8"),
 }
 CALIB_BYTES = 1 << 30
+# matrix-core counters of the prefill attention kernel: one rocprofv3 pass
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                 "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+NUM_SIMDS = 1024            # 256 CUs x 4 SIMDs
+NUM_XCDS = 8
 
 
 def traffic_run():
@@ -367,6 +626,15 @@ def traffic_run():
     print("traffic run done", flush=True)
 
 
+def counter_run():
+    """Prefill steps of the 128K and 32K workloads (run under rocprofv3 --pmc MFMA_COUNTERS)."""
+    from workloads import spec_by_name, SPECS
+    for name in ("prefill_bf16_s131072", "prefill_bf16_s32768"):
+        sp = spec_by_name(name)
+        run_prefill(sp, SPECS.index(sp), 2, 1)
+        print(f"counter run: {name} done", flush=True)
+
+
 def _pmc_rows(directory):
     import csv
     import glob
@@ -377,8 +645,10 @@ def _pmc_rows(directory):
     per = {}
     for r in rows:
         did = int(r["Dispatch_Id"])
-        per.setdefault(did, {"name": r["Kernel_Name"], "val": 0.0})
-        per[did]["val"] += float(r["Counter_Value"])
+        e = per.setdefault(did, {"name": r["Kernel_Name"], "val": 0.0, "counters": {}})
+        v = float(r["Counter_Value"])
+        e["val"] += v
+        e["counters"][r["Counter_Name"]] = e["counters"].get(r["Counter_Name"], 0.0) + v
     return [per[k] for k in sorted(per)]
 
 
@@ -410,22 +680,68 @@ def summarize_traffic(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+def summarize_counters(pmc_dir, trace_dir):
+    """MFMA utilisation of the prefill attention kernel from one --pmc pass (MFMA_COUNTERS) and its
+    kernel trace (durations).  Writes profiles/sparse_attn_prefill_<workload>_mfma.json per workload."""
+    import csv
+    import glob
+    rows = [r for r in _pmc_rows(pmc_dir) if "attn_prefill_mfma" in r["name"]]
+    tfiles = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    durs = []
+    if tfiles:
+        for r in csv.DictReader(open(tfiles[0])):
+            if "attn_prefill_mfma" in r["Kernel_Name"]:
+                durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    # the counter run launches 3 prefill steps of the 128K workload, then 3 of the 32K one
+    groups = {"s131072": rows[:3], "s32768": rows[3:6]}
+    dgroups = {"s131072": durs[:3], "s32768": durs[3:6]}
+    out = []
+    for wl, rs in groups.items():
+        if not rs:
+            continue
+        c = {k: sum(r["counters"].get(k, 0.0) for r in rs) / len(rs) for k in MFMA_COUNTERS}
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"]
+        # GRBM_GUI_ACTIVE is summed over the XCDs; per XCD it counts the kernel's active GPU cycles
+        active = c["GRBM_GUI_ACTIVE"] / NUM_XCDS
+        rec = {"kernel": "attn_prefill_mfma_kernel", "workload": f"prefill_bf16_{wl}",
+               "source_hash": _kernel_hash("attn_prefill.hip"), "launches": len(rs), "counters_per_launch": c,
+               "mfma_busy_frac": busy / (active * NUM_SIMDS) if active else None,
+               "mfma_valu_coexec_frac": c["SQ_VALU_MFMA_COEXEC_CYCLES"] / (active * NUM_SIMDS) if active else None,
+               "valu_insts_per_mfma": c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"] if c["SQ_INSTS_MFMA"] else None,
+               "active_cycles_per_xcd": active}
+        dd = dgroups.get(wl) or []
+        if dd:
+            rec["trace_duration_ms"] = 1e3 * sum(dd) / len(dd)
+            rec["observed_clock_ghz"] = active / (sum(dd) / len(dd)) / 1e9
+        with open(os.path.join(PROFILE_DIR, f"sparse_attn_prefill_{wl}_mfma.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        out.append(rec)
+        print(json.dumps(rec))
+    return out
+
+
+# ------------------------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_bf16_s131072")
-    ap.add_argument("--decode-workload", default="decode_bf16_b32_ctx131072")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
-    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--only", default="all",
+                    help="comma list of parts: prefill,prefill32k,decode,decode1m,fp8,tokens (default all)")
     ap.add_argument("--traffic-run", action="store_true", help="one prefill + decode step and a calibration copy")
+    ap.add_argument("--counter-run", action="store_true", help="prefill steps for rocprofv3 --pmc of MFMA counters")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output directories -> profiles/*_traffic.json")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "TRACE_DIR"),
+                    help="rocprofv3 --pmc (MFMA counters) and --kernel-trace output directories of --counter-run "
+                         "-> profiles/sparse_attn_prefill_*_mfma.json")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library has no multi-GPU path; "
@@ -441,77 +757,77 @@ def main():
     if args.traffic_run:
         traffic_run()
         return
-    spec = spec_by_name(args.workload)
-    seed = args.seed if args.seed is not None else SPECS.index(spec)
+    if args.counter_run:
+        counter_run()
+        return
+    parts = set(("prefill,prefill32k,decode,decode1m,fp8,tokens" if args.only == "all" else args.only).split(","))
+    steps = max(args.steps, 1)
 
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    spec = spec_by_name("prefill_bf16_s131072")
     line = {"metric": METRIC}
-    if spec.mode == "prefill":
-        r = run_prefill(spec, seed, args.steps, args.warmup)
-        tok_s = r["tokens"] / (r["ms_per_step"] / 1e3)
-        attn_ms = r["stage_ms"]["sparse_attn_prefill"]
-        achieved = r["attn_flops"] / (attn_ms / 1e3) / 1e12
-        line.update(value=tok_s, unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+    if "prefill" in parts:
+        r = run_prefill(spec, SPECS.index(spec), steps, args.warmup, tile_stats=True)
+        p = prefill_line(spec, r)
+        log(f"prefill 128K: {p['tok_per_s'] / 1e6:.2f} M tok/s, attention {p['roofline']['avg_launch_ms']:.2f} ms")
+        roof = dict(p["roofline"], traffic=_traffic("sparse_attn_prefill_s131072", ["attn_prefill.hip"]))
+        mf = _profile_record("sparse_attn_prefill_s131072_mfma", ["attn_prefill.hip"])
+        roof["mfma_util"] = None if mf is None else {k: mf.get(k) for k in (
+            "mfma_busy_frac", "mfma_valu_coexec_frac", "valu_insts_per_mfma", "observed_clock_ghz")}
+        line.update(value=p["tok_per_s"], unit="tok/s", n_gpus=1, steps=steps, warmup=args.warmup,
                     ms_per_step=r["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None,
                     dtype="bf16", data="synthetic (seeded planted-block generator)",
                     config={"workload": spec.name, "batch": spec.batch, "seq_len": spec.seq_len,
                             "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
                             "head_dim": spec.head_dim, "block_size": spec.page_size, "top_k": spec.top_k},
-                    roofline={"kernel": "sparse_attn_prefill", "bound": "mfma", "achieved": achieved,
-                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                              "traffic": _traffic("sparse_attn_prefill_s131072", ["attn_prefill.hip"]),
-                              "flops_per_launch": r["attn_flops"], "avg_launch_ms": attn_ms},
-                    stages_ms=r["stage_ms"], wall_ms_per_step=r["wall_ms_per_step"],
-                    pipeline_mfma_frac=(r["attn_flops"] / (r["ms_per_step"] / 1e3) / 1e12) / PEAK_BF16_TFLOPS)
-        dspec = spec_by_name(args.decode_workload)
-        d = run_decode(dspec, SPECS.index(dspec), max(args.steps, 40), args.warmup)
-        gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9
+                    roofline=roof, stages_ms=p["stages_ms"], wall_ms_per_step=r["wall_ms_per_step"],
+                    pipeline_mfma_frac=p["pipeline_mfma_frac"], tiles=p["tiles"])
+    if "prefill32k" in parts:
+        s1 = spec_by_name("prefill_bf16_s32768")
+        r1 = run_prefill(s1, SPECS.index(s1), steps, args.warmup, tile_stats=True)
+        p1 = prefill_line(s1, r1)
+        mf1 = _profile_record("sparse_attn_prefill_s32768_mfma", ["attn_prefill.hip"])
+        p1["roofline"]["mfma_util"] = None if mf1 is None else {k: mf1.get(k) for k in (
+            "mfma_busy_frac", "mfma_valu_coexec_frac", "valu_insts_per_mfma", "observed_clock_ghz")}
+        line["prefill_s32768"] = p1
+        log(f"prefill 32K: {p1['tok_per_s'] / 1e6:.2f} M tok/s, attention {p1['roofline']['avg_launch_ms']:.3f} ms")
+    dsteps = max(steps, 400)
+    if "decode" in parts:
+        ds = spec_by_name("decode_bf16_b32_ctx131072")
+        seed = SPECS.index(ds)
+        warm = run_decode(ds, seed, dsteps, args.warmup)
+        cold = run_decode(ds, seed, dsteps, args.warmup, rotate=4)
         tr_a = _traffic("decode_attn_b32_ctx131072", ["attn_decode.hip"])
         tr_s = _traffic("decode_scan_b32_ctx131072", ["decode_select.hip"])
-        line["decode"] = {"workload": dspec.name, "us_per_step": d["us_per_step"], "api": "bsg_decode_step",
-                          "steps": d["steps"], "timing": "8 steps per HIP graph replay, HIP events",
-                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                       "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": d["bytes"],
-                                       "bytes_parts": d["bytes_parts"],
-                                       "traffic": (tr_a + tr_s) if (tr_a and tr_s) else None},
-                          "wall_us_per_step": d["wall_us_per_step"]}
-        d8 = run_decode(dspec, SPECS.index(dspec), max(args.steps, 40), args.warmup, fp8=True)
+        line["decode"] = decode_line(ds, warm, "bsg_decode_step", (tr_a + tr_s) if (tr_a and tr_s) else None, cold)
+        log(f"decode 128K x 32: warm {warm['us']['mean']:.1f} us, cold {cold['us']['mean']:.1f} us")
+        if not args.no_cpu_baseline:
+            line["decode"]["cpu_baseline"] = cpu_baseline_decode(ds, seed)
+    if "fp8" in parts:
+        ds = spec_by_name("decode_bf16_b32_ctx131072")
+        d8 = run_decode(ds, SPECS.index(ds), dsteps, args.warmup, fp8=True)
         tr_a8 = _traffic("decode_fp8_attn_b32_ctx131072", ["attn_decode.hip"])
         tr_s8 = _traffic("decode_fp8_scan_b32_ctx131072", ["decode_select.hip"])
-        gbs8 = d8["bytes"] / (d8["us_per_step"] / 1e6) / 1e9
-        line["decode_fp8"] = {"workload": dspec.name + " (K, V and block cache in fp8 E4M3)",
-                              "us_per_step": d8["us_per_step"], "api": "bsg_decode_step_fp8", "steps": d8["steps"],
-                              "timing": "8 steps per HIP graph replay, HIP events",
-                              "roofline": {"bound": "hbm", "achieved": gbs8, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                           "frac": gbs8 / PEAK_HBM_GBS, "bytes_per_step": d8["bytes"],
-                                           "bytes_parts": d8["bytes_parts"],
-                                           "traffic": (tr_a8 + tr_s8) if (tr_a8 and tr_s8) else None},
-                              "wall_us_per_step": d8["wall_us_per_step"]}
+        l8 = decode_line(ds, d8, "bsg_decode_step_fp8", (tr_a8 + tr_s8) if (tr_a8 and tr_s8) else None)
+        l8["workload"] = ds.name + " (K, V and block cache in fp8 E4M3)"
+        line["decode_fp8"] = l8
+    if "decode1m" in parts:
+        s4 = spec_by_name("decode_bf16_b4_ctx512k_1m")
+        seed = SPECS.index(s4)
+        warm = run_decode(s4, seed, dsteps, args.warmup)
+        cold = run_decode(s4, seed, dsteps, args.warmup, rotate=4)
+        line["decode_ragged_1m"] = decode_line(s4, warm, "bsg_decode_step", None, cold)
+        log(f"decode ~1M x 4: warm {warm['us']['mean']:.1f} us, cold {cold['us']['mean']:.1f} us")
+    if "tokens" in parts:
+        ds = spec_by_name("decode_bf16_b32_ctx131072")
         for key, K, two in (("decode_tokens", 2048, False), ("decode_two_level", 512, True)):
-            dt = run_decode_tokens(dspec, SPECS.index(dspec), max(args.steps, 16), args.warmup, K, two)
-            gbt = dt["bytes"] / (dt["us_per_step"] / 1e6) / 1e9
-            line[key] = {"workload": dspec.name + (f" (block top-{dspec.top_k}, then token top-{K})" if two
-                                                   else f" (token top-{K})"),
-                         "us_per_step": dt["us_per_step"], "api": "bsg_decode_step_tokens", "steps": dt["steps"],
-                         "timing": "4 steps per HIP graph replay, HIP events",
-                         "roofline": {"bound": "hbm", "achieved": gbt, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                      "frac": gbt / PEAK_HBM_GBS, "bytes_per_step": dt["bytes"],
-                                      "bytes_parts": dt["bytes_parts"], "traffic": None}}
-    else:
-        d = run_decode(spec, seed, args.steps, args.warmup)
-        gbs = d["bytes"] / (d["us_per_step"] / 1e6) / 1e9
-        line.update(value=d["us_per_step"], unit="us/step", n_gpus=1, steps=args.steps, warmup=args.warmup,
-                    ms_per_step=d["us_per_step"] / 1e3, higher_is_better=False, scaling="weak", vs_baseline=None,
-                    dtype="bf16", data="synthetic (seeded planted-block generator)",
-                    config={"workload": spec.name, "batch": spec.batch, "num_q_heads": spec.num_q_heads,
-                            "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
-                            "block_size": spec.page_size, "top_k": spec.top_k},
-                    roofline={"kernel": "decode step", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                              "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None,
-                              "bytes_per_step": d["bytes"]})
-    if not args.no_cpu_baseline and spec.mode == "prefill":
-        line["cpu_baseline"] = cpu_baseline_prefill(spec, seed, args.cpu_tokens)
-    else:
-        line["cpu_baseline"] = None
+            dt = run_decode_tokens(ds, SPECS.index(ds), max(steps, 64), args.warmup, K, two)
+            dt["workload"] = ds.name + (f" (block top-{ds.top_k}, then token top-{K})" if two else f" (token top-{K})")
+            line[key] = dt
+    if "prefill" in parts:
+        line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(spec, SPECS.index(spec))
     print(json.dumps(line), flush=True)
 
 

@@ -5,7 +5,7 @@
 //
 // bf16 path (matrix cores, gfx950 v_mfma_f32_32x32x16_bf16)
 // ---------------------------------------------------------
-// A workgroup (4 waves) owns 128 query rows = TT tokens x HG heads of one GQA group.  It
+// A workgroup (8 waves) owns 256 query rows = TT tokens x HG heads of one GQA group.  It
 // builds the union of its tokens' selected blocks (ascending) and streams those blocks'
 // K and V tiles through LDS once; every wave runs the blocks that any of its rows selected
 // and skips the others.  Per wave, 32 query rows:
@@ -75,9 +75,11 @@ __device__ __forceinline__ void wait_copies_barrier() {
 //  * a workgroup is 8 waves (256 query rows = 32 tokens x 8 heads for G = 8): the selections
 //    of neighbouring tokens overlap, so the union grows much slower than the row count and
 //    the K/V bytes fetched per query row drop with the tile size;
-//  * wave-uniform fast path without masks when every row of the wave selected the block
-//    and it is no row's own block; the running maximum (and with it the output) is only
-//    moved when some row's maximum exceeds it by more than a factor 2^8 in probability;
+//  * a wave skips every sub-block that none of its rows attends to; rows of the wave that did
+//    not select the block get weight 0 through an infinite offset, and the causal mask is
+//    applied only when the block is some row's own block;
+//  * each row keeps a lazy reference maximum: the output and sum are only rescaled when a
+//    sub-block would push a lane's sum of weights past 2^64 (or on the row's first block);
 //  * workgroups are mapped to tiles XCD by XCD: the dispatcher deals workgroups to the 8
 //    XCDs round robin, so consecutive ids are remapped to give each XCD a contiguous range
 //    of tiles, whose selections overlap, in its own L2.
@@ -356,7 +358,11 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
 #pragma unroll
           for (int e = 0; e < 16; e++) mx = fmaxf(mx, sacc[kc][e]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const bool bad_row = bad || __shfl_xor((int)bad, 32, 64) != 0;
+        // both halves of a row must move together: every lane reads its partner's flag (a
+        // cross-lane read inside a short-circuit would run only in the lanes that are not bad,
+        // and their partners, the bad lanes, would be inactive sources)
+        const int partner_bad = __shfl_xor((int)bad, 32, 64);
+        const bool bad_row = bad || partner_bad != 0;
         const float m_new = (act && bad_row) ? fmaxf(m_i, mx) : m_i;
         const float alpha = m_new == m_i ? 1.0f : __builtin_amdgcn_exp2f((m_i - m_new) * c2);
         l_i *= alpha;

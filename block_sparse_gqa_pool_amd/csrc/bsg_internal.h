@@ -9,8 +9,8 @@
 
 namespace bsg {
 // Gated fusion of an attention output with a caller tensor ("Sparse Attention for
-// Long-Context LLMs", section 5.5, step 6: out = Gate * A + (1 - Gate) * X, the gate being
-// a scalar or a per-dimension vector).  g == nullptr: no fusion.  g is fp32, one value per
+// Long-Context LLMs", section 4.3 "Gating Mechanisms Reduce Risk", step 6: out = Gate * A +
+// (1 - Gate) * X, the gate being a scalar or a per-dimension vector).  g == nullptr: no fusion.  g is fp32, one value per
 // (sequence, head, query) row (per_dim = 0) or per element (per_dim = 1); x has the output's
 // dtype and layout.
 struct gate_args {

@@ -177,9 +177,10 @@ int bsg_sparse_attn_prefill(const bsg_dims* dims, const void* q, int32_t q_len,
 /*
  * bsg_sparse_attn_prefill_gated -- bsg_sparse_attn_prefill followed by the gated fusion
  * of its output A with a caller tensor x ("Sparse Attention for Long-Context LLMs",
- * section 5.5, step 6: the output is Gate * A + (1 - Gate) * the original representation,
- * the gate being a scalar or a per-dimension vector; the Linear Backbones page, section
- * 5.5, ends its pseudocode the same way):
+ * section 4.3 "Gating Mechanisms Reduce Risk", step 6: the output is Gate * A plus
+ * (1 - Gate) times the original representation, the gate being a scalar or a
+ * per-dimension vector; the pseudocode of the Linear Backbones page, section 5.5, also
+ * ends with a gated fusion):
  *     out = g * A + (1 - g) * x
  * computed in fp32 from the fp32 attention output and rounded once to the dtype.
  * gate : fp32, [B, Hq, q_len] (gate_per_dim = 0: one gate per head and query) or

@@ -33,7 +33,7 @@ What is computed, with the passage each step follows:
    mask, i.e. the unselected keys do not take part).  Inside the own block a
    key takes part only if its position is at most the query's position.
 5. Gated fusion (optional; "Sparse Attention for Long-Context LLMs", section
-   5.5, step 6: the final output is the gate times the attention output plus
+   4.3 "Gating Mechanisms Reduce Risk", step 6: the final output is the gate times the attention output plus
    one minus the gate times the original representation, the gate being a
    scalar or a vector per dimension).  Here the gate and the other tensor are
    caller inputs: out = g * A + (1 - g) * x, in float64.
@@ -321,7 +321,7 @@ def decode_reference(q, k_pages, v_pages, page_table, kv_lens, page_size, top_k,
 # 5. gated fusion
 
 def gated_fusion(a: np.ndarray, gate: np.ndarray, x: np.ndarray) -> np.ndarray:
-    """Gate * A + (1 - Gate) * X ("Sparse Attention for Long-Context LLMs", section 5.5,
+    """Gate * A + (1 - Gate) * X ("Sparse Attention for Long-Context LLMs", section 4.3,
     step 6), in float64.  ``a`` and ``x`` have the output's shape [..., D]; ``gate`` has
     that shape (one gate per dimension) or that shape without the last axis (one gate per
     row, broadcast over D)."""

@@ -107,6 +107,25 @@ def check_out(gpu_out: np.ndarray, ref: np.ndarray, dtype: str, what: str):
         assert mx <= F32_MAX, f"{what}: max {mx}"
 
 
+def check_out_peaked(gpu_out: np.ndarray, ref: np.ndarray, what: str):
+    """bf16 outputs of a sharply peaked softmax (large logits): element-wise
+    |err| <= BF16_MAX + 2^-7 |ref| and mean-abs <= BF16_MEAN.
+
+    When one weight dominates, the output is close to a single value row, and two bf16
+    roundings each cost up to the unit roundoff 2^-8 of its magnitude: the output's own
+    rounding, and the rounding of the dominant weight (the weights enter the value product
+    in bf16, their sum in fp32).  The absolute bound alone is sized for outputs averaged over
+    many keys, whose magnitude is well below 1."""
+    err = np.abs(gpu_out.astype(np.float64) - ref)
+    lim = BF16_MAX + 2.0 ** -7 * np.abs(ref)
+    worst = float((err / lim).max()) if err.size else 0.0
+    mean = float(err.mean()) if err.size else 0.0
+    note(f"  {what}: max abs err {float(err.max()) if err.size else 0:.3e} (|ref| up to "
+         f"{float(np.abs(ref).max()) if err.size else 0:.2f}), worst err / bound {worst:.3f}, mean abs err {mean:.3e}")
+    assert np.all(np.isfinite(gpu_out)), f"{what}: non-finite outputs"
+    assert worst <= 1.0 and mean <= BF16_MEAN, f"{what}: worst err/bound {worst}, mean {mean}"
+
+
 def mini_pool(w, seqs: Sequence[int]):
     """Host copies holding only the pages of the given sequences, with a remapped table."""
     pt = w.page_table.cpu().numpy()
@@ -151,3 +170,45 @@ def compare_token_selection(gpu_idx: np.ndarray, ora_idx: np.ndarray, scores64: 
                                              for j in set(gi) ^ set(oi))
         (exempt if ok else bad).append((int(b), int(g), int(t)))
     return bad, exempt
+
+
+def lazy_max_rescale_rows(q, kp, pt, kv, idx, scale: float, page_size: int, group_size: int, sub: int = 64):
+    """Rows (sequence, query head, query) of a prefill that must move a lazily kept softmax
+    reference maximum after their first sub-block.
+
+    The matrix-core prefill kernel keeps, per row, the maximum m of the first 64-key sub-block
+    it attends to, and only rescales its accumulated output and sum when a later sub-block
+    holds a weight exp(z - m) above 2^64, i.e. a scaled logit z more than 64 ln 2 above m.
+    Sub-blocks are visited in ascending key order (selected blocks ascending, the causal keys
+    of each).  This returns a bool array [B, Hq, q_len]: True where some later sub-block's
+    maximum exceeds the first one's by more than 64 ln 2 + 1, which forces at least one
+    rescale of a non-empty accumulator (the first such sub-block triggers unless an earlier
+    one already did).  q: [B, Hq, T, D]; kp: [P, Hkv, bs, D]; idx: [B, Hkv, T, k]."""
+    B, Hq, T, D = q.shape
+    thr = 64.0 * math.log(2.0) + 1.0
+    res = np.zeros((B, Hq, T), bool)
+    for b in range(B):
+        L = kv[b]
+        nb = (L + page_size - 1) // page_size
+        pos = np.arange(L - T, L)
+        for g in range(Hq // group_size):
+            keys = kp[pt[b, :nb], g].reshape(nb * page_size, D)[:L].astype(np.float64)
+            selm = np.zeros((T, nb), bool)
+            for s in range(idx.shape[3]):
+                j = idx[b, g, :, s]
+                ok = j >= 0
+                selm[np.nonzero(ok)[0], j[ok]] = True
+            keep = np.repeat(selm, page_size, axis=1)[:, :L] & (np.arange(L)[None, :] <= pos[:, None])
+            nsub = (L + sub - 1) // sub
+            for h in range(g * group_size, (g + 1) * group_size):
+                z = (q[b, h].astype(np.float64) @ keys.T) * scale
+                z = np.where(keep, z, -np.inf)
+                zp = np.full((T, nsub * sub), -np.inf)
+                zp[:, :L] = z
+                m = zp.reshape(T, nsub, sub).max(-1)                     # [T, nsub]
+                fin = np.isfinite(m)
+                first = np.argmax(fin, axis=1)
+                m0 = m[np.arange(T), first]
+                later = np.where(np.arange(nsub)[None, :] > first[:, None], m, -np.inf).max(1)
+                res[b, h] = fin.any(1) & (later - m0 > thr)
+    return res

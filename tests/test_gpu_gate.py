@@ -1,5 +1,5 @@
 """GPU parity of the gated epilogue: out = g * A + (1 - g) * x ("Sparse Attention for
-Long-Context LLMs", section 5.5, step 6), with one gate per (head, query) row or per element.
+Long-Context LLMs", section 4.3, step 6), with one gate per (head, query) row or per element.
 
 The reference is the oracle's attention output A (float64) passed through the oracle's
 gated_fusion; lse must equal the ungated call's bit for bit (the gate does not touch it).

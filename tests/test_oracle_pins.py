@@ -429,7 +429,7 @@ def test_chunked_prefill_rows_equal_full_prefill_rows():
 
 
 # --------------------------------------------------------------------------
-# gated fusion (Long-Context page, section 5.5, step 6)
+# gated fusion (Long-Context page, section 4.3, step 6)
 # --------------------------------------------------------------------------
 def test_gated_fusion_hand_values():
     a = np.array([[1.0, 2.0], [3.0, 4.0]])
