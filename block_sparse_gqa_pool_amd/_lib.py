@@ -18,13 +18,14 @@ LIB_PATH = os.path.join(_PKG, "libbsg.so")
 
 BSG_F32, BSG_BF16 = 0, 1
 STATUS = {0: "BSG_OK", -1: "BSG_ERR_NULL", -2: "BSG_ERR_SHAPE", -3: "BSG_ERR_UNSUPPORTED",
-          -4: "BSG_ERR_WORKSPACE", -5: "BSG_ERR_HIP"}
+          -4: "BSG_ERR_WORKSPACE", -5: "BSG_ERR_HIP", -6: "BSG_ERR_SCRATCH"}
 
 # every symbol include/bsg.h declares
 EXPORTS = ("bsg_version", "bsg_status_str", "bsg_block_pool", "bsg_group_score", "bsg_topk_blocks",
            "bsg_group_score_topk_workspace_bytes", "bsg_group_score_topk", "bsg_sparse_attn_prefill",
            "bsg_sparse_attn_prefill_gated", "bsg_decode_workspace_bytes", "bsg_sparse_attn_decode",
            "bsg_decode_step_workspace_bytes", "bsg_decode_step", "bsg_decode_step_gated",
+           "bsg_noalloc_scratch_bytes", "bsg_decode_step_noalloc",
            "bsg_quantize_pages_fp8", "bsg_block_pool_fp8", "bsg_decode_step_fp8",
            "bsg_token_topk_workspace_bytes", "bsg_token_topk", "bsg_decode_tokens_workspace_bytes",
            "bsg_sparse_attn_decode_tokens", "bsg_decode_step_tokens_workspace_bytes", "bsg_decode_step_tokens")
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
             "bsg_decode_step": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, vp, vp], ctypes.c_int),
             "bsg_decode_step_gated": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, i32, vp, vp, vp, vp],
                                       ctypes.c_int),
+            "bsg_noalloc_scratch_bytes": ([], sz),
+            "bsg_decode_step_noalloc": ([dp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp], ctypes.c_int),
             "bsg_quantize_pages_fp8": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "bsg_block_pool_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "bsg_decode_step_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp, vp, vp],
@@ -416,6 +419,42 @@ def decode_step_gated(q, kv_lens, block_cache, k_cache, v_cache, page_table, sca
         ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(block_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         float(scale), _ptr(block_idx), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(gate),
         per_dim, _ptr(x), _ptr(out), _ptr(lse), _stream(stream)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static device scratch that bsg_decode_step_noalloc uses (per GPU)."""
+    return int(lib().bsg_noalloc_scratch_bytes())
+
+
+def decode_step_noalloc(q, kv_lens, block_cache, k_cache, v_cache, page_table, scale: float, block_idx, out,
+                        lse=None, stream=None):
+    """bsg_decode_step_noalloc: bsg_decode_step with the library's static scratch as workspace
+    (nothing is allocated; calls that overlap in time on one GPU race)."""
+    _req(k_cache, "k_cache", None, 4)
+    dev = k_cache.device
+    _req(v_cache, "v_cache", k_cache.dtype, 4, dev)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    _req(block_cache, "block_cache", k_cache.dtype, 3, dev)
+    P, Hkv, bs, D = k_cache.shape
+    if tuple(block_cache.shape) != (P, Hkv, D):
+        raise ValueError("block_cache must be [num_pages, Hkv, D]")
+    _req(q, "q", k_cache.dtype, 3, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(block_idx, "block_idx", torch.int32, 3, dev)
+    _req(out, "out", k_cache.dtype, 3, dev)
+    B, Hq, D2 = q.shape
+    if out.shape != q.shape or D2 != D or page_table.shape[0] != B or tuple(block_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("shape mismatch between q, out, caches, page_table and block_idx")
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 2, dev)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
+    d = dims(k_cache, page_table, Hq, block_idx.shape[2])
+    _check("bsg_decode_step_noalloc", lib().bsg_decode_step_noalloc(
+        ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(block_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        float(scale), _ptr(block_idx), _ptr(out), _ptr(lse), _stream(stream)))
     return out
 
 

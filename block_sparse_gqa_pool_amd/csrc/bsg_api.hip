@@ -39,6 +39,8 @@ const char* bsg_status_str(int status) {
     case BSG_ERR_UNSUPPORTED: return "BSG_ERR_UNSUPPORTED: dtype, head_dim, page_size or top_k not supported";
     case BSG_ERR_WORKSPACE: return "BSG_ERR_WORKSPACE: workspace missing or too small";
     case BSG_ERR_HIP: return "BSG_ERR_HIP: the HIP runtime reported an error";
+    case BSG_ERR_SCRATCH:
+      return "BSG_ERR_SCRATCH: these sizes need more workspace than the library's static scratch holds";
     default: return "unknown bsg status";
   }
 }

@@ -65,7 +65,9 @@ typedef enum {
   BSG_ERR_SHAPE = -2,       /* inconsistent or non-positive sizes */
   BSG_ERR_UNSUPPORTED = -3, /* valid but not implemented (dtype, D, page size, k) */
   BSG_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
-  BSG_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+  BSG_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
+  BSG_ERR_SCRATCH = -6      /* the sizes need more than the library's static scratch
+                               (bsg_decode_step_noalloc only) */
 } bsg_status;
 
 typedef enum { BSG_F32 = 0, BSG_BF16 = 1 } bsg_dtype;
@@ -245,6 +247,24 @@ int bsg_decode_step_gated(const bsg_dims* dims, const void* q, const int32_t* kv
                           const int32_t* page_table, float scale, int32_t* block_idx, void* workspace,
                           size_t workspace_bytes, const float* gate, int32_t gate_per_dim, const void* x,
                           void* out, float* lse, void* stream);
+
+/*
+ * bsg_decode_step_noalloc -- bsg_decode_step without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array of the library,
+ * BSG_NOALLOC_SCRATCH_BYTES bytes per GPU, held until the process ends; the call allocates
+ * nothing.  Same arguments, results and validation as bsg_decode_step; if the sizes need more
+ * workspace than the array holds (bsg_decode_step_workspace_bytes(dims) >
+ * bsg_noalloc_scratch_bytes()) it returns BSG_ERR_SCRATCH and enqueues nothing.  All calls
+ * on one GPU share that GPU's array: calls that overlap in time on one GPU (other streams,
+ * other host threads) race and must not be issued; calls in order on one stream are safe.
+ */
+#define BSG_NOALLOC_SCRATCH_BYTES (8u << 20)
+size_t bsg_noalloc_scratch_bytes(void);
+int bsg_decode_step_noalloc(const bsg_dims* dims, const void* q, const int32_t* kv_lens,
+                            const void* block_cache, const void* k_cache, const void* v_cache,
+                            const int32_t* page_table, float scale, int32_t* block_idx, void* out,
+                            float* lse, void* stream);
 
 /*
  * fp8 KV cache and block cache.  The pages list KV-cache quantisation among the
