@@ -592,13 +592,11 @@ def cpu_baseline_decode(spec, seed, n_sample=8, n_steps=5):
 TRAFFIC_KERNELS = {
     # key: (kernel-name substring, source files, workload); the fp8 instantiations carry F8 = true
     "sparse_attn_prefill_s131072": ("attn_prefill_mfma", ["attn_prefill.hip"], "prefill_bf16_s131072"),
-    "decode_attn_b32_ctx131072": ("attn_decode_mfma_kernel<128, 64, true, false>", ["attn_decode.hip"],
+    "decode_unit_b32_ctx131072": ("decode_unit_kernel<128, 64, false>", ["attn_decode.hip", "decode_prologue.h"],
                                   "decode_bf16_b32_ctx131072"),
-    "decode_scan_b32_ctx131072": ("decode_score_chunk_kernel<128, false>", ["decode_select.hip"],
-                                  "decode_bf16_b32_ctx131072"),
-    "decode_fp8_attn_b32_ctx131072": ("attn_decode_mfma_kernel<128, 64, true, true>", ["attn_decode.hip"],
-                                      "decode_bf16_b32_ctx131072 in fp8"),
-    "decode_fp8_scan_b32_ctx131072": ("decode_score_chunk_kernel<128, true>", ["decode_select.hip"],
+    "decode_merge_b32_ctx131072": ("attn_decode_merge_kernel<unsigned short, 128>", ["attn_decode.hip"],
+                                   "decode_bf16_b32_ctx131072 (bf16 and fp8 steps)"),
+    "decode_fp8_unit_b32_ctx131072": ("decode_unit_kernel<128, 64, true>", ["attn_decode.hip", "decode_prologue.h"],
                                       "decode_bf16_b32_ctx131072 in fp8"),
 }
 CALIB_BYTES = 1 << 30
@@ -799,18 +797,18 @@ def main():
         seed = SPECS.index(ds)
         warm = run_decode(ds, seed, dsteps, args.warmup)
         cold = run_decode(ds, seed, dsteps, args.warmup, rotate=4)
-        tr_a = _traffic("decode_attn_b32_ctx131072", ["attn_decode.hip"])
-        tr_s = _traffic("decode_scan_b32_ctx131072", ["decode_select.hip"])
-        line["decode"] = decode_line(ds, warm, "bsg_decode_step", (tr_a + tr_s) if (tr_a and tr_s) else None, cold)
+        tr_u = _traffic("decode_unit_b32_ctx131072", ["attn_decode.hip", "decode_prologue.h"])
+        tr_m = _traffic("decode_merge_b32_ctx131072", ["attn_decode.hip"])
+        line["decode"] = decode_line(ds, warm, "bsg_decode_step", (tr_u + tr_m) if (tr_u and tr_m) else None, cold)
         log(f"decode 128K x 32: warm {warm['us']['mean']:.1f} us, cold {cold['us']['mean']:.1f} us")
         if not args.no_cpu_baseline:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(ds, seed)
     if "fp8" in parts:
         ds = spec_by_name("decode_bf16_b32_ctx131072")
         d8 = run_decode(ds, SPECS.index(ds), dsteps, args.warmup, fp8=True)
-        tr_a8 = _traffic("decode_fp8_attn_b32_ctx131072", ["attn_decode.hip"])
-        tr_s8 = _traffic("decode_fp8_scan_b32_ctx131072", ["decode_select.hip"])
-        l8 = decode_line(ds, d8, "bsg_decode_step_fp8", (tr_a8 + tr_s8) if (tr_a8 and tr_s8) else None)
+        tr_u8 = _traffic("decode_fp8_unit_b32_ctx131072", ["attn_decode.hip", "decode_prologue.h"])
+        tr_m = _traffic("decode_merge_b32_ctx131072", ["attn_decode.hip"])
+        l8 = decode_line(ds, d8, "bsg_decode_step_fp8", (tr_u8 + tr_m) if (tr_u8 and tr_m) else None)
         l8["workload"] = ds.name + " (K, V and block cache in fp8 E4M3)"
         line["decode_fp8"] = l8
     if "decode1m" in parts:

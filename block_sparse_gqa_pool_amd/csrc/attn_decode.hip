@@ -847,6 +847,616 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// The decode step for page-table rows of at most DU_MAXC candidate blocks (bf16, G <= 16):
+// S workgroups ("members", S = 2 or 4 while every member still has a CU of its own, else 1)
+// per (sequence, group) unit, eight waves each.  Every member runs phases 1-2 in full (the
+// members of a unit sit on the same XCD, so the second reader of a block-cache line finds it
+// in that XCD's L2) and takes every S-th kept page in phase 3:
+//  0. the group-summed fp32 query (heads in order);
+//  1. scan: every candidate block's representative of this group (D bf16 = one 256-byte
+//     slice of the page's block-cache row) is dotted with the group-summed query, with the
+//     arithmetic of decode_score_chunk_kernel (same per-lane products, same DPP segment sums,
+//     so the same fp32 scores); the 64-bit (score, index) keys go to LDS;
+//  2. select: the top_k - 1 largest keys, exactly.  The maxima of 64 disjoint groups of keys
+//     bound the answer from below (the cnt-th largest group maximum has cnt keys at or above
+//     it), so only the keys at or above that bound survive, typically a few dozen; they are
+//     ranked against each other.  If more than DU_MAXS survive (keys piled into few groups),
+//     a radix select over all keys decides instead (11/11/10-bit digits of the score half,
+//     then of the index half).  The kept ids are sorted ascending and the own block appended
+//     (member 0 writes them to block_idx);
+//  3. attend: page e of the list (own block first) goes to member e % S, wave (e / S) % 8;
+//     per 64-key sub-block the layout of attn_decode_mfma_kernel (K straight from HBM as the
+//     A operand of v_mfma_f32_16x16x32_bf16, V through LDS with the transposing read), exact
+//     running maximum per sub-block;
+//  4. merge the eight waves' (max, sum, output) in LDS; with S = 1 write out, lse (and the
+//     gate), else the member's partial, which attn_decode_merge_kernel then merges.
+// F8: the caches hold OCP E4M3 codes with power-of-two scales per (page, head), taken as in
+// the fp8 paths of decode_score_chunk_kernel and attn_decode_mfma_kernel (the scale applied
+// to a representative's segment sum, to a page's scores, and to its weights before their
+// bf16 rounding), so the result equals the bf16 kernel on the decoded caches.
+// Measured on the 128K x 32 workload (128 units, S = 2): a merge in the last-arriving member
+// (an arrival counter plus one L2 write-back and one L2 invalidate per workgroup) cost more
+// than the second launch, so the merge stays a kernel of its own.
+namespace {
+constexpr int DU_WAVES = 8;
+constexpr int DU_NT = 64 * DU_WAVES;
+constexpr int DU_MAXC = 4096;                // candidate blocks per unit (keys in LDS)
+constexpr int DU_BINS = 2048;                // radix bins per digit (11 bits)
+constexpr int DU_MAXS = 1024;                // survivors ranked directly
+}  // namespace
+
+template <int D>
+static size_t decode_unit_smem_bytes() {
+  const size_t scan = (size_t)D * 4 + (size_t)DU_MAXC * 12 + (size_t)DU_BINS * 4 + (size_t)(DU_MAXS + 128) * 8;
+  const size_t stage = (size_t)DU_WAVES * 64 * (D + DM_VPAD) * 2;
+  const size_t merge = (size_t)DU_WAVES * 16 * (D + 2) * 4;
+  size_t m = scan > stage ? scan : stage;
+  return m > merge ? m : merge;
+}
+
+template <int D, int BS, bool F8>
+__global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const void* __restrict__ block_cache,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache, const int32_t* __restrict__ page_table,
+    float scale, int32_t* __restrict__ block_idx, bf16_t* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv,
+    int top_k, int num_pages, int pt_stride, gate_args ga, const float* __restrict__ rep_scales,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, int nunits, int S,
+    float* __restrict__ part) {
+  constexpr int ES = F8 ? 1 : 2;             // bytes per cache element
+  constexpr int VPP = F8 ? 16 : 8;           // values per 16-byte piece of a representative
+  constexpr int SEG = D / VPP;               // lanes per representative
+  constexpr int BPI = 64 / SEG;              // representatives per wave-wide load
+  constexpr int U = 64 / BPI;                // loads in flight per lane: one batch = 64 blocks
+  constexpr int NDS = D / 32;
+  constexpr int NDT = D / 16;
+  constexpr int VS = D + DM_VPAD;
+  constexpr int SUB = 64;
+  constexpr int NSP = BS / SUB;
+  constexpr int PPR = D / 8;
+  constexpr int NV = SUB * PPR / 64;
+  extern __shared__ __attribute__((aligned(16))) unsigned char du_smem[];
+  float* qs = reinterpret_cast<float*>(du_smem);                                   // [D]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(du_smem + D * 4);                   // [DU_MAXC]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(du_smem + D * 4 + DU_MAXC * 8);     // [DU_BINS]
+  int32_t* cpage = reinterpret_cast<int32_t*>(du_smem + D * 4 + DU_MAXC * 8 + DU_BINS * 4);   // [DU_MAXC]
+  uint64_t* gmax = reinterpret_cast<uint64_t*>(du_smem + D * 4 + DU_MAXC * 12 + DU_BINS * 4);   // [64]
+  uint64_t* surv = gmax + 128;                                                                    // [DU_MAXS]
+  __shared__ uint64_t tau_s;
+  __shared__ int wl[64];                       // kept blocks, ascending, own block last
+  __shared__ int wpg[64];                      // their physical pages
+  __shared__ int wsel[64];
+  __shared__ uint32_t red[DU_WAVES + 1];
+  __shared__ uint32_t sel_s[3];
+  __shared__ int counter_s;
+
+  // workgroup x serves unit ((x / 8S) * 8 + x % 8) as its member (x / 8) % S: the S members of
+  // a unit sit 8 apart in dispatch order, so on the same XCD (workgroups go to the eight XCDs
+  // in turn) and their block-cache reads meet in that XCD's L2
+  const int xw = blockIdx.x;
+  const int sm = (xw >> 3) % S;
+  const int unit = (xw / (8 * S)) * 8 + (xw & 7);
+  if (unit >= nunits) return;
+  const int g = unit % Hkv, b = unit / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = Hq / Hkv;
+  const int L = kv_lens[b];
+  const int pos = max(L - 1, 0);
+  const int own = pos / BS;
+  const int ncand = min(own, min(pt_stride, DU_MAXC));
+  const int m = top_k - 1;
+  const int cnt = min(m, ncand);
+  const int32_t* ptrow = page_table + (size_t)b * pt_stride;
+
+  // the scan's page ids (wave w takes blocks [w0, w1)) and the own block's page go out first,
+  // so that their round trip overlaps the query's
+  const int nper = ((ncand + DU_WAVES - 1) / DU_WAVES + 63) / 64 * 64;
+  const int w0 = wave * nper, w1 = min(w0 + nper, ncand);
+  constexpr int NPB = DU_MAXC / DU_WAVES / 64;
+  int pids[NPB];
+#pragma unroll
+  for (int c = 0; c < NPB; c++) {
+    const int jb = w0 + 64 * c + lane;
+    pids[c] = (cnt > 0 && jb < w1) ? clampi(ptrow[jb], 0, num_pages - 1) : 0;
+  }
+  const int own_page = clampi(ptrow[min(own, pt_stride - 1)], 0, num_pages - 1);
+  // ---- 0. group-summed query (fp32, heads in order): the group's G query rows with one
+  // 16-byte load per thread, parked in LDS as floats, then summed
+  float* qf = reinterpret_cast<float*>(du_smem + D * 4 + DU_MAXC * 8);   // [G][D] (the histogram area)
+  {
+    const int nq = G * (D / 8);
+    uint4 qv4 = make_uint4(0, 0, 0, 0);
+    if (tid < nq) qv4 = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + g * G) * D + 8 * tid);
+    if (tid < nq) {
+      const uint32_t wd[4] = {qv4.x, qv4.y, qv4.z, qv4.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        qf[8 * tid + 2 * i] = __uint_as_float(wd[i] << 16);
+        qf[8 * tid + 2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+      }
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += DU_NT) {
+      float s = 0.0f;
+      for (int h = 0; h < G; h++) s += qf[h * D + d];
+      qs[d] = s;
+    }
+    __syncthreads();
+  }
+
+  // ---- 1. scan: wave w takes blocks [w0, w1), 64 per batch (BPI per load, U loads in flight)
+  if (cnt > 0) {
+    const int piece = lane % SEG, sg = lane / SEG;
+    float qv[VPP];
+#pragma unroll
+    for (int i = 0; i < VPP; i++) qv[i] = qs[piece * VPP + i];
+    const char* bc = reinterpret_cast<const char*>(block_cache) + (size_t)g * D * ES + piece * 16;
+    // the page ids of the wave's range (up to DU_MAXC / DU_WAVES blocks: 8 per lane) are kept
+    // in LDS beside the keys for the attention phase
+#pragma unroll
+    for (int c = 0; c < NPB; c++) {
+      const int jb = w0 + 64 * c + lane;
+      if (jb < w1) cpage[jb] = pids[c];
+    }
+    // row loads of batch c (64 blocks, U per lane)
+    uint4 raw[2][U];
+    float scl[2][U];                                      // F8: the representative's scale
+    auto issue_rows = [&](int c, uint4 (&rw)[U], float (&sc)[U]) {
+      const int base = w0 + 64 * c;
+      int pid = 0;
+#pragma unroll
+      for (int c2 = 0; c2 < NPB; c2++)
+        if (c2 == c) pid = pids[c2];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int jl = u * BPI + sg;                      // block of this lane, relative to base
+        const int p = __shfl(pid, jl, 64);
+        rw[u] = base + jl < w1 ? *reinterpret_cast<const uint4*>(bc + (size_t)p * Hkv * D * ES)
+                               : make_uint4(0, 0, 0, 0);
+        if (F8) sc[u] = (base + jl < w1 && piece == 0) ? rep_scales[(size_t)p * Hkv + g] : 0.0f;
+      }
+    };
+    const int nbat = (w1 - w0 + 63) / 64;
+    if (nbat > 0) issue_rows(0, raw[0], scl[0]);
+#pragma unroll
+    for (int c = 0; c < NPB; c++) {
+      if (c >= nbat) break;
+      if (c + 1 < nbat) issue_rows(c + 1, raw[(c + 1) & 1], scl[(c + 1) & 1]);
+      const int base = w0 + 64 * c;
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int jb = base + u * BPI + sg;
+        const uint4 rr = raw[c & 1][u];
+        const uint32_t wd[4] = {rr.x, rr.y, rr.z, rr.w};
+        float s = 0.0f;
+        if constexpr (F8) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], true);
+            s = fmaf(qv[4 * i], lo[0], s);
+            s = fmaf(qv[4 * i + 1], lo[1], s);
+            s = fmaf(qv[4 * i + 2], hi[0], s);
+            s = fmaf(qv[4 * i + 3], hi[1], s);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            s = fmaf(qv[2 * i], __uint_as_float(wd[i] << 16), s);
+            s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
+          }
+        }
+        s = seg_sum_dpp<SEG>(s);
+        if (F8) s *= scl[c & 1][u];
+        if (piece == 0 && jb < w1) keys[jb] = sel_key(s, jb);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. select the cnt largest keys (distinct: the low half holds the block index)
+  bool ranked = false;                                      // workgroup-uniform
+  if (cnt > 0) {
+    // lower bound tau: the cnt-th largest of 64 group maxima.  The groups are disjoint sets of
+    // keys: with ncand >= DU_NT, thread t takes keys t, t + DU_NT, ... and a group is 8
+    // consecutive threads; with fewer keys, group l takes keys l, l + 64, ...  At least
+    // min(64, ncand) >= cnt groups are non-empty, so at least cnt keys are >= tau.
+    auto shfl_xor64 = [](uint64_t v, int o) {
+      return ((uint64_t)(uint32_t)__shfl_xor((int)(v >> 32), o, 64) << 32) |
+             (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)v, o, 64);
+    };
+    if (ncand >= DU_NT) {
+      uint64_t mx = 0;                                      // 0 is below every real key
+      for (int e = tid; e < ncand; e += DU_NT) mx = max(mx, keys[e]);
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) mx = max(mx, shfl_xor64(mx, o));
+      if ((lane & 7) == 0) gmax[tid >> 3] = mx;
+    } else if (wave == 0) {
+      uint64_t mx = 0;
+      for (int e = lane; e < ncand; e += 64) mx = max(mx, keys[e]);
+      gmax[lane] = mx;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint64_t gm = gmax[lane];
+      const ulonglong2* g2 = reinterpret_cast<const ulonglong2*>(gmax);
+      int rank = 0;
+#pragma unroll 8
+      for (int i = 0; i < 32; i++) {
+        const ulonglong2 v = g2[i];
+        rank += (v.x > gm ? 1 : 0) + (v.y > gm ? 1 : 0);
+      }
+      // the real maxima are distinct; empty groups (0) rank last
+      if (gm != 0ull && rank == cnt - 1) tau_s = gm;
+      if (lane == 0) counter_s = 0;
+    }
+    __syncthreads();
+    const uint64_t tau = tau_s;
+    for (int e = tid; e < ncand; e += DU_NT) {
+      const uint64_t k = keys[e];
+      if (k >= tau) {
+        const int at = atomicAdd(&counter_s, 1);
+        if (at < DU_MAXS) surv[at] = k;
+      }
+    }
+    __syncthreads();
+    const int ns = counter_s;
+    if (ns <= DU_MAXS) {
+      const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(surv);
+      for (int e = tid; e < ns; e += DU_NT) {
+        const uint64_t k = surv[e];
+        int rank = 0;
+#pragma unroll 4
+        for (int i = 0; i < ns / 2; i++) {
+          const ulonglong2 v = s2[i];
+          rank += (v.x > k ? 1 : 0) + (v.y > k ? 1 : 0);
+        }
+        if (ns & 1) rank += surv[ns - 1] > k ? 1 : 0;
+        if (rank < cnt) wsel[rank] = sel_key_index(k);
+      }
+      ranked = true;
+    }
+    __syncthreads();
+  }
+  if (cnt > 0 && !ranked) {
+    uint64_t prefix = 0, pmask = 0;
+    uint32_t above = 0;
+    bool done = false;
+    for (int lv = 0; lv < 6 && !done; lv++) {
+      const int shift = lv == 0 ? 53 : lv == 1 ? 42 : lv == 2 ? 32 : lv == 3 ? 21 : lv == 4 ? 10 : 0;
+      const int nbits = (lv == 2 || lv == 5) ? 10 : 11;
+      const uint32_t dmask = (1u << nbits) - 1u;
+      for (int i = tid; i < DU_BINS; i += DU_NT) hist[i] = 0u;
+      __syncthreads();
+      for (int e = tid; e < ncand; e += DU_NT) {
+        const uint64_t k = keys[e];
+        if ((k & pmask) == prefix) atomicAdd(&hist[(uint32_t)(k >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      // bins from the top: this thread sums `per` consecutive bins, then a block scan
+      const uint32_t need = (uint32_t)cnt - above;
+      const int nb = 1 << nbits;
+      const int per = nb / DU_NT;
+      uint32_t mine = 0;
+      for (int k = 0; k < per; k++) mine += hist[nb - 1 - (tid * per + k)];
+      uint32_t incl = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      if (lane == 63) red[wave] = incl;
+      __syncthreads();
+      uint32_t before = incl - mine;
+      for (int w2 = 0; w2 < wave; w2++) before += red[w2];
+      uint32_t run = before;
+      for (int k = 0; k < per; k++) {
+        const int bin = nb - 1 - (tid * per + k);
+        const uint32_t h = hist[bin];
+        if (run < need && need <= run + h) {
+          sel_s[0] = (uint32_t)bin;
+          sel_s[1] = run;
+          sel_s[2] = h;
+        }
+        run += h;
+      }
+      __syncthreads();
+      prefix |= (uint64_t)sel_s[0] << shift;
+      pmask |= (uint64_t)dmask << shift;
+      above += sel_s[1];
+      done = above + sel_s[2] == (uint32_t)cnt;
+      __syncthreads();
+    }
+    // the kept keys are those whose masked top bits are >= prefix (exactly cnt of them)
+    if (tid == 0) counter_s = 0;
+    __syncthreads();
+    for (int e = tid; e < ncand; e += DU_NT) {
+      const uint64_t k = keys[e];
+      if ((k & pmask) >= prefix) {
+        const int at = atomicAdd(&counter_s, 1);
+        if (at < 64) wsel[at] = sel_key_index(k);
+      }
+    }
+    __syncthreads();
+  }
+  if (cnt > 0) {
+    if (tid < cnt) {                                         // ascending
+      const int ji = wsel[tid];
+      int r2 = 0;
+      for (int i = 0; i < cnt; i++) r2 += wsel[i] < ji ? 1 : 0;
+      wl[r2] = ji;
+    }
+  }
+  if (tid == 0) wl[cnt] = own;
+  __syncthreads();
+  if (sm == 0 && tid < top_k) block_idx[((size_t)b * Hkv + g) * top_k + tid] = tid <= cnt ? wl[tid] : -1;
+  // pages in the attention order: the own block first (its page from the table), then the
+  // kept blocks ascending (their pages from the scan)
+  if (tid <= cnt) {
+    const int jb = tid == 0 ? own : wl[tid - 1];
+    wpg[tid] = tid == 0 ? own_page : cpage[jb];
+  }
+  __syncthreads();
+
+  // ---- 3. attention over the kept pages, page e on member e % S, wave (e / S) % DU_WAVES
+  const int n = lane & 15, qd = lane >> 4;
+  bf16_t* Vs = reinterpret_cast<bf16_t*>(du_smem) + (size_t)wave * SUB * VS;
+  const float c2 = scale * 1.4426950408889634f;
+  bf16x8_t qb[NDS];
+  {
+    const bool hv = n < G;
+    const bf16_t* qp = q + ((size_t)b * Hq + (size_t)g * G + (hv ? n : 0)) * D + 8 * qd;
+#pragma unroll
+    for (int s = 0; s < NDS; s++) {
+      uint4 v = hv ? *reinterpret_cast<const uint4*>(qp + 32 * s) : make_uint4(0, 0, 0, 0);
+      qb[s] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; i++) o[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int vtr = (4 * qd + ((lane & 15) >> 2)) * VS + 4 * (lane & 3);
+  const int npages = cnt + 1;
+  for (int e = wave * S + sm; e < npages; e += DU_WAVES * S) {
+    const int jj = e == 0 ? own : wl[e - 1];
+    const int p = wpg[e];
+    const int nk = clampi(pos - jj * BS + 1, 0, BS);
+    const char* kpg = reinterpret_cast<const char*>(k_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
+    const char* vpg = reinterpret_cast<const char*>(v_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
+    const float skp = F8 ? k_scales[(size_t)p * Hkv + g] : 1.0f;
+    const float svp = F8 ? v_scales[(size_t)p * Hkv + g] : 1.0f;
+#pragma unroll
+    for (int h2 = 0; h2 < NSP; h2++) {
+      const int kb = h2 * SUB;
+      if (kb >= nk) break;
+      // every K and V load of the sub-block goes out before its first product
+      uint4 rv[F8 ? 1 : NV];
+      uint2 rv8[F8 ? NV : 1];
+      uint4 rk[F8 ? 1 : SUB / 16][NDS];
+      uint2 rk8[F8 ? SUB / 16 : 1][NDS];
+#pragma unroll
+      for (int i = 0; i < NV; i++) {
+        const int pc = i * 64 + lane;
+        const int r = pc / PPR, c = pc % PPR;
+        const char* src = vpg + ((size_t)(kb + r) * D + 8 * c) * ES;
+        if constexpr (F8) rv8[i] = *reinterpret_cast<const uint2*>(src);
+        else rv[i] = *reinterpret_cast<const uint4*>(src);
+      }
+#pragma unroll
+      for (int T = 0; T < SUB / 16; T++) {
+        const char* kr = kpg + ((size_t)(kb + 16 * T + n) * D + 8 * qd) * ES;
+#pragma unroll
+        for (int s2 = 0; s2 < NDS; s2++) {
+          if constexpr (F8) rk8[T][s2] = *reinterpret_cast<const uint2*>(kr + 32 * s2);
+          else rk[T][s2] = *reinterpret_cast<const uint4*>(kr + 64 * s2);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4_t sacc[SUB / 16];
+#pragma unroll
+      for (int T = 0; T < SUB / 16; T++) {
+        sacc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s2 = 0; s2 < NDS; s2++) {
+          bf16x8_t ka;
+          if constexpr (F8) ka = e4m3x8_to_bf16(rk8[T][s2]);
+          else ka = *reinterpret_cast<const bf16x8_t*>(&rk[T][s2]);
+          sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s2], sacc[T], 0, 0, 0);
+        }
+        if constexpr (F8) sacc[T] *= skp;
+      }
+#pragma unroll
+      for (int i = 0; i < NV; i++) {           // V rows past nk (inside the page) are zeroed
+        const int pc = i * 64 + lane;
+        const int r = pc / PPR, c = pc % PPR;
+        const bool ok = kb + r < nk;
+        if constexpr (F8) {
+          const bf16x8_t v = e4m3x8_to_bf16(ok ? rv8[i] : make_uint2(0, 0));
+          *reinterpret_cast<bf16x8_t*>(Vs + r * VS + 8 * c) = v;
+        } else {
+          *reinterpret_cast<uint4*>(Vs + r * VS + 8 * c) = ok ? rv[i] : make_uint4(0, 0, 0, 0);
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < SUB / 16; T++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int key = kb + 16 * T + 4 * qd + i;
+          const float sc = key < nk ? sacc[T][i] : -INFINITY;
+          sacc[T][i] = sc;
+          mx = fmaxf(mx, sc);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      m_run = m_new;
+      float rs = 0.0f;
+#pragma unroll
+      for (int T = 0; T < SUB / 16; T++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float pe = __builtin_amdgcn_exp2f((sacc[T][i] - m_use) * c2);
+          sacc[T][i] = pe;
+          rs += pe;
+        }
+      l_run = l_run * alpha + rs;
+#pragma unroll
+      for (int i = 0; i < NDT; i++) o[i] *= alpha;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int k2 = 0; k2 < SUB / 32; k2++) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          pb[i] = (__bf16)(F8 ? sacc[2 * k2][i] * svp : sacc[2 * k2][i]);
+          pb[4 + i] = (__bf16)(F8 ? sacc[2 * k2 + 1][i] * svp : sacc[2 * k2 + 1][i]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+          const bf16_t* vb = Vs + vtr + (32 * k2) * VS + 16 * dt;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dm_lds_s16x4_ptr)(vb + 16 * VS));
+          bf16x8_t va;
+          *reinterpret_cast<s16x4_t*>(&va) = lo;
+          *(reinterpret_cast<s16x4_t*>(&va) + 1) = hi;
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[dt], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  float l_h = l_run + __shfl_xor(l_run, 16, 64);
+  l_h += __shfl_xor(l_h, 32, 64);
+
+  // ---- 4. merge the waves and write the output
+  __syncthreads();
+  float* mrg = reinterpret_cast<float*>(du_smem);               // [DU_WAVES][16][D + 2]
+  {
+    float* mw = mrg + ((size_t)wave * 16 + n) * (D + 2);
+    if (qd == 0) {
+      mw[0] = m_run;
+      mw[1] = l_h;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mw[2 + 16 * dt + 4 * qd + i] = o[dt][i];
+  }
+  __syncthreads();
+  float* myp = part + ((size_t)unit * S + sm) * G * (D + 2);
+  for (int e2 = tid; e2 < G * D; e2 += DU_NT) {
+    const int h = e2 / D, d = e2 % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < DU_WAVES; w++) mm = fmaxf(mm, mrg[((size_t)w * 16 + h) * (D + 2)]);
+    float ll = 0.0f, oo = 0.0f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < DU_WAVES; w++) {
+        const float* mw = mrg + ((size_t)w * 16 + h) * (D + 2);
+        if (mw[0] == -INFINITY) continue;
+        const float sc = __builtin_amdgcn_exp2f((mw[0] - mm) * c2);
+        ll += mw[1] * sc;
+        oo += mw[2 + d] * sc;
+      }
+    }
+    if (S > 1) {             // a partial in the layout attn_decode_merge_kernel reads
+      myp[h * (D + 2) + 2 + d] = oo;
+      if (d == 0) {
+        myp[h * (D + 2)] = mm == -INFINITY ? -INFINITY : mm * scale;   // natural-log units
+        myp[h * (D + 2) + 1] = ll;
+      }
+      continue;
+    }
+    const size_t row = (size_t)b * Hq + (size_t)g * G + h;
+    float a = oo * (ll > 0.0f ? 1.0f / ll : 0.0f);
+    if (ga.g) {                                        // out = g A + (1 - g) x, one rounding
+      const float gv = ga.per_dim ? ga.g[row * D + d] : ga.g[row];
+      a = gv * a + (1.0f - gv) * bf16_to_f32(static_cast<const bf16_t*>(ga.x)[row * D + d]);
+    }
+    out[row * D + d] = f32_to_bf16(a);
+    if (lse && d == 0) lse[row] = mm * scale + logf(ll);
+  }
+}
+
+static size_t decode_unit_smem(const bsg_dims& d) {
+  return d.head_dim == 128 ? decode_unit_smem_bytes<128>() : decode_unit_smem_bytes<64>();
+}
+
+bool decode_unit_supported(const bsg_dims& d) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  return d.dtype == BSG_BF16 && G <= 16 && d.pt_stride <= DU_MAXC && decode_unit_smem(d) <= 160 * 1024;
+}
+
+// workgroups per (sequence, group) unit: 2 or 4 while every member still gets a CU of its own
+static int decode_unit_members(const bsg_dims& d) {
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 256;
+  const long long units = (long long)d.batch * d.num_kv_heads;
+  const long long padded = (units + 7) / 8 * 8;
+  int S = 1;
+  while (S < 4 && padded * S * 2 <= ncu) S *= 2;
+  return S;
+}
+
+static size_t decode_unit_workspace_bytes(const bsg_dims& d) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  const int S = decode_unit_members(d);
+  return S > 1 ? (size_t)d.batch * d.num_kv_heads * S * G * (d.head_dim + 2) * sizeof(float) : 0;
+}
+
+static hipError_t launch_decode_unit(const bsg_dims& d, const void* q, const int32_t* kv_lens,
+                                     const void* block_cache, const void* k_cache, const void* v_cache,
+                                     const int32_t* page_table, float scale, int32_t* block_idx, void* out,
+                                     float* lse, hipStream_t stream, gate_args ga, const float* rep_scales,
+                                     const float* k_scales, const float* v_scales, float* part) {
+  const size_t smem = decode_unit_smem(d);
+  const bool f8 = k_scales != nullptr;
+  const int S = decode_unit_members(d);
+  const int nunits = d.batch * d.num_kv_heads;
+  dim3 grid((nunits + 7) / 8 * 8 * S);
+#define BSG_DU(DD, BB, F)                                                                                          \
+  do {                                                                                                              \
+    auto kfn = decode_unit_kernel<DD, BB, F>;                                                                       \
+    hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);   \
+    if (ea != hipSuccess) return ea;                                                                                \
+    hipLaunchKernelGGL(kfn, grid, dim3(DU_NT), smem, stream, (const bf16_t*)q, kv_lens, block_cache, k_cache,       \
+                       v_cache, page_table, scale, block_idx, (bf16_t*)out, lse, d.num_q_heads, d.num_kv_heads,     \
+                       d.top_k, d.num_pages, d.pt_stride, ga, rep_scales, k_scales, v_scales, nunits, S, part);    \
+  } while (0)
+#define BSG_DU_F(DD, BB)                 \
+  do {                                   \
+    if (f8) BSG_DU(DD, BB, true);        \
+    else BSG_DU(DD, BB, false);          \
+  } while (0)
+  if (d.head_dim == 128) {
+    if (d.page_size == 64) BSG_DU_F(128, 64); else BSG_DU_F(128, 128);
+  } else {
+    if (d.page_size == 64) BSG_DU_F(64, 64); else BSG_DU_F(64, 128);
+  }
+#undef BSG_DU_F
+#undef BSG_DU
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  dim3 mgrid(d.batch * d.num_q_heads);
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 128>), mgrid, dim3(128), 0, stream, part, (bf16_t*)out, lse,
+                       d.num_q_heads, d.num_kv_heads, S, ga);
+  else
+    hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
+                       d.num_q_heads, d.num_kv_heads, S, ga);
+  return hipGetLastError();
+}
+
 // LDS of the fused decode attention kernel: V staging, the wave merge, or the selection
 // prologue's lists plus its tops / survivors, whichever is largest.  lt: log2 of the
 // number of leading keys the prologue takes from every chunk list.
@@ -869,7 +1479,9 @@ bool decode_step_fused_supported(const bsg_dims& d) {
 size_t decode_step_workspace_bytes(const bsg_dims& d) {
   if (!decode_step_fused_supported(d)) return 0;
   const size_t a = (decode_select_workspace_bytes(d) + 255) / 256 * 256;
-  return a + decode_workspace_bytes(d);
+  const size_t w = decode_workspace_bytes(d);
+  const size_t u = decode_unit_supported(d) ? decode_unit_workspace_bytes(d) : 0;
+  return a + (w > u ? w : u);
 }
 
 hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
@@ -878,6 +1490,9 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
                               gate_args ga, const float* rep_scales, const float* k_scales, const float* v_scales) {
   const bool f8 = k_scales != nullptr;
   const size_t a = (decode_select_workspace_bytes(d) + 255) / 256 * 256;
+  if (decode_unit_supported(d))
+    return launch_decode_unit(d, q, kv_lens, block_cache, k_cache, v_cache, page_table, scale, block_idx, out, lse,
+                              stream, ga, rep_scales, k_scales, v_scales, (float*)((char*)workspace + a));
   uint64_t* lists = (uint64_t*)workspace;
   float* part = (float*)((char*)workspace + a);
   hipError_t e = launch_decode_score_chunks(d, q, kv_lens, block_cache, page_table, lists, stream, rep_scales);

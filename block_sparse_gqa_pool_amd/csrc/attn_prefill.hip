@@ -31,6 +31,7 @@ constexpr int PF_WAVES = 8;                 // waves per workgroup
 constexpr int PF_ROWS = 32 * PF_WAVES;      // query rows per workgroup (32 per wave)
 constexpr int PF_SUB = 64;                  // keys per staged sub-block
 constexpr int PF_MAX_STAGES = 4;            // depth of the LDS ring of K/V sub-blocks
+constexpr int PF_KW = 4;                    // K operand reads in flight ahead of the score product
 constexpr float LOG2E = 1.4426950408889634f;
 }  // namespace
 
@@ -70,8 +71,9 @@ __device__ __forceinline__ void wait_copies_barrier() {
 // Data movement and scheduling:
 //  * the union's blocks are streamed in 64-key sub-blocks through a ring of nst LDS stages
 //    (K and V tile each); the copies of sub-block i+nst-1 are issued straight from global
-//    memory into LDS (no register staging) right after the barrier of iteration i, so up to
-//    nst-1 sub-blocks are in flight while one is computed;
+//    memory into LDS (no register staging) at the end of iteration i, into the stage every
+//    wave released before that iteration's barrier, so up to nst-1 sub-blocks are in flight
+//    while one is computed;
 //  * a workgroup is 8 waves (256 query rows = 32 tokens x 8 heads for G = 8): the selections
 //    of neighbouring tokens overlap, so the union grows much slower than the row count and
 //    the K/V bytes fetched per query row drop with the tile size;
@@ -310,13 +312,34 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
       const unsigned char* sbp = pf_smem + r_stage * STG;
       f32x16_t sacc[2];
       const f32x16_t zero16 = {};
+      {
+        // Score product: the two 32-key chains interleaved (k-step outer), every K operand
+        // read PF_KW products ahead of its use, so that no product waits on a read issued
+        // just before it (the chains' accumulation order is unchanged).
+        constexpr int NK = 2 * NDS;
+        bf16x8_t kbuf[PF_KW];
 #pragma unroll
-      for (int kc = 0; kc < 2; kc++) {
+        for (int n = 0; n < PF_KW; n++)
+          kbuf[n] = *reinterpret_cast<const bf16x8_t*>(sbp + koff[n >> 1] + (n & 1) * 32 * D * 2);
 #pragma unroll
-        for (int ks = 0; ks < NDS; ks++) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sbp + koff[ks] + kc * 32 * D * 2);
+        for (int n = 0; n < NK; n++) {
+          const int ks = n >> 1, kc = n & 1;
+          const bf16x8_t a = kbuf[n % PF_KW];
           sacc[kc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], ks == 0 ? zero16 : sacc[kc], 0, 0, 0);
+          if (n + PF_KW < NK)
+            kbuf[n % PF_KW] =
+                *reinterpret_cast<const bf16x8_t*>(sbp + koff[(n + PF_KW) >> 1] + ((n + PF_KW) & 1) * 32 * D * 2);
         }
+        // schedule: PF_KW reads, then alternately one product and one read, then the rest
+#pragma unroll
+        for (int n = 0; n < PF_KW; n++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+#pragma unroll
+        for (int n = 0; n < NK - PF_KW; n++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int n = 0; n < PF_KW; n++) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
       if (__ballot(act && j == own) != 0) {             // causal mask inside the own block
         const int klim = j == own ? pos - kfirst : SUB - 1;

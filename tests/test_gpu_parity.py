@@ -463,3 +463,87 @@ def test_fused_selection_exact_ties(top_k):
     note(f"  rows checked {checked} of {ok.size}, exact ties at the boundary {ties}, mismatches {len(bad)}")
     assert len(bad) == 0, [(tuple(i), got[tuple(i)], ref[tuple(i)]) for i in bad[:3]]
     assert ties > 0 and checked > 0.9 * ok.size
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("case", [dict(), dict(page_size=128, top_k=9), dict(head_dim=64, top_k=8)])
+def test_decode_step_wide_page_table(case, fp8):
+    """Page-table rows longer than the one-workgroup step takes (4096 blocks) run the chunked
+    scan, selection-in-attention and merge kernels; the same sequences behind a wide table must
+    give the oracle's result (and, in fp8, the bf16 result on decoded caches bit for bit)."""
+    spec = SPECS[2].replace(**{"batch": 3, "ctx_len": 64 * 150 + 11, **case})
+    note(f"[case] decode step, wide page table {case} fp8={fp8}")
+    w = make_workload(spec, 27, tail_fill=float("nan")).to(DEV)
+    wide = torch.zeros(w.page_table.shape[0], 4200, dtype=torch.int32, device=DEV)
+    wide[:, :w.page_table.shape[1]] = w.page_table
+    B, Hq, _, D = w.q.shape
+    Hkv, k = spec.num_kv_heads, spec.top_k
+    scale = 1.0 / math.sqrt(D)
+    q1 = w.q[:, :, 0].contiguous()
+    cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=DEV)
+    bsg.block_pool(w.k_cache, wide, w.kv_lens, cache)
+    idx = torch.full((B, Hkv, k), -7, dtype=torch.int32, device=DEV)
+    out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+    if not fp8:
+        bsg.decode_step(q1, w.kv_lens, cache, w.k_cache, w.v_cache, wide, scale, idx, out, lse)
+        torch.cuda.synchronize()
+        check_decode(w, idx, out, lse)
+        return
+    P = w.k_cache.shape[0]
+    bs = spec.page_size
+    kc = torch.zeros(P, Hkv, bs, D, dtype=torch.uint8, device=DEV)
+    vc = torch.zeros_like(kc)
+    ks = torch.ones(P, Hkv, dtype=torch.float32, device=DEV)
+    vs = torch.ones_like(ks)
+    bsg.quantize_pages_fp8(w.k_cache, wide, w.kv_lens, kc, ks)
+    bsg.quantize_pages_fp8(w.v_cache, wide, w.kv_lens, vc, vs)
+    rc = torch.zeros(P, Hkv, D, dtype=torch.uint8, device=DEV)
+    rs = torch.ones(P, Hkv, dtype=torch.float32, device=DEV)
+    bsg.block_pool_fp8(kc, ks, wide, w.kv_lens, rc, rs)
+    bsg.decode_step_fp8(q1, w.kv_lens, rc, rs, kc, ks, vc, vs, wide, scale, idx, out, lse)
+
+    def dec(c, s):                     # code values times their (page, head) scale, exact in bf16
+        return (c.view(torch.float8_e4m3fn).float() * s.reshape(s.shape + (1,) * (c.dim() - 2))).to(torch.bfloat16)
+    kd, vd, rd = dec(kc, ks), dec(vc, vs), dec(rc, rs)
+    idx2 = torch.full_like(idx, -7)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    bsg.decode_step(q1, w.kv_lens, rd, kd, vd, wide, scale, idx2, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("nblk", [2000, 4000])
+def test_decode_step_selection_with_piled_keys(nblk):
+    """Representatives whose scores grow with the block index put every kept block in the last
+    groups of candidates, so many keys pass the one-workgroup step's lower bound: about 960
+    (ranked directly) at 2000 blocks, about 1900 (the radix select over all keys) at 4000.
+    Many scores tie exactly (bf16 representatives), and the lower index must win as in the
+    oracle."""
+    spec = SPECS[2].replace(batch=1, ctx_len=64 * nblk + 5, num_q_heads=16, num_kv_heads=2)
+    note(f"[case] decode step, piled keys, {nblk} blocks")
+    w = make_workload(spec, 29).to(DEV)
+    B, Hq, _, D = w.q.shape
+    Hkv, k, G = spec.num_kv_heads, spec.top_k, spec.group_size
+    q, kp, vp, pt, kv = np_inputs(w)
+    own = (kv[0] - 1) // 64
+    rep = np.zeros((kp.shape[0], Hkv, D), np.float32)
+    for g in range(Hkv):
+        u = np.sign(q[0, g * G:(g + 1) * G, 0].astype(np.float64).sum(0)).astype(np.float32)
+        for j in range(own):
+            rep[pt[0, j], g] = (j + 1) / own * u
+    rep = O.bf16_value(O.bf16_bits(rep)).astype(np.float32)
+    r = O.decode_reference(q, kp, vp, pt, kv, spec.page_size, k, "bf16", 1.0 / math.sqrt(D), block_cache=rep)
+    cache = torch.from_numpy(rep).to(torch.bfloat16).to(DEV)
+    idx = torch.full((B, Hkv, k), -7, dtype=torch.int32, device=DEV)
+    out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+    bsg.decode_step(w.q[:, :, 0].contiguous(), w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table,
+                    1.0 / math.sqrt(D), idx, out, lse)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), r["block_idx"][:, :, 0])
+    check_out(to_np(out), r["out"][:, :, 0], "bf16", "decode out")
+    assert np.abs(lse.cpu().numpy() - r["lse"][:, :, 0]).max() <= 2e-3
