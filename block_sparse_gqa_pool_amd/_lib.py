@@ -14,14 +14,15 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbsg.so")
+# BSG_LIBRARY selects another build of the library (the debug or the host-ASan variant)
+LIB_PATH = os.environ.get("BSG_LIBRARY") or os.path.join(_PKG, "libbsg.so")
 
 BSG_F32, BSG_BF16 = 0, 1
 STATUS = {0: "BSG_OK", -1: "BSG_ERR_NULL", -2: "BSG_ERR_SHAPE", -3: "BSG_ERR_UNSUPPORTED",
           -4: "BSG_ERR_WORKSPACE", -5: "BSG_ERR_HIP", -6: "BSG_ERR_SCRATCH"}
 
 # every symbol include/bsg.h declares
-EXPORTS = ("bsg_version", "bsg_status_str", "bsg_block_pool", "bsg_group_score", "bsg_topk_blocks",
+EXPORTS = ("bsg_version", "bsg_status_str", "bsg_debug_errors", "bsg_block_pool", "bsg_group_score", "bsg_topk_blocks",
            "bsg_group_score_topk_workspace_bytes", "bsg_group_score_topk", "bsg_sparse_attn_prefill",
            "bsg_sparse_attn_prefill_gated", "bsg_decode_workspace_bytes", "bsg_sparse_attn_decode",
            "bsg_decode_step_workspace_bytes", "bsg_decode_step", "bsg_decode_step_gated",
@@ -58,6 +59,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "bsg_version": ([], ctypes.c_int),
             "bsg_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "bsg_debug_errors": ([ctypes.POINTER(ctypes.c_uint32), ctypes.c_int], ctypes.c_int),
             "bsg_block_pool": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "bsg_group_score": ([dp, vp, i32, vp, vp, vp, vp, i32, vp], ctypes.c_int),
             "bsg_topk_blocks": ([dp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
@@ -420,6 +422,14 @@ def decode_step_gated(q, kv_lens, block_cache, k_cache, v_cache, page_table, sca
         float(scale), _ptr(block_idx), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(gate),
         per_dim, _ptr(x), _ptr(out), _ptr(lse), _stream(stream)))
     return out
+
+
+def debug_errors(reset: bool = True) -> int:
+    """Bits of the ids the kernels clamped since the last reset (a library built with
+    -DBSG_DEBUG only: 1 page id, 2 block id, 4 token id); raises on a release build."""
+    bits = ctypes.c_uint32(0)
+    _check("bsg_debug_errors", lib().bsg_debug_errors(ctypes.byref(bits), 1 if reset else 0))
+    return int(bits.value)
 
 
 def noalloc_scratch_bytes() -> int:

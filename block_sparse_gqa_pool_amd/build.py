@@ -1,16 +1,23 @@
 """Build the gfx950 shared library ``libbsg.so`` in-tree with hipcc.
 
-    python -m block_sparse_gqa_pool_amd.build [-v]
+    python -m block_sparse_gqa_pool_amd.build [-v] [--debug] [--asan] [--all]
 
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in parallel) and
 linked into ``block_sparse_gqa_pool_amd/libbsg.so``.  Packed fp32 VALU instructions are
-disabled for device code.
+disabled for device code.  Two more variants, each in its own object folder:
+
+* ``--debug``: ``libbsg_debug.so`` with ``-DBSG_DEBUG`` (kernels record the table ids they
+  clamp; ``bsg_debug_errors`` reads them back);
+* ``--asan``: ``libbsg_asan.so``, the host code built with AddressSanitizer (device code as
+  usual), for the host-side argument checks of the C layer on a machine without a GPU.  Load
+  it with the sanitizer runtime preloaded (``asan_runtime()``).
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
 import os
+import shlex
 import subprocess
 import sys
 
@@ -18,7 +25,6 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsg.so")
 ARCH = os.environ.get("BSG_OFFLOAD_ARCH", "gfx950")
 
@@ -41,19 +47,50 @@ def _run(cmd, verbose):
         print(msg)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+# variant: (library file, object folder, extra compile flags, extra link flags)
+VARIANTS = {
+    "release": ("libbsg.so", "_build", [], []),
+    "debug": ("libbsg_debug.so", "_build_debug", ["-DBSG_DEBUG"], []),
+    "asan": ("libbsg_asan.so", "_build_asan",
+             shlex.split("-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer"),
+             shlex.split("-Xarch_host -fsanitize=address -shared-libasan")),
+}
+
+
+def lib_path(variant: str = "release") -> str:
+    return os.path.join(PKG, VARIANTS[variant][0])
+
+
+def asan_runtime() -> str:
+    """The AddressSanitizer runtime of the ROCm clang that builds the asan variant."""
+    import glob as _glob
+    hits = sorted(_glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm/lib/clang")
+    return hits[-1]
+
+
+def build(verbose: bool = False, jobs: int = 8, variant: str = "release") -> str:
+    libname, objdir, cflags, lflags = VARIANTS[variant]
+    out_dir = os.path.join(PKG, objdir)
+    lib = os.path.join(PKG, libname)
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(OUT_DIR, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(out_dir, os.path.basename(s) + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        futs = [ex.submit(_run, [HIPCC, *FLAGS, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [HIPCC, *FLAGS, *cflags, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *lflags, *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    v = "-v" in sys.argv
+    chosen = [k for k, flag in (("debug", "--debug"), ("asan", "--asan")) if flag in sys.argv or "--all" in sys.argv]
+    if "--all" in sys.argv or not chosen:
+        chosen = ["release"] + chosen
+    for var in chosen:
+        print(build(verbose=v, variant=var))

@@ -54,8 +54,8 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
   for (int si = s0; si < s1; si++) {
     const int j = sl[si];
     if (j < 0) break;
-    const int jj = clampi(j, 0, pt_stride - 1);
-    const int p = clampi(page_table[(size_t)b * pt_stride + jj], 0, num_pages - 1);
+    const int jj = block_id(j, pt_stride);
+    const int p = page_id(page_table[(size_t)b * pt_stride + jj], num_pages);
     const int nk = max(0, min(BS, pos - jj * BS + 1));
     const T* kp = k_cache + (((size_t)p * Hkv + g) * BS) * D;
     const T* vp = v_cache + (((size_t)p * Hkv + g) * BS) * D;
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
   }
 #pragma unroll
   for (int t = 0; t < 2; t++)
-    pv[t] = jv[t] >= 0 ? page_table[(size_t)b * pt_stride + clampi(jv[t], 0, pt_stride - 1)] : 0;
+    pv[t] = jv[t] >= 0 ? page_table[(size_t)b * pt_stride + block_id(jv[t], pt_stride)] : 0;
   constexpr int ES = F8 ? 1 : 2;                        // bytes per K/V element
   constexpr int NSP = BS / SUB;                         // sub-blocks per page
   constexpr int PPR = D / 8;                            // 8-element pieces per row
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     const int jj = clampi(jv[t], 0, pt_stride - 1);
-    const int p = clampi(pv[t], 0, num_pages - 1);
+    const int p = page_id(pv[t], num_pages);
     nkp[t] = jv[t] >= 0 ? clampi(pos - jj * BS + 1, 0, BS) : 0;
     kpg[t] = reinterpret_cast<const char*>(k_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
     vpg[t] = reinterpret_cast<const char*>(v_cache) + (((size_t)p * Hkv + g) * BS) * D * ES;
@@ -533,8 +533,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
   }
 #pragma unroll
   for (int t = 0; t < 2; t++) {
-    const int pid = tok[t] >= 0 ? clampi(page_table[(size_t)b * pt_stride + min(tok[t] / BS, pt_stride - 1)], 0,
-                                         num_pages - 1)
+    dbg_flag(tok[t] >= pt_stride * BS, DBG_TOKEN_ID);
+    const int pid = tok[t] >= 0 ? page_id(page_table[(size_t)b * pt_stride + min(tok[t] / BS, pt_stride - 1)],
+                                          num_pages)
                                 : 0;
     rb[t] = tok[t] >= 0 ? ((((long long)pid * Hkv + g) * BS + tok[t] % BS) * D) : 0;
   }
@@ -957,9 +958,9 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
 #pragma unroll
   for (int c = 0; c < NPB; c++) {
     const int jb = w0 + 64 * c + lane;
-    pids[c] = (cnt > 0 && jb < w1) ? clampi(ptrow[jb], 0, num_pages - 1) : 0;
+    pids[c] = (cnt > 0 && jb < w1) ? page_id(ptrow[jb], num_pages) : 0;
   }
-  const int own_page = clampi(ptrow[min(own, pt_stride - 1)], 0, num_pages - 1);
+  const int own_page = page_id(ptrow[min(own, pt_stride - 1)], num_pages);
   // ---- 0. group-summed query (fp32, heads in order): the group's G query rows with one
   // 16-byte load per thread, parked in LDS as floats, then summed
   float* qf = reinterpret_cast<float*>(du_smem + D * 4 + DU_MAXC * 8);   // [G][D] (the histogram area)
@@ -1535,5 +1536,7 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
                        d.num_q_heads, d.num_kv_heads, nwg, ga);
   return hipGetLastError();
 }
+
+BSG_DEBUG_FILE(attn_decode)
 
 }  // namespace bsg

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
     const int t = t0 + tt;
     int j = -1;
     if (t < q_len) j = block_idx[(((size_t)b * Hkv + g) * q_len + t) * top_k + s];
-    sel[e] = (j >= 0 && j < pt_stride) ? j : (j >= pt_stride ? pt_stride - 1 : -1);
+    sel[e] = j >= 0 ? block_id(j, pt_stride) : -1;
   }
   for (int w = tid; w < nbw; w += NT) bitmap[w] = 0u;
   __syncthreads();
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
         bits &= bits - 1;
         const int j = (w << 5) + bit;
         ulist[off] = j;
-        upage[off] = clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1);
+        upage[off] = page_id(page_table[(size_t)b * pt_stride + j], num_pages);
         off++;
       }
     }
@@ -482,8 +482,8 @@ __global__ __launch_bounds__(256) void attn_prefill_valu_kernel(
   for (int s = 0; s < top_k; s++) {
     const int j = sl[s];
     if (j < 0) break;
-    const int jj = clampi(j, 0, pt_stride - 1);
-    const int p = clampi(page_table[(size_t)b * pt_stride + jj], 0, num_pages - 1);
+    const int jj = block_id(j, pt_stride);
+    const int p = page_id(page_table[(size_t)b * pt_stride + jj], num_pages);
     const int nk = min(bs, pos - jj * bs + 1);
     const T* kp = k_cache + (((size_t)p * Hkv + g) * bs) * D;
     const T* vp = v_cache + (((size_t)p * Hkv + g) * bs) * D;
@@ -578,5 +578,7 @@ hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, cons
 #undef BSG_PV
   return hipGetLastError();
 }
+
+BSG_DEBUG_FILE(attn_prefill)
 
 }  // namespace bsg

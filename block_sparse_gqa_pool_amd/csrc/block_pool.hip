@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
     const int u = w % units;
     const int g = u / (D / N);
     const int d0 = (u % (D / N)) * N;
-    const int p = clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1);
+    const int p = page_id(page_table[(size_t)b * pt_stride + j], num_pages);
     const T* src = k_cache + (((size_t)p * Hkv + g) * BS) * D + d0;
     float acc[N];
 #pragma unroll
@@ -103,5 +103,7 @@ hipError_t launch_block_pool(const bsg_dims& d, const void* k_cache, const int32
 #undef BSG_BP
   return hipGetLastError();
 }
+
+BSG_DEBUG_FILE(block_pool)
 
 }  // namespace bsg

@@ -31,6 +31,28 @@ extern "C" {
 
 int bsg_version(void) { return 10000; }
 
+int bsg_debug_errors(unsigned int* bits, int reset) {
+  if (!bits) return BSG_ERR_NULL;
+#ifdef BSG_DEBUG
+  int (*const fetch[])(unsigned*, int) = {bsg::dbg_fetch_attn_decode,   bsg::dbg_fetch_attn_prefill,
+                                          bsg::dbg_fetch_block_pool,    bsg::dbg_fetch_decode_select,
+                                          bsg::dbg_fetch_fp8_cache,     bsg::dbg_fetch_group_score,
+                                          bsg::dbg_fetch_score_topk_fused, bsg::dbg_fetch_token_select};
+  unsigned all = 0;
+  for (auto f : fetch) {
+    unsigned w = 0;
+    if (f(&w, reset)) return BSG_ERR_HIP;
+    all |= w;
+  }
+  *bits = all;
+  return BSG_OK;
+#else
+  (void)reset;
+  *bits = 0;
+  return BSG_ERR_UNSUPPORTED;
+#endif
+}
+
 const char* bsg_status_str(int status) {
   switch (status) {
     case BSG_OK: return "BSG_OK";

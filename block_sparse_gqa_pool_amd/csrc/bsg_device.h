@@ -61,6 +61,34 @@ __device__ __forceinline__ int sel_key_index(uint64_t key) { return (int)(0xffff
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Ids read from the caller's tables are clamped into range before they address memory, so a
+// bad entry never leads a kernel out of its buffers.  Debug builds (-DBSG_DEBUG) also record
+// each clamped id as a bit of a device word (one per source file, the file's kernels being
+// compiled apart), which bsg_debug_errors() reads back; release builds only clamp.
+enum : unsigned { DBG_PAGE_ID = 1u, DBG_BLOCK_ID = 2u, DBG_TOKEN_ID = 4u };
+#ifdef BSG_DEBUG
+[[maybe_unused]] static __device__ unsigned int dbg_word;
+#endif
+__device__ __forceinline__ void dbg_flag(bool bad, unsigned bit) {
+#ifdef BSG_DEBUG
+  if (bad) atomicOr(&dbg_word, bit);
+#else
+  (void)bad;
+  (void)bit;
+#endif
+}
+// physical page id from a page table: [0, num_pages)
+__device__ __forceinline__ int page_id(int p, int num_pages) {
+  dbg_flag(p < 0 || p >= num_pages, DBG_PAGE_ID);
+  return clampi(p, 0, num_pages - 1);
+}
+// logical block id from a selection (>= 0 here; -1 padding is handled by the caller): below
+// pt_stride
+__device__ __forceinline__ int block_id(int j, int pt_stride) {
+  dbg_flag(j < 0 || j >= pt_stride, DBG_BLOCK_ID);
+  return clampi(j, 0, pt_stride - 1);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll
@@ -88,5 +116,41 @@ __device__ __forceinline__ float seg_sum_dpp(float v) {
   if (SEG >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // mirror
   return v;
 }
+
+// Ascending bitonic sort of N (a power of two) ints held in registers: every index is a
+// compile-time constant once the loops unroll (a rank count over N x N pairs would not
+// unroll at N = 64 and would move the array to scratch).
+template <int N>
+__device__ __forceinline__ void sort_ints_asc(int (&v)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; i++) {
+        const int l = i ^ j;
+        if (l > i) {
+          const int x = v[i], y = v[l];
+          const bool up = (i & k) == 0;
+          v[i] = up ? min(x, y) : max(x, y);
+          v[l] = up ? max(x, y) : min(x, y);
+        }
+      }
+}
+
+// Host side of the debug word of the file that expands this (once, at namespace scope):
+// reads it and, with reset, clears it.  Synchronous.
+#ifdef BSG_DEBUG
+#define BSG_DEBUG_FILE(name)                                                                    \
+  __attribute__((visibility("hidden"))) int dbg_fetch_##name(unsigned* out, int reset) {         \
+    if (hipMemcpyFromSymbol(out, HIP_SYMBOL(dbg_word), sizeof(unsigned)) != hipSuccess) return -1; \
+    const unsigned zero = 0;                                                                     \
+    if (reset && hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &zero, sizeof(unsigned)) != hipSuccess) \
+      return -1;                                                                                 \
+    return 0;                                                                                    \
+  }
+#else
+#define BSG_DEBUG_FILE(name)
+#endif
 
 }  // namespace bsg

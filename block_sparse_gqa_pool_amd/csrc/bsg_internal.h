@@ -88,4 +88,16 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
                               const int32_t* block_idx, float scale, void* workspace, void* out,
                               float* lse, hipStream_t stream, gate_args ga = {nullptr, 0, nullptr});
 
+#ifdef BSG_DEBUG
+// the debug words of the kernel files (BSG_DEBUG_FILE in bsg_device.h)
+int dbg_fetch_attn_decode(unsigned* out, int reset);
+int dbg_fetch_attn_prefill(unsigned* out, int reset);
+int dbg_fetch_block_pool(unsigned* out, int reset);
+int dbg_fetch_decode_select(unsigned* out, int reset);
+int dbg_fetch_fp8_cache(unsigned* out, int reset);
+int dbg_fetch_group_score(unsigned* out, int reset);
+int dbg_fetch_score_topk_fused(unsigned* out, int reset);
+int dbg_fetch_token_select(unsigned* out, int reset);
+#endif
+
 }  // namespace bsg

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
   // the chunk's page ids, one per lane (DS_CH = 64 = wave size): a block row's page is then a
   // lane shuffle, so all row loads below go out without waiting on the page table
   static_assert(DS_CH == 64, "one page id per lane");
-  const int pid = lane < nloc ? clampi(ptrow[lane], 0, num_pages - 1) : 0;
+  const int pid = lane < nloc ? page_id(ptrow[lane], num_pages) : 0;
   uint4 raw[U];
   float scl[U];                          // F8: the piece's (page, group) scale, segment leaders
   const char* bc = reinterpret_cast<const char*>(block_cache);
@@ -256,5 +256,7 @@ hipError_t launch_decode_select(const bsg_dims& d, const void* q, const int32_t*
                      block_idx, d.num_kv_heads, d.page_size, d.top_k, nchunks, d.pt_stride, lt);
   return hipGetLastError();
 }
+
+BSG_DEBUG_FILE(decode_select)
 
 }  // namespace bsg

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void quantize_pages_fp8_kernel(const bf16_t* _
   const int nblk = min((L + BS - 1) / BS, pt_stride);
   if (j >= nblk) return;
   const int n = min(BS, L - j * BS);            // valid tokens of the block
-  const int p = clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1);
+  const int p = page_id(page_table[(size_t)b * pt_stride + j], num_pages);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int g = 0; g < Hkv; g++) {
     const size_t tile = ((size_t)p * Hkv + g) * BS * D;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void block_pool_fp8_kernel(const uint8_t* __re
   const int nfull = min(L / BS, pt_stride);
   const int begin = blk_begin ? max(blk_begin[b], 0) : 0;
   if (j < begin || j >= nfull) return;
-  const int p = clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1);
+  const int p = page_id(page_table[(size_t)b * pt_stride + j], num_pages);
   const float inv = 1.0f / (float)BS;
   // every pass covers 256 / SEG whole heads, so a head's SEG threads are one aligned lane group
   for (int u0 = 0; u0 < Hkv * SEG; u0 += 256) {
@@ -191,5 +191,7 @@ hipError_t launch_block_pool_fp8(const bsg_dims& d, const uint8_t* k_codes, cons
 #undef BSG_BP8
   return hipGetLastError();
 }
+
+BSG_DEBUG_FILE(fp8_cache)
 
 }  // namespace bsg

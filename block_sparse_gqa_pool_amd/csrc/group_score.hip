@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void group_score_kernel(const T* __restrict__ 
     const int j = j0 + jj;
     float v = 0.0f;
     if (j < jlim) {
-      const int p = clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1);
+      const int p = page_id(page_table[(size_t)b * pt_stride + j], num_pages);
       v = ld_any(block_cache + ((size_t)p * Hkv + g) * D + dd);
     }
     rs[jj * DP + dd] = v;
@@ -97,5 +97,7 @@ hipError_t launch_group_score(const bsg_dims& d, const void* q, int q_len, const
                        d.num_kv_heads, d.head_dim, d.page_size, d.num_pages, d.pt_stride);
   return hipGetLastError();
 }
+
+BSG_DEBUG_FILE(group_score)
 
 }  // namespace bsg

@@ -107,8 +107,16 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
   const int tlast = min(t0 + FS_TOK, q_len) - 1;
   const int nc_max = min(max(L - q_len + tlast, 0) / bs, pt_stride);   // candidates of the tile's last token
 
-  // group-summed query, split into three bf16 terms (B operand: k = d, n = token)
-  bf16x8_t qh[NDS], qm[NDS], ql[NDS];
+  // group-summed query, split into three bf16 terms (B operand: k = d, n = token).  With
+  // KCAP = 64 the register list of keys takes 128 registers, so the terms wait in LDS (in the
+  // region the final merge reuses), each lane reading back only what it wrote.
+  constexpr bool QLDS = KCAP > 32;
+  bf16x8_t qreg[QLDS ? 1 : 3][QLDS ? 1 : NDS];
+  bf16x8_t* qlds = reinterpret_cast<bf16x8_t*>(fs_lists);   // [4 waves][3 terms][NDS][64 lanes]
+  auto qterm = [&](int term, int ks) -> bf16x8_t {
+    if constexpr (QLDS) return qlds[((wave * 3 + term) * NDS + ks) * 64 + lane];
+    else return qreg[term][ks];
+  };
   {
     float acc[NDS][8];
 #pragma unroll
@@ -148,7 +156,8 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < NDS; ks++)
+    for (int ks = 0; ks < NDS; ks++) {
+      bf16x8_t th, tm, tl;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const float x = acc[ks][i];
@@ -156,10 +165,20 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
         const float r1 = x - (float)h;
         const __bf16 m = (__bf16)r1;
         const float r2 = r1 - (float)m;
-        qh[ks][i] = h;
-        qm[ks][i] = m;
-        ql[ks][i] = (__bf16)r2;
+        th[i] = h;
+        tm[i] = m;
+        tl[i] = (__bf16)r2;
       }
+      if constexpr (QLDS) {
+        qlds[((wave * 3 + 0) * NDS + ks) * 64 + lane] = th;
+        qlds[((wave * 3 + 1) * NDS + ks) * 64 + lane] = tm;
+        qlds[((wave * 3 + 2) * NDS + ks) * 64 + lane] = tl;
+      } else {
+        qreg[0][ks] = th;
+        qreg[1][ks] = tm;
+        qreg[2][ks] = tl;
+      }
+    }
   }
 
   double best[KCAP];                                // descending; 0 marks an empty slot
@@ -184,7 +203,7 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
 #pragma unroll
     for (int u = 0; u < NPC; u++) {
       const int piece = (u * 256 + tid) % CPR;
-      const int pid = clampi(raw[u], 0, num_pages - 1);
+      const int pid = page_id(raw[u], num_pages);
       v[u] = *reinterpret_cast<const uint4*>(block_cache + ((size_t)pid * Hkv + g) * D + 8 * piece);
     }
   };
@@ -207,9 +226,9 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
 #pragma unroll
     for (int ks = 0; ks < NDS; ks++) {
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(R + col * RS + 16 * ks + 8 * half);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[ks], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qm[ks], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[ks], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qterm(0, ks), sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qterm(1, ks), sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qterm(2, ks), sc, 0, 0, 0);
     }
     return sc;
   };
@@ -269,9 +288,10 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
     for (int ks = 0; ks < NDS; ks++) {
       const bf16x8_t a_nxt =
           *reinterpret_cast<const bf16x8_t*>(R + col * RS + 16 * (ks + 1 < NDS ? ks + 1 : ks) + 8 * half);
+      const bf16x8_t b3[3] = {qterm(0, ks), qterm(1, ks), qterm(2, ks)};
 #pragma unroll
       for (int i = 0; i < 3; i++) {
-        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur, i == 0 ? qh[ks] : (i == 1 ? qm[ks] : ql[ks]), sn, 0, 0, 0);
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur, b3[i], sn, 0, 0, 0);
         const int slot = 3 * ks + i;
 #pragma unroll
         for (int x = 0; x < (NST + NPROD - 1) / NPROD; x++) {
@@ -291,7 +311,10 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
     s_cur = sn;
   }
 
-  // merge the two half-lists of each token, append the own block, write ascending
+  // merge the two half-lists of each token, append the own block, write ascending (with
+  // QLDS this overwrites the query terms: every wave has passed the loop's last barrier, or,
+  // with no chunk at all, the barrier below orders it after this wave's own reads)
+  if (nchunks == 0) __syncthreads();
   uint64_t* mine = fs_lists + (size_t)tid * KCAP;
 #pragma unroll
   for (int i = 0; i < KCAP; i++) mine[i] = __builtin_bit_cast(uint64_t, best[i]);
@@ -317,13 +340,20 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
         ib += ta ? 0 : 1;
       }
     }
+    if constexpr (KCAP > 32) {
+      sort_ints_asc(ids);                          // unused slots hold INT_MAX and sort last
 #pragma unroll
-    for (int i = 0; i < KCAP; i++) {
-      if (i < cnt) {
-        int rank = 0;
+      for (int i = 0; i < KCAP; i++)
+        if (i < cnt) out[i] = ids[i];
+    } else {
 #pragma unroll
-        for (int i2 = 0; i2 < KCAP; i2++) rank += (i2 < cnt && ids[i2] < ids[i]) ? 1 : 0;
-        out[rank] = ids[i];
+      for (int i = 0; i < KCAP; i++) {
+        if (i < cnt) {
+          int rank = 0;
+#pragma unroll
+          for (int i2 = 0; i2 < KCAP; i2++) rank += (i2 < cnt && ids[i2] < ids[i]) ? 1 : 0;
+          out[rank] = ids[i];
+        }
       }
     }
     out[cnt] = own;
@@ -363,5 +393,7 @@ hipError_t launch_group_score_topk_fused(const bsg_dims& d, const void* q, int q
 #undef BSG_FS
   return hipGetLastError();
 }
+
+BSG_DEBUG_FILE(score_topk_fused)
 
 }  // namespace bsg

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     const int t0 = g < Hkv ? cand_token<BS, TWO>(c0, brow) : -1;
     const int j = t0 >= 0 ? t0 / BS : -1;
     const bool live = j >= 0 && j < pt_stride && t0 <= pos;
-    const int p = live ? clampi(page_table[(size_t)b * pt_stride + j], 0, num_pages - 1) : 0;
+    const int p = live ? page_id(page_table[(size_t)b * pt_stride + j], num_pages) : 0;
     tok0[hh] = live ? t0 : -1;
     rows[hh] = k_cache + (((size_t)p * Hkv + (live ? g : 0)) * BS + (live ? t0 % BS : 0)) * D;
   }
@@ -479,5 +479,7 @@ hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv
 #undef BSG_TK
   return hipGetLastError();
 }
+
+BSG_DEBUG_FILE(token_select)
 
 }  // namespace bsg

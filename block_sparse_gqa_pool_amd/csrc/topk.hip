@@ -47,16 +47,27 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
   }
   const int cnt = min(m, ncand);
   int32_t* out = block_idx + (size_t)row * top_k;
-  // rank of each kept id among the kept ids gives its ascending position
+  if constexpr (KCAP > 32) {
+    // ascending by a register sorting network (unused slots hold INT_MAX and sort last)
+    int ids[KCAP];
 #pragma unroll
-  for (int i = 0; i < KCAP; i++) {
-    if (i < cnt) {
-      const int ji = sel_key_index(best[i]);
-      int rank = 0;
+    for (int i = 0; i < KCAP; i++) ids[i] = i < cnt ? sel_key_index(best[i]) : 0x7fffffff;
+    sort_ints_asc(ids);
 #pragma unroll
-      for (int i2 = 0; i2 < KCAP; i2++)
-        if (i2 < cnt) rank += (sel_key_index(best[i2]) < ji) ? 1 : 0;
-      out[rank] = ji;
+    for (int i = 0; i < KCAP; i++)
+      if (i < cnt) out[i] = ids[i];
+  } else {
+    // rank of each kept id among the kept ids gives its ascending position
+#pragma unroll
+    for (int i = 0; i < KCAP; i++) {
+      if (i < cnt) {
+        const int ji = sel_key_index(best[i]);
+        int rank = 0;
+#pragma unroll
+        for (int i2 = 0; i2 < KCAP; i2++)
+          if (i2 < cnt) rank += (sel_key_index(best[i2]) < ji) ? 1 : 0;
+        out[rank] = ji;
+      }
     }
   }
   out[cnt] = own;

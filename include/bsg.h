@@ -91,6 +91,19 @@ int bsg_version(void);
 const char* bsg_status_str(int status);
 
 /*
+ * bsg_debug_errors -- the ids the kernels had to clamp, in a library built with -DBSG_DEBUG
+ * (block_sparse_gqa_pool_amd.build --debug: libbsg_debug.so).  Every kernel clamps the ids
+ * it reads from the caller's tables before they address memory, so a bad entry never takes
+ * it out of its buffers; the debug build also records each clamped id in a device word:
+ *     bit 0 (1): a page-table entry outside [0, num_pages) for a block the call reads,
+ *     bit 1 (2): a block id of block_idx at or past pt_stride,
+ *     bit 2 (4): a token id of token_idx at or past pt_stride * page_size.
+ * *bits receives the OR of the words of the current device; reset != 0 then clears them.
+ * Synchronous (waits for the device).  A release build returns BSG_ERR_UNSUPPORTED.
+ */
+int bsg_debug_errors(unsigned int* bits, int reset);
+
+/*
  * bsg_block_pool -- write block representatives for complete blocks.
  * Follows the Ling 2.0 page, "Summarizing the Breakthrough" (blocks are
  * aggregated into representatives stored in a cache that shares the KV

@@ -44,6 +44,13 @@ def test_header_declarations_match_exports(L):
         getattr(L, name)
 
 
+def test_debug_errors_in_release_build(L):
+    bits = ctypes.c_uint32(99)
+    assert L.bsg_debug_errors(None, 0) == -1
+    expect = -3 if os.path.basename(_lib.LIB_PATH) != "libbsg_debug.so" else 0
+    assert L.bsg_debug_errors(ctypes.byref(bits), 0) == expect
+
+
 def test_version_and_status_strings(L):
     assert L.bsg_version() == 10000
     for st, name in _lib.STATUS.items():
