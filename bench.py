@@ -230,6 +230,95 @@ def prefill_line(spec, r):
     return d
 
 
+def run_prefill_tokens(spec, seed, steps, warmup, K, two):
+    """Token-level (two False) or two-level prefill of the workload: [block_pool + block
+    selection,] token scores + top-K, attention over the kept tokens; HIP events per stage.
+    Work counts from the device selections: candidates scored (per row and group), tokens
+    attended."""
+    import torch
+    import block_sparse_gqa_pool_amd as bsg
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    w = make_workload(spec, seed, device=dev)
+    B, Hq, S, D = w.q.shape
+    Hkv, bs, k = spec.num_kv_heads, spec.page_size, spec.top_k
+    scale = 1.0 / math.sqrt(D)
+    cache = torch.zeros(w.k_cache.shape[0], Hkv, D, dtype=w.k_cache.dtype, device=dev)
+    bidx = torch.empty(B, Hkv, S, k, dtype=torch.int32, device=dev) if two else None
+    tok = torch.empty(B, Hkv, S, K, dtype=torch.int32, device=dev)
+    out = torch.empty_like(w.q)
+    d = bsg.dims(w.k_cache, w.page_table, Hq, k if two else 1)
+    ws = torch.empty(int(bsg.lib().bsg_token_topk_prefill_workspace_bytes(__import__("ctypes").byref(d), S, int(two))),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        if two:
+            bsg.block_pool(w.k_cache, w.page_table, w.kv_lens, cache)
+            bsg.group_score_topk(w.q, w.kv_lens, cache, w.page_table, bidx, page_size=bs)
+        if ev:
+            ev[1].record(stream)
+        bsg.token_topk_prefill(w.q, w.kv_lens, w.k_cache, w.page_table, tok, block_idx=bidx, workspace=ws)
+        if ev:
+            ev[2].record(stream)
+        bsg.sparse_attn_prefill_tokens(w.q, w.kv_lens, w.k_cache, w.v_cache, w.page_table, tok, scale, out)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    names = ("block_selection", "token_topk_prefill", "sparse_attn_prefill_tokens")
+    stage = {n: _stats([e[i].elapsed_time(e[i + 1]) for e in evs]) for i, n in enumerate(names)}
+    if not two:
+        del stage["block_selection"]
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    L = int(w.kv_lens_host[0])
+    pos = torch.arange(S, dtype=torch.float64) + (L - S)
+    if two:                                          # candidates: the valid tokens of the kept blocks
+        j = bidx.long()
+        nk = torch.clamp(pos.to(dev).view(1, 1, S, 1) - j * bs + 1, min=0, max=bs)
+        cand = float(torch.where(j >= 0, nk, torch.zeros_like(nk)).sum().item())
+    else:
+        cand = float((pos + 1).sum().item()) * B * Hkv
+    kept = float((tok >= 0).sum().item())
+    res = dict(tokens=B * S, ms_per_step=sum(step_ms) / steps, stage=stage, K=K,
+               score_flops=2.0 * D * cand, score_bytes=8.0 * cand, candidates=cand,
+               attn_flops=4.0 * D * spec.group_size * kept, attn_kv_bytes=4.0 * D * kept, kept_tokens=kept)
+    del w, cache, bidx, tok, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_tokens_line(spec, r, two):
+    sel = r["stage"]["token_topk_prefill"]
+    att = r["stage"]["sparse_attn_prefill_tokens"]
+    a_tf = r["attn_flops"] / (att["mean"] / 1e3) / 1e12
+    s_gbs = r["score_bytes"] / (sel["mean"] / 1e3) / 1e9
+    d = {"workload": spec.name + (f" (block top-{spec.top_k}, then token top-{r['K']})" if two
+                                  else f" (token top-{r['K']}, identity indexer)"),
+         "api": ("bsg_group_score_topk + " if two else "") + "bsg_token_topk_prefill + bsg_sparse_attn_prefill_tokens",
+         "tok_per_s": r["tokens"] / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+         "stages_ms": {n: {"mean": x["mean"], "median": x["median"]} for n, x in r["stage"].items()},
+         "selection": {"bound": "hbm", "achieved": s_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": s_gbs / PEAK_HBM_GBS, "bytes_per_launch": r["score_bytes"],
+                       "bytes_basis": "each candidate's fp32 score written once and read once",
+                       "score_tflops": r["score_flops"] / (sel["mean"] / 1e3) / 1e12,
+                       "candidates": r["candidates"]},
+         "attention": {"bound": "mfma", "achieved": a_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": a_tf / PEAK_BF16_TFLOPS, "flops_per_launch": r["attn_flops"],
+                       "kv_gather_gbs": r["attn_kv_bytes"] / (att["mean"] / 1e3) / 1e9,
+                       "kept_tokens": r["kept_tokens"]}}
+    return d
+
+
 # ------------------------------------------------------------------------------------ decode
 def _decode_setup(spec, seed, dev, fp8=False):
     """One decode workload on the device with its block cache built (as at the end of a prefill)."""
@@ -758,7 +847,8 @@ def main():
     if args.counter_run:
         counter_run()
         return
-    parts = set(("prefill,prefill32k,decode,decode1m,fp8,tokens" if args.only == "all" else args.only).split(","))
+    parts = set(("prefill,prefill32k,decode,decode1m,fp8,tokens,prefill_tokens" if args.only == "all"
+                 else args.only).split(","))
     steps = max(args.steps, 1)
 
     def log(msg):
@@ -824,6 +914,12 @@ def main():
             dt = run_decode_tokens(ds, SPECS.index(ds), max(steps, 64), args.warmup, K, two)
             dt["workload"] = ds.name + (f" (block top-{ds.top_k}, then token top-{K})" if two else f" (token top-{K})")
             line[key] = dt
+    if "prefill_tokens" in parts:
+        s1 = spec_by_name("prefill_bf16_s32768")
+        for key, K, two in (("prefill_tokens", 2048, False), ("prefill_two_level", 512, True)):
+            r = run_prefill_tokens(s1, SPECS.index(s1), max(3, min(steps, 10)), 1, K, two)
+            line[key] = prefill_tokens_line(s1, r, two)
+            log(f"{key} 32K: {r['ms_per_step']:.2f} ms per prefill")
     if "prefill" in parts:
         line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(spec, SPECS.index(spec))
     print(json.dumps(line), flush=True)

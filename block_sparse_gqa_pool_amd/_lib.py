@@ -29,7 +29,8 @@ EXPORTS = ("bsg_version", "bsg_status_str", "bsg_debug_errors", "bsg_block_pool"
            "bsg_noalloc_scratch_bytes", "bsg_decode_step_noalloc",
            "bsg_quantize_pages_fp8", "bsg_block_pool_fp8", "bsg_decode_step_fp8",
            "bsg_token_topk_workspace_bytes", "bsg_token_topk", "bsg_decode_tokens_workspace_bytes",
-           "bsg_sparse_attn_decode_tokens", "bsg_decode_step_tokens_workspace_bytes", "bsg_decode_step_tokens")
+           "bsg_sparse_attn_decode_tokens", "bsg_decode_step_tokens_workspace_bytes", "bsg_decode_step_tokens",
+           "bsg_token_topk_prefill_workspace_bytes", "bsg_token_topk_prefill", "bsg_sparse_attn_prefill_tokens")
 
 
 class BsgDims(ctypes.Structure):
@@ -87,6 +88,10 @@ def lib() -> ctypes.CDLL:
             "bsg_decode_step_tokens_workspace_bytes": ([dp, i32, i32], sz),
             "bsg_decode_step_tokens": ([dp, vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, sz, vp, vp, vp],
                                        ctypes.c_int),
+            "bsg_token_topk_prefill_workspace_bytes": ([dp, i32, i32], sz),
+            "bsg_token_topk_prefill": ([dp, vp, i32, vp, vp, vp, vp, i32, vp, vp, sz, vp], ctypes.c_int),
+            "bsg_sparse_attn_prefill_tokens": ([dp, vp, i32, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp],
+                                               ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -640,4 +645,57 @@ def decode_step_tokens(q, kv_lens, k_cache, v_cache, page_table, scale: float, t
         ctypes.byref(d), _ptr(q), _ptr(kv_lens), _ptr(block_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         K, int(two), float(scale), _ptr(block_idx), _ptr(token_idx), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+    return out
+
+
+def token_topk_prefill(q, kv_lens, k_cache, page_table, token_idx, block_idx=None, workspace=None, stream=None):
+    """bsg_token_topk_prefill: q [B, Hq, q_len, D] -> token_idx [B, Hkv, q_len, K]; two level
+    when block_idx [B, Hkv, q_len, k] is given."""
+    _req(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _req(q, "q", torch.bfloat16, 4, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(token_idx, "token_idx", torch.int32, 4, dev)
+    B, Hq, ql, D = q.shape
+    Hkv = k_cache.shape[1]
+    if tuple(token_idx.shape[:3]) != (B, Hkv, ql) or D != k_cache.shape[3] or page_table.shape[0] != B:
+        raise ValueError("token_idx must be [B, Hkv, q_len, K] and q match k_cache / page_table")
+    kb = 1
+    if block_idx is not None:
+        _req(block_idx, "block_idx", torch.int32, 4, dev)
+        if tuple(block_idx.shape[:3]) != (B, Hkv, ql):
+            raise ValueError("block_idx must be [B, Hkv, q_len, k]")
+        kb = block_idx.shape[3]
+    d = dims(k_cache, page_table, Hq, kb)
+    two = int(block_idx is not None)
+    workspace = _ws(workspace, int(lib().bsg_token_topk_prefill_workspace_bytes(ctypes.byref(d), ql, two)), dev)
+    _check("bsg_token_topk_prefill", lib().bsg_token_topk_prefill(
+        ctypes.byref(d), _ptr(q), ql, _ptr(kv_lens), _ptr(k_cache), _ptr(page_table), _ptr(block_idx),
+        token_idx.shape[3], _ptr(token_idx), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return token_idx
+
+
+def sparse_attn_prefill_tokens(q, kv_lens, k_cache, v_cache, page_table, token_idx, scale: float, out, lse=None,
+                               stream=None):
+    """bsg_sparse_attn_prefill_tokens: out [B, Hq, q_len, D] (and lse [B, Hq, q_len])."""
+    _req(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _req(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _req(q, "q", torch.bfloat16, 4, dev)
+    _tables(page_table, kv_lens, dev)
+    _req(token_idx, "token_idx", torch.int32, 4, dev)
+    _req(out, "out", torch.bfloat16, 4, dev)
+    B, Hq, ql, D = q.shape
+    Hkv = k_cache.shape[1]
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or tuple(token_idx.shape[:3]) != (B, Hkv, ql):
+        raise ValueError("shape mismatch between q, out, caches and token_idx")
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 3, dev)
+        if tuple(lse.shape) != (B, Hq, ql):
+            raise ValueError("lse must be [B, Hq, q_len]")
+    d = dims(k_cache, page_table, Hq, 1)
+    _check("bsg_sparse_attn_prefill_tokens", lib().bsg_sparse_attn_prefill_tokens(
+        ctypes.byref(d), _ptr(q), ql, _ptr(kv_lens), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        _ptr(token_idx), token_idx.shape[3], float(scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out

@@ -61,6 +61,15 @@ def lib_path(variant: str = "release") -> str:
     return os.path.join(PKG, VARIANTS[variant][0])
 
 
+def is_stale(variant: str = "release") -> bool:
+    """True when the variant's library is missing or older than a source or header."""
+    lib = lib_path(variant)
+    if not os.path.exists(lib):
+        return True
+    srcs = glob.glob(os.path.join(CSRC, "*")) + glob.glob(os.path.join(INCLUDE, "*.h"))
+    return max(os.path.getmtime(f) for f in srcs) > os.path.getmtime(lib)
+
+
 def asan_runtime() -> str:
     """The AddressSanitizer runtime of the ROCm clang that builds the asan variant."""
     import glob as _glob

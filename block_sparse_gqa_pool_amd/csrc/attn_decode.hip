@@ -483,13 +483,17 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
 // with its 64-key sub-blocks taken from consecutive entries of the row's ascending token list
 // instead of one page.  Each lane looks up the page of one entry; a key row's address then
 // reaches the lanes that read it by shuffle.  Entries are kept tokens followed by -1 padding,
-// so the valid keys of a sub-block are a prefix of it.
+// so the valid keys of a sub-block are a prefix of it.  A row is one query position of one
+// sequence (RowWindow): decode rows split their list over nwg workgroups and leave partials
+// for attn_decode_merge_kernel; with nwg = 1 (prefill rows, each a workgroup of its own) the
+// wave takes ppw sub-blocks, two at a time, and the workgroup writes out and lse itself.
 template <int D, int BS>
 __global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ token_idx, int Kt, float scale, float* __restrict__ part, int Hq, int Hkv,
-    int num_pages, int pt_stride, int nwg, int ppw) {
+    int num_pages, int pt_stride, int nwg, int ppw, RowWindow rw, bf16_t* __restrict__ out,
+    float* __restrict__ lse) {
   constexpr int NDS = D / 32;
   constexpr int NDT = D / 16;
   constexpr int VS = D + DM_VPAD;
@@ -498,18 +502,20 @@ __global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
   constexpr int NV = SUB * PPR / 64;
   extern __shared__ __attribute__((aligned(16))) unsigned char dm_smem[];
   const int G = Hq / Hkv;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y, rl = blockIdx.z;
+  const int b = rw.seq(rl), tq = rw.pos(rl);
+  if (tq >= rw.T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, qd = lane >> 4;
   bf16_t* Vs = reinterpret_cast<bf16_t*>(dm_smem) + (size_t)wave * SUB * VS;
   const float c2 = scale * 1.4426950408889634f;
-  const int32_t* trow = token_idx + ((size_t)b * Hkv + g) * Kt;
+  const int32_t* trow = token_idx + (((size_t)b * Hkv + g) * rw.T + tq) * Kt;
   (void)kv_lens;
 
   bf16x8_t qb[NDS];
   {
     const bool hv = n < G;
-    const bf16_t* qp = q + ((size_t)b * Hq + (size_t)g * G + (hv ? n : 0)) * D + 8 * qd;
+    const bf16_t* qp = q + (((size_t)b * Hq + (size_t)g * G + (hv ? n : 0)) * rw.T + tq) * D + 8 * qd;
 #pragma unroll
     for (int s = 0; s < NDS; s++) {
       uint4 v = hv ? *reinterpret_cast<const uint4*>(qp + 32 * s) : make_uint4(0, 0, 0, 0);
@@ -522,14 +528,15 @@ __global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
   for (int i = 0; i < NDT; i++) o[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int vtr = (4 * qd + ((lane & 15) >> 2)) * VS + 4 * (lane & 3);
 
-  // this wave's (at most two) sub-blocks of the list: tokens, then their pages, together
-  const int u0 = (blockIdx.x * 4 + wave) * min(ppw, 2);
+  // this wave's sub-blocks of the list, two at a time: tokens, then their pages, together
+  for (int i0 = 0; i0 < ppw; i0 += 2) {
+  const int u0 = (blockIdx.x * 4 + wave) * ppw + i0;
   int tok[2];
   long long rb[2];
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     const int e = (u0 + t) * SUB + lane;
-    tok[t] = (t < ppw && e < Kt) ? trow[e] : -1;
+    tok[t] = (i0 + t < ppw && e < Kt) ? trow[e] : -1;
   }
 #pragma unroll
   for (int t = 0; t < 2; t++) {
@@ -628,6 +635,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     __builtin_amdgcn_sched_barrier(0);
   }
+  }  // pairs of sub-blocks
   float l_h = l_run + __shfl_xor(l_run, 16, 64);
   l_h += __shfl_xor(l_h, 32, 64);
   __syncthreads();
@@ -645,7 +653,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
   }
   __syncthreads();
   const size_t pstride = (size_t)G * (D + 2);
-  float* myp = part + (((size_t)b * Hkv + g) * nwg + blockIdx.x) * pstride;
+  float* myp = part + (((size_t)rl * Hkv + g) * nwg + blockIdx.x) * pstride;
   for (int e = tid; e < G * D; e += 256) {
     const int h = e / D, d = e % D;
     float mm = -INFINITY;
@@ -661,6 +669,12 @@ __global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
         ll += mw[1] * sc;
         oo += mw[2 + d] * sc;
       }
+    }
+    if (nwg == 1) {                                  // the whole list: the final row
+      const size_t row = ((size_t)b * Hq + (size_t)g * G + h) * rw.T + tq;
+      out[row * D + d] = f32_to_bf16(oo * (ll > 0.0f ? 1.0f / ll : 0.0f));
+      if (lse && d == 0) lse[row] = mm == -INFINITY ? -INFINITY : mm * scale + logf(ll);
+      continue;
     }
     myp[h * (D + 2) + 2 + d] = oo;
     if (d == 0) {
@@ -691,16 +705,14 @@ size_t token_attn_workspace_bytes(const bsg_dims& d, int Kt) {
   return (size_t)d.batch * d.num_kv_heads * token_attn_nwg(d, Kt) * G * (d.head_dim + 2) * sizeof(float);
 }
 
-hipError_t launch_attn_decode_tokens(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
-                                     const void* v_cache, const int32_t* page_table, const int32_t* token_idx, int Kt,
-                                     float scale, void* workspace, void* out, float* lse, hipStream_t stream) {
-  const int nwg = token_attn_nwg(d, Kt);
-  const int ppw = token_attn_ppw(d, Kt);
-  float* part = (float*)workspace;
+static hipError_t token_attn_rows(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
+                                  const void* v_cache, const int32_t* page_table, const int32_t* token_idx, int Kt,
+                                  float scale, float* part, void* out, float* lse, RowWindow rw, int nrows, int nwg,
+                                  int ppw, hipStream_t stream) {
   const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
   const size_t smem_m = (size_t)4 * 16 * (d.head_dim + 2) * sizeof(float);
   const size_t smem = smem_v > smem_m ? smem_v : smem_m;
-  dim3 grid(nwg, d.num_kv_heads, d.batch);
+  dim3 grid(nwg, d.num_kv_heads, nrows);
 #define BSG_DT(DD, BB)                                                                                            \
   do {                                                                                                             \
     auto kfn = attn_decode_tokens_kernel<DD, BB>;                                                                  \
@@ -708,7 +720,7 @@ hipError_t launch_attn_decode_tokens(const bsg_dims& d, const void* q, const int
     if (ea != hipSuccess) return ea;                                                                               \
     hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache,      \
                        (const bf16_t*)v_cache, page_table, token_idx, Kt, scale, part, d.num_q_heads,              \
-                       d.num_kv_heads, d.num_pages, d.pt_stride, nwg, ppw);                                        \
+                       d.num_kv_heads, d.num_pages, d.pt_stride, nwg, ppw, rw, (bf16_t*)out, lse);                 \
   } while (0)
   if (d.head_dim == 128) {
     if (d.page_size == 64) BSG_DT(128, 64); else BSG_DT(128, 128);
@@ -716,8 +728,18 @@ hipError_t launch_attn_decode_tokens(const bsg_dims& d, const void* q, const int
     if (d.page_size == 64) BSG_DT(64, 64); else BSG_DT(64, 128);
   }
 #undef BSG_DT
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode_tokens(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
+                                     const void* v_cache, const int32_t* page_table, const int32_t* token_idx, int Kt,
+                                     float scale, void* workspace, void* out, float* lse, hipStream_t stream) {
+  const int nwg = token_attn_nwg(d, Kt);
+  const int ppw = token_attn_ppw(d, Kt);
+  float* part = (float*)workspace;
+  hipError_t e = token_attn_rows(d, q, kv_lens, k_cache, v_cache, page_table, token_idx, Kt, scale, part, out, lse,
+                                 RowWindow{1, 0, 1}, d.batch, nwg, ppw, stream);
+  if (e != hipSuccess || nwg == 1) return e;         // one workgroup per row wrote the rows itself
   dim3 mgrid(d.batch * d.num_q_heads);
   if (d.head_dim == 128)
     hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 128>), mgrid, dim3(128), 0, stream, part, (bf16_t*)out, lse,
@@ -726,6 +748,18 @@ hipError_t launch_attn_decode_tokens(const bsg_dims& d, const void* q, const int
     hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
                        d.num_q_heads, d.num_kv_heads, nwg, gate_args{nullptr, 0, nullptr});
   return hipGetLastError();
+}
+
+// Prefill rows: one workgroup per (sequence, position, group), the list dealt to its four
+// waves (ppw sub-blocks of 64 entries each), the row written directly.
+hipError_t launch_attn_prefill_tokens(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
+                                      const void* k_cache, const void* v_cache, const int32_t* page_table,
+                                      const int32_t* token_idx, int Kt, float scale, void* out, float* lse,
+                                      hipStream_t stream) {
+  const int units = (Kt + 63) / 64;
+  const int ppw = (units + 3) / 4;
+  return token_attn_rows(d, q, kv_lens, k_cache, v_cache, page_table, token_idx, Kt, scale, nullptr, out, lse,
+                         RowWindow{q_len, 0, q_len}, d.batch * q_len, 1, ppw, stream);
 }
 
 static bool decode_mfma_path(const bsg_dims& d) {

@@ -290,6 +290,39 @@ int bsg_token_topk(const bsg_dims* dims, const void* q, const int32_t* kv_lens, 
                                           token_idx, workspace, (hipStream_t)stream));
 }
 
+size_t bsg_token_topk_prefill_workspace_bytes(const bsg_dims* dims, int32_t q_len, int32_t two_level) {
+  if (check_dims(dims) || q_len < 1) return 0;
+  return bsg::token_topk_prefill_workspace_bytes(*dims, q_len, two_level != 0);
+}
+
+int bsg_token_topk_prefill(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                           const void* k_cache, const int32_t* page_table, const int32_t* block_idx,
+                           int32_t top_k_tokens, int32_t* token_idx, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->dtype != BSG_BF16) return BSG_ERR_UNSUPPORTED;
+  if (!q || !kv_lens || !k_cache || !page_table || !token_idx) return BSG_ERR_NULL;
+  if (q_len < 1 || top_k_tokens < 1) return BSG_ERR_SHAPE;
+  const size_t need = bsg::token_topk_prefill_workspace_bytes(*dims, q_len, block_idx != nullptr);
+  if (!workspace || workspace_bytes < need) return BSG_ERR_WORKSPACE;
+  return to_status(bsg::launch_token_topk_prefill(*dims, q, q_len, kv_lens, k_cache, page_table, block_idx,
+                                                  top_k_tokens, token_idx, workspace, (hipStream_t)stream));
+}
+
+int bsg_sparse_attn_prefill_tokens(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                                   const void* k_cache, const void* v_cache, const int32_t* page_table,
+                                   const int32_t* token_idx, int32_t top_k_tokens, float scale, void* out,
+                                   float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!bsg::token_attn_supported(*dims)) return BSG_ERR_UNSUPPORTED;
+  if (!q || !kv_lens || !k_cache || !v_cache || !page_table || !token_idx || !out) return BSG_ERR_NULL;
+  if (q_len < 1 || top_k_tokens < 1) return BSG_ERR_SHAPE;
+  return to_status(bsg::launch_attn_prefill_tokens(*dims, q, q_len, kv_lens, k_cache, v_cache, page_table,
+                                                   token_idx, top_k_tokens, scale, out, lse, (hipStream_t)stream));
+}
+
 size_t bsg_decode_tokens_workspace_bytes(const bsg_dims* dims, int32_t top_k_tokens) {
   if (check_dims(dims) || top_k_tokens < 1) return 0;
   return bsg::token_attn_workspace_bytes(*dims, top_k_tokens);

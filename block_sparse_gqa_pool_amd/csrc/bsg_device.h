@@ -61,6 +61,16 @@ __device__ __forceinline__ int sel_key_index(uint64_t key) { return (int)(0xffff
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Rows of the token-list kernels: (sequence b, query position t) for the window [t0, t0 + CT)
+// of the T query positions of every sequence, local row rl = b * CT + (t - t0); positions
+// at or past T are absent.  Decode: T = CT = 1, t0 = 0, so rl = b.  Query position t of
+// sequence b sits at cache position kv_lens[b] - T + t.
+struct RowWindow {
+  int T, t0, CT;
+  __host__ __device__ int seq(int rl) const { return rl / CT; }
+  __host__ __device__ int pos(int rl) const { return t0 + rl % CT; }
+};
+
 // Ids read from the caller's tables are clamped into range before they address memory, so a
 // bad entry never leads a kernel out of its buffers.  Debug builds (-DBSG_DEBUG) also record
 // each clamped id as a bit of a device word (one per source file, the file's kernels being

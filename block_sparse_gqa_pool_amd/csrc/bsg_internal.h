@@ -63,6 +63,14 @@ size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level);
 hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
                              const int32_t* page_table, const int32_t* block_idx, int top_k_tokens,
                              int32_t* token_idx, void* workspace, hipStream_t stream);
+size_t token_topk_prefill_workspace_bytes(const bsg_dims& d, int q_len, bool two_level);
+hipError_t launch_token_topk_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
+                                     const void* k_cache, const int32_t* page_table, const int32_t* block_idx,
+                                     int top_k_tokens, int32_t* token_idx, void* workspace, hipStream_t stream);
+hipError_t launch_attn_prefill_tokens(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
+                                      const void* k_cache, const void* v_cache, const int32_t* page_table,
+                                      const int32_t* token_idx, int Kt, float scale, void* out, float* lse,
+                                      hipStream_t stream);
 bool token_attn_supported(const bsg_dims& d);
 size_t token_attn_workspace_bytes(const bsg_dims& d, int Kt);
 hipError_t launch_attn_decode_tokens(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,

@@ -52,20 +52,31 @@ __device__ __forceinline__ int cand_token(int c, const int32_t* __restrict__ bro
   }
 }
 
+// Candidates a selection reads from a row of nc scores.  Token level: the positions up to
+// the query's, rounded up to 64 (the score kernels write -inf past the query's position up to
+// there; a row of a prefill tile may hold nothing valid beyond); two level: all block slots.
+template <bool TWO>
+__device__ __forceinline__ int row_candidates(int nc, int pos) {
+  if constexpr (TWO) return nc;
+  else return min(nc, (max(pos, 0) + 64) / 64 * 64);
+}
+
 template <int D, int BS, bool TWO>
 __global__ __launch_bounds__(256) void token_score_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ block_idx, int kblk,
-    float* __restrict__ scores, int nc, int Hq, int Hkv, int num_pages, int pt_stride) {
+    float* __restrict__ scores, int nc, int Hq, int Hkv, int num_pages, int pt_stride, RowWindow rw) {
   static_assert(BS % TS_CH == 0, "a chunk lies in one page");
   constexpr int SEG = D / 8;                       // lanes per key row
   constexpr int PPH = TS_CH * SEG;                 // 16-byte pieces per head
   constexpr int NP = TS_HPW * PPH / 256;           // pieces per thread
   __shared__ float qs[TS_HPW][D];
-  const int c0 = blockIdx.x * TS_CH, g0 = blockIdx.y * TS_HPW, b = blockIdx.z;
+  const int c0 = blockIdx.x * TS_CH, g0 = blockIdx.y * TS_HPW, rl = blockIdx.z;
+  const int b = rw.seq(rl), t = rw.pos(rl);
+  if (t >= rw.T) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int G = Hq / Hkv;
-  const int pos = kv_lens[b] - 1;
+  const int pos = kv_lens[b] - rw.T + t;
   // per head of this workgroup: the chunk's first token and key rows (a chunk is 64
   // consecutive tokens of one block; at token level the same block for every head)
   int tok0[TS_HPW];
@@ -73,7 +84,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 #pragma unroll
   for (int hh = 0; hh < TS_HPW; hh++) {
     const int g = g0 + hh;
-    const int32_t* brow = TWO ? block_idx + ((size_t)b * Hkv + min(g, Hkv - 1)) * kblk : nullptr;
+    const int32_t* brow = TWO ? block_idx + (((size_t)b * Hkv + min(g, Hkv - 1)) * rw.T + t) * kblk : nullptr;
     const int t0 = g < Hkv ? cand_token<BS, TWO>(c0, brow) : -1;
     const int j = t0 >= 0 ? t0 / BS : -1;
     const bool live = j >= 0 && j < pt_stride && t0 <= pos;
@@ -95,7 +106,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     if (g < Hkv)
       for (int h = 0; h < G; h++) {
-        const uint4 v = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + g * G + h) * D + d0);
+        const uint4 v = *reinterpret_cast<const uint4*>(q + (((size_t)b * Hq + g * G + h) * rw.T + t) * D + d0);
         const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -122,7 +133,141 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     s = seg_sum_dpp<SEG>(s);
     const int g = g0 + hh;
     if ((lane % SEG) == 0 && g < Hkv)
-      scores[((size_t)b * Hkv + g) * nc + c0 + r] = (tok0[hh] >= 0 && tok0[hh] + r <= pos) ? s : -INFINITY;
+      scores[((size_t)rl * Hkv + g) * nc + c0 + r] = (tok0[hh] >= 0 && tok0[hh] + r <= pos) ? s : -INFINITY;
+  }
+}
+
+// Token-level scores of prefill rows on the matrix cores.  A workgroup (4 waves) takes 128
+// query positions of one (sequence, group), a wave 32 of them, and walks the candidate
+// positions of the tile in chunks of 32 (all in one page): the chunk's 32 key rows go through
+// LDS (double-buffered, the next chunk's loads in flight during the products) and
+//   S^T (32 candidates x 32 queries) = K (candidates x D) . (hi + mid + lo)^T (D x queries)
+// with v_mfma_f32_32x32x16_bf16, where hi + mid + lo are three bf16 terms of the fp32
+// group-summed query (exact to ~2^-24 relative, as in the fused block selection), so the
+// scores are the fp32 dot products up to accumulation order.  Each lane holds 16 candidates
+// of one query; candidates past the query's position are written as -inf, up to the tile's
+// last candidate rounded up to 64 (what the selection reads).
+template <int D, int BS>
+__global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
+    const int32_t* __restrict__ page_table, float* __restrict__ scores, int nc, int Hq, int Hkv, int num_pages,
+    int pt_stride, RowWindow rw) {
+  constexpr int NDS = D / 16;                      // k-steps of the product
+  constexpr int RS = D + 8;                        // LDS row stride (bf16)
+  constexpr int CH = 32;                           // candidates per chunk
+  constexpr int CPR = D / 8;                       // 16-byte pieces per key row
+  constexpr int NPC = CH * CPR / 256;              // pieces per thread per chunk
+  static_assert(NPC * 256 == CH * CPR && BS % CH == 0, "chunk split");
+  __shared__ __attribute__((aligned(16))) bf16_t kt[2][CH * RS];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = Hq / Hkv;
+  const int L = kv_lens[b];
+  const int tend = min(rw.T, rw.t0 + rw.CT);
+  const int tw0 = rw.t0 + blockIdx.x * 128;
+  if (tw0 >= tend) return;
+  const int t = tw0 + wave * 32 + col;
+  const bool row_ok = t < tend;
+  const int pos = L - rw.T + t;
+  const int plast = L - rw.T + min(tw0 + 128, tend) - 1;
+  const int ncand = min(nc, (max(plast, 0) + 64) / 64 * 64);
+  const size_t rl = (size_t)b * rw.CT + (t - rw.t0);
+
+  // group-summed query of position t (fp32, heads in order), as three bf16 terms; the
+  // B operand of k-step ks holds dims 16 ks + 8 half .. + 7 of query col
+  bf16x8_t qh[NDS], qm[NDS], ql[NDS];
+  {
+    float acc[NDS][8];
+#pragma unroll
+    for (int ks = 0; ks < NDS; ks++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[ks][i] = 0.0f;
+    if (row_ok) {
+      const bf16_t* qp = q + (((size_t)b * Hq + (size_t)g * G) * rw.T + t) * D + 8 * half;
+      for (int h = 0; h < G; h++) {
+        uint4 v[NDS];
+#pragma unroll
+        for (int ks = 0; ks < NDS; ks++) v[ks] = *reinterpret_cast<const uint4*>(qp + (size_t)h * rw.T * D + 16 * ks);
+#pragma unroll
+        for (int ks = 0; ks < NDS; ks++) {
+          const uint32_t w4[4] = {v[ks].x, v[ks].y, v[ks].z, v[ks].w};
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            acc[ks][2 * i] += __uint_as_float(w4[i] << 16);
+            acc[ks][2 * i + 1] += __uint_as_float(w4[i] & 0xffff0000u);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < NDS; ks++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float x = acc[ks][i];
+        const __bf16 h = (__bf16)x;
+        const float r1 = x - (float)h;
+        const __bf16 m = (__bf16)r1;
+        qh[ks][i] = h;
+        qm[ks][i] = m;
+        ql[ks][i] = (__bf16)(r1 - (float)m);
+      }
+  }
+
+  auto issue = [&](int cc, uint4* v) {
+    const int s0 = cc * CH;
+    const int j = min(s0 / BS, pt_stride - 1);
+    const int p = page_id(page_table[(size_t)b * pt_stride + j], num_pages);
+    const bf16_t* base = k_cache + (((size_t)p * Hkv + g) * BS + s0 % BS) * D;
+#pragma unroll
+    for (int u = 0; u < NPC; u++) {
+      const int e = u * 256 + tid;
+      v[u] = *reinterpret_cast<const uint4*>(base + (size_t)(e / CPR) * D + 8 * (e % CPR));
+    }
+  };
+  auto stash = [&](const uint4* v, int buf) {
+#pragma unroll
+    for (int u = 0; u < NPC; u++) {
+      const int e = u * 256 + tid;
+      *reinterpret_cast<uint4*>(&kt[buf][(e / CPR) * RS + 8 * (e % CPR)]) = v[u];
+    }
+  };
+  const int nch = ncand / CH;
+  uint4 v[NPC];
+  if (nch > 0) {
+    issue(0, v);
+    stash(v, 0);
+  }
+  if (nch > 1) issue(1, v);
+  __syncthreads();
+  float* srow = scores + (rl * Hkv + g) * nc;
+  for (int cc = 0; cc < nch; cc++) {
+    const bf16_t* R = kt[cc & 1];
+    f32x16_t sc;
+#pragma unroll
+    for (int e = 0; e < 16; e++) sc[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < NDS; ks++) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(R + col * RS + 16 * ks + 8 * half);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[ks], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qm[ks], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[ks], sc, 0, 0, 0);
+    }
+    if (row_ok) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        const int s0 = cc * CH + 8 * q4 + 4 * half;
+        float4 w;
+        w.x = s0 <= pos ? sc[4 * q4] : -INFINITY;
+        w.y = s0 + 1 <= pos ? sc[4 * q4 + 1] : -INFINITY;
+        w.z = s0 + 2 <= pos ? sc[4 * q4 + 2] : -INFINITY;
+        w.w = s0 + 3 <= pos ? sc[4 * q4 + 3] : -INFINITY;
+        *reinterpret_cast<float4*>(srow + s0) = w;
+      }
+    }
+    if (cc + 1 < nch) stash(v, (cc + 1) & 1);      // the buffer chunk cc - 1 used
+    if (cc + 2 < nch) issue(cc + 2, v);
+    __syncthreads();
   }
 }
 
@@ -171,16 +316,20 @@ __device__ __forceinline__ uint32_t tk_scan(uint32_t v, uint32_t* red, uint32_t*
 template <int BS, bool TWO>
 __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restrict__ scores, int nc, int K,
                                                           const int32_t* __restrict__ block_idx, int kblk,
-                                                          int32_t* __restrict__ token_idx, int Hkv) {
+                                                          int32_t* __restrict__ token_idx, int Hkv,
+                                                          const int32_t* __restrict__ kv_lens, RowWindow rw) {
   extern __shared__ uint32_t hcopy[];              // level 1: TK_BINS bins x TK_COPIES copies
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t red[TK_NW + 1];
   __shared__ uint32_t sel_s[3];                    // digit, count above the digit, count in it
-  const int g = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.x, rl = blockIdx.y;
+  const int b = rw.seq(rl), t = rw.pos(rl);
+  if (t >= rw.T) return;
   const int tid = threadIdx.x;
-  const float* row = scores + ((size_t)b * Hkv + g) * nc;
-  const int32_t* brow = TWO ? block_idx + ((size_t)b * Hkv + g) * kblk : nullptr;
-  int32_t* orow = token_idx + ((size_t)b * Hkv + g) * K;
+  const float* row = scores + ((size_t)rl * Hkv + g) * nc;
+  const int32_t* brow = TWO ? block_idx + (((size_t)b * Hkv + g) * rw.T + t) * kblk : nullptr;
+  int32_t* orow = token_idx + (((size_t)b * Hkv + g) * rw.T + t) * K;
+  nc = row_candidates<TWO>(nc, kv_lens[b] - rw.T + t);
   // TK_UNR tiles of the row from cb on, 4 scores per thread per tile, all loads in flight
   // together (-inf past the row; nc is a multiple of 64)
   auto load_batch = [&](int cb, float4* v) {
@@ -323,16 +472,20 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
 template <int BS, bool TWO, int PER>
 __global__ __launch_bounds__(TKS_NT) void token_topk_small_kernel(const float* __restrict__ scores, int nc, int K,
                                                                   const int32_t* __restrict__ block_idx, int kblk,
-                                                                  int32_t* __restrict__ token_idx, int Hkv) {
+                                                                  int32_t* __restrict__ token_idx, int Hkv,
+                                                                  const int32_t* __restrict__ kv_lens, RowWindow rw) {
   constexpr int NW = TKS_NT / 64;
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t red[NW + 1];
   __shared__ uint32_t sel_s[3];
-  const int g = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.x, rl = blockIdx.y;
+  const int b = rw.seq(rl), t = rw.pos(rl);
+  if (t >= rw.T) return;
   const int tid = threadIdx.x;
-  const float* row = scores + ((size_t)b * Hkv + g) * nc;
-  const int32_t* brow = TWO ? block_idx + ((size_t)b * Hkv + g) * kblk : nullptr;
-  int32_t* orow = token_idx + ((size_t)b * Hkv + g) * K;
+  const float* row = scores + ((size_t)rl * Hkv + g) * nc;
+  const int32_t* brow = TWO ? block_idx + (((size_t)b * Hkv + g) * rw.T + t) * kblk : nullptr;
+  int32_t* orow = token_idx + (((size_t)b * Hkv + g) * rw.T + t) * K;
+  nc = row_candidates<TWO>(nc, kv_lens[b] - rw.T + t);
   const int c0 = tid * PER;
   uint32_t key[PER];
 #pragma unroll
@@ -418,36 +571,53 @@ size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level) {
   return (size_t)d.batch * d.num_kv_heads * nc * sizeof(float);
 }
 
-hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
-                             const int32_t* page_table, const int32_t* block_idx, int top_k_tokens,
-                             int32_t* token_idx, void* workspace, hipStream_t stream) {
+// Scores of rows rw (B * rw.CT of them) into `scores`, then their exact top-K into token_idx.
+// gemm: token level on the matrix cores (prefill tiles of 128 positions); else the per-row
+// kernel (decode rows, and two-level rows whose candidates differ from row to row).
+static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
+                                  const int32_t* page_table, const int32_t* block_idx, int top_k_tokens,
+                                  int32_t* token_idx, float* scores, RowWindow rw, bool gemm, hipStream_t stream) {
   const bool two = block_idx != nullptr;
   const int nc = two ? d.top_k * d.page_size : d.pt_stride * d.page_size;
-  float* scores = (float*)workspace;
-  dim3 g1(nc / TS_CH, (d.num_kv_heads + TS_HPW - 1) / TS_HPW, d.batch);
+  const int nrows = d.batch * rw.CT;
+  if (gemm) {
+    dim3 g0((rw.CT + 127) / 128, d.num_kv_heads, d.batch);
+#define BSG_TG(DD, BB)                                                                                         \
+  hipLaunchKernelGGL((token_score_gemm_kernel<DD, BB>), g0, dim3(256), 0, stream, (const bf16_t*)q, kv_lens,    \
+                     (const bf16_t*)k_cache, page_table, scores, nc, d.num_q_heads, d.num_kv_heads, d.num_pages, \
+                     d.pt_stride, rw)
+    if (d.head_dim == 128) {
+      if (d.page_size == 64) BSG_TG(128, 64); else BSG_TG(128, 128);
+    } else {
+      if (d.page_size == 64) BSG_TG(64, 64); else BSG_TG(64, 128);
+    }
+#undef BSG_TG
+  } else {
+    dim3 g1(nc / TS_CH, (d.num_kv_heads + TS_HPW - 1) / TS_HPW, nrows);
 #define BSG_TS(DD, BB, TW)                                                                                     \
   hipLaunchKernelGGL((token_score_kernel<DD, BB, TW>), g1, dim3(256), 0, stream, (const bf16_t*)q, kv_lens,     \
                      (const bf16_t*)k_cache, page_table, block_idx, d.top_k, scores, nc, d.num_q_heads,         \
-                     d.num_kv_heads, d.num_pages, d.pt_stride)
+                     d.num_kv_heads, d.num_pages, d.pt_stride, rw)
 #define BSG_TS_B(DD, TW)                                    \
   do {                                                      \
     if (d.page_size == 64) BSG_TS(DD, 64, TW);              \
     else BSG_TS(DD, 128, TW);                               \
   } while (0)
-  if (d.head_dim == 128) {
-    if (two) BSG_TS_B(128, true); else BSG_TS_B(128, false);
-  } else {
-    if (two) BSG_TS_B(64, true); else BSG_TS_B(64, false);
-  }
+    if (d.head_dim == 128) {
+      if (two) BSG_TS_B(128, true); else BSG_TS_B(128, false);
+    } else {
+      if (two) BSG_TS_B(64, true); else BSG_TS_B(64, false);
+    }
 #undef BSG_TS_B
 #undef BSG_TS
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2(d.num_kv_heads, d.batch);
+  dim3 g2(d.num_kv_heads, nrows);
   if (nc <= TKS_NT * 16) {                         // short rows: keys in registers
 #define BSG_TKS(BB, TW, PP)                                                                                    \
   hipLaunchKernelGGL((token_topk_small_kernel<BB, TW, PP>), g2, dim3(TKS_NT), 0, stream, scores, nc, top_k_tokens, \
-                     block_idx, d.top_k, token_idx, d.num_kv_heads)
+                     block_idx, d.top_k, token_idx, d.num_kv_heads, kv_lens, rw)
 #define BSG_TKS_P(BB, TW)                                    \
   do {                                                       \
     if (nc <= TKS_NT * 8) BSG_TKS(BB, TW, 8);                \
@@ -469,7 +639,7 @@ hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv
     hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
     if (ea != hipSuccess) return ea;                                                                            \
     hipLaunchKernelGGL(kfn, g2, dim3(TK_NT), smem, stream, scores, nc, top_k_tokens, block_idx, d.top_k,        \
-                       token_idx, d.num_kv_heads);                                                              \
+                       token_idx, d.num_kv_heads, kv_lens, rw);                                                 \
   } while (0)
   if (d.page_size == 64) {
     if (two) BSG_TK(64, true); else BSG_TK(64, false);
@@ -478,6 +648,44 @@ hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv
   }
 #undef BSG_TK
   return hipGetLastError();
+}
+
+hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
+                             const int32_t* page_table, const int32_t* block_idx, int top_k_tokens,
+                             int32_t* token_idx, void* workspace, hipStream_t stream) {
+  return token_topk_rows(d, q, kv_lens, k_cache, page_table, block_idx, top_k_tokens, token_idx, (float*)workspace,
+                         RowWindow{1, 0, 1}, false, stream);
+}
+
+// Prefill: the q_len positions go through in windows of CT rows per sequence, so that the
+// scores of one window (B * CT * Hkv rows of nc floats) stay within TOKEN_PREFILL_WS bytes.
+static constexpr size_t TOKEN_PREFILL_WS = (size_t)1 << 30;
+
+static int token_prefill_window(const bsg_dims& d, int q_len, bool two) {
+  const size_t nc = two ? (size_t)d.top_k * d.page_size : (size_t)d.pt_stride * d.page_size;
+  const size_t per_pos = (size_t)d.batch * d.num_kv_heads * nc * sizeof(float);
+  long long ct = (long long)(TOKEN_PREFILL_WS / per_pos);
+  if (ct >= 128) ct = ct / 128 * 128;                  // whole tiles of the matrix-core kernel
+  if (ct < 1) ct = 1;
+  return (int)(ct < q_len ? ct : q_len);
+}
+
+size_t token_topk_prefill_workspace_bytes(const bsg_dims& d, int q_len, bool two_level) {
+  const size_t nc = two_level ? (size_t)d.top_k * d.page_size : (size_t)d.pt_stride * d.page_size;
+  return (size_t)d.batch * token_prefill_window(d, q_len, two_level) * d.num_kv_heads * nc * sizeof(float);
+}
+
+hipError_t launch_token_topk_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
+                                     const void* k_cache, const int32_t* page_table, const int32_t* block_idx,
+                                     int top_k_tokens, int32_t* token_idx, void* workspace, hipStream_t stream) {
+  const bool two = block_idx != nullptr;
+  const int ct = token_prefill_window(d, q_len, two);
+  for (int t0 = 0; t0 < q_len; t0 += ct) {
+    hipError_t e = token_topk_rows(d, q, kv_lens, k_cache, page_table, block_idx, top_k_tokens, token_idx,
+                                   (float*)workspace, RowWindow{q_len, t0, ct}, !two, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 BSG_DEBUG_FILE(token_select)

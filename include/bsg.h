@@ -397,6 +397,39 @@ int bsg_decode_step_tokens(const bsg_dims* dims, const void* q, const int32_t* k
                            float scale, int32_t* block_idx, int32_t* token_idx, void* workspace,
                            size_t workspace_bytes, void* out, float* lse, void* stream);
 
+/*
+ * Token-level and two-level selection for prefill: the same definitions as the decode
+ * calls above, for each query position t of q [B, Hq, q_len, D] (cache position
+ * kv_lens[b] - q_len + t; candidates s <= that position).  token_idx is
+ * [B, Hkv, q_len, top_k_tokens] (ascending, -1 padded); block_idx (two level) is
+ * [B, Hkv, q_len, dims.top_k] as bsg_group_score_topk writes it, NULL for token level.
+ *
+ * bsg_token_topk_prefill -- scores and exact top-K of every row.  Token level scores each
+ * tile of 128 positions against all earlier tokens on the matrix cores (the fp32
+ * group-summed query as three bf16 terms); two level scores each row's block tokens.  The
+ * positions go through in windows whose scores fit the workspace: >=
+ * bsg_token_topk_prefill_workspace_bytes(dims, q_len, two_level) bytes, no initialisation.
+ * dtype must be BSG_BF16.
+ */
+size_t bsg_token_topk_prefill_workspace_bytes(const bsg_dims* dims, int32_t q_len, int32_t two_level);
+int bsg_token_topk_prefill(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                           const void* k_cache, const int32_t* page_table, const int32_t* block_idx,
+                           int32_t top_k_tokens, int32_t* token_idx, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * bsg_sparse_attn_prefill_tokens -- exact attention of every query position over its kept
+ * tokens (token_idx as above; -1 entries skipped):
+ *     out[b, h, t] = sum_s softmax_s(q[b, h, t] . k_s * scale) v_s,  lse = log sum_s exp(...)
+ * out [B, Hq, q_len, D] bf16, lse [B, Hq, q_len] fp32 or NULL.  One workgroup per
+ * (sequence, position, group); no workspace.  bf16 with G = Hq / Hkv <= 16 (else
+ * BSG_ERR_UNSUPPORTED).
+ */
+int bsg_sparse_attn_prefill_tokens(const bsg_dims* dims, const void* q, int32_t q_len, const int32_t* kv_lens,
+                                   const void* k_cache, const void* v_cache, const int32_t* page_table,
+                                   const int32_t* token_idx, int32_t top_k_tokens, float scale, void* out,
+                                   float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ def test_abi_checks_pass_under_asan():
     except RuntimeError as e:
         pytest.skip(str(e))
     lib = bld.lib_path("asan")
-    if not os.path.exists(lib):
+    if bld.is_stale("asan"):
         bld.build(variant="asan")
     syms = subprocess.run(["nm", "-D", lib], capture_output=True, text=True).stdout
     assert "__asan_report_load" in syms, "the asan variant is not instrumented"

@@ -24,8 +24,8 @@ PAGE, BLOCK, TOKEN = 1, 2, 4
 @pytest.fixture
 def debug_lib():
     path = bld.lib_path("debug")
-    if not os.path.exists(path):
-        pytest.fail(f"{path} is missing: python -m block_sparse_gqa_pool_amd.build --debug")
+    if bld.is_stale("debug"):
+        pytest.fail(f"{path} is missing or older than the sources: python -m block_sparse_gqa_pool_amd.build --debug")
     saved = (_lib.LIB_PATH, _lib._lib)
     _lib.LIB_PATH, _lib._lib = path, None
     bsg.debug_errors(reset=True)
@@ -65,6 +65,8 @@ def test_clean_step_records_nothing_and_matches_release():
     spec, w, cache = _decode_inputs(11)
     ref = _step(spec, w, cache, w.page_table)
     path = bld.lib_path("debug")
+    if bld.is_stale("debug"):
+        pytest.fail(f"{path} is missing or older than the sources: python -m block_sparse_gqa_pool_amd.build --debug")
     saved = (_lib.LIB_PATH, _lib._lib)
     _lib.LIB_PATH, _lib._lib = path, None
     try:
