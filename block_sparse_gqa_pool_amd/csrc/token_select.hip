@@ -38,6 +38,8 @@ constexpr int TK_BINS = 2048;  // radix bins per level (11 bits)
 constexpr int TK_UNR = 8;      // row tiles (4 scores per thread each) loaded per batch
 constexpr int TK_COPIES = 16;  // level-1 histogram copies (lane % 16): few lanes meet on one entry
 constexpr int TKS_NT = 256;    // threads of the short-row selection workgroup
+constexpr int TKM_NT = 1024;   // threads and keys per thread of the register selection of
+constexpr int TKM_PER = 32;    //   rows up to 32768 candidates
 }  // namespace
 
 // Token of candidate c of row (b, g): two level, slot c % BS of block block_idx[c / BS];
@@ -138,8 +140,9 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 }
 
 // Token-level scores of prefill rows on the matrix cores.  A workgroup (4 waves) takes 128
-// query positions of one (sequence, group), a wave 32 of them, and walks the candidate
-// positions of the tile in chunks of 32 (all in one page): the chunk's 32 key rows go through
+// query positions of one (sequence, group), a wave 32 of them, and one range of TG_RANGE
+// candidate positions (the tile's candidates end at its last position, so the ranges past
+// it have no workgroup's work), walked in chunks of 32 (all in one page): the chunk's 32 key rows go through
 // LDS (double-buffered, the next chunk's loads in flight during the products) and
 //   S^T (32 candidates x 32 queries) = K (candidates x D) . (hi + mid + lo)^T (D x queries)
 // with v_mfma_f32_32x32x16_bf16, where hi + mid + lo are three bf16 terms of the fp32
@@ -147,6 +150,8 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 // scores are the fp32 dot products up to accumulation order.  Each lane holds 16 candidates
 // of one query; candidates past the query's position are written as -inf, up to the tile's
 // last candidate rounded up to 64 (what the selection reads).
+constexpr int TG_RANGE = 2048;                    // candidates per workgroup of token_score_gemm_kernel
+
 template <int D, int BS>
 __global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
   constexpr int NPC = CH * CPR / 256;              // pieces per thread per chunk
   static_assert(NPC * 256 == CH * CPR && BS % CH == 0, "chunk split");
   __shared__ __attribute__((aligned(16))) bf16_t kt[2][CH * RS];
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.z % Hkv, b = blockIdx.z / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int G = Hq / Hkv;
@@ -172,6 +177,9 @@ __global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
   const int pos = L - rw.T + t;
   const int plast = L - rw.T + min(tw0 + 128, tend) - 1;
   const int ncand = min(nc, (max(plast, 0) + 64) / 64 * 64);
+  const int cbeg = blockIdx.y * TG_RANGE;               // this workgroup's candidates
+  if (cbeg >= ncand) return;
+  const int cend = min(ncand, cbeg + TG_RANGE);
   const size_t rl = (size_t)b * rw.CT + (t - rw.t0);
 
   // group-summed query of position t (fp32, heads in order), as three bf16 terms; the
@@ -232,15 +240,13 @@ __global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
       *reinterpret_cast<uint4*>(&kt[buf][(e / CPR) * RS + 8 * (e % CPR)]) = v[u];
     }
   };
-  const int nch = ncand / CH;
+  const int c0 = cbeg / CH, nch = (cend - cbeg) / CH;   // chunks c0 .. c0 + nch - 1
   uint4 v[NPC];
-  if (nch > 0) {
-    issue(0, v);
-    stash(v, 0);
-  }
-  if (nch > 1) issue(1, v);
+  issue(c0, v);
+  stash(v, 0);
+  if (nch > 1) issue(c0 + 1, v);
   __syncthreads();
-  float* srow = scores + (rl * Hkv + g) * nc;
+  float* srow = scores + (rl * Hkv + g) * nc + (size_t)c0 * CH;
   for (int cc = 0; cc < nch; cc++) {
     const bf16_t* R = kt[cc & 1];
     f32x16_t sc;
@@ -256,17 +262,18 @@ __global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
     if (row_ok) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; q4++) {
-        const int s0 = cc * CH + 8 * q4 + 4 * half;
+        const int s0 = cc * CH + 8 * q4 + 4 * half;         // within the range
+        const int sa = c0 * CH + s0;                         // candidate position
         float4 w;
-        w.x = s0 <= pos ? sc[4 * q4] : -INFINITY;
-        w.y = s0 + 1 <= pos ? sc[4 * q4 + 1] : -INFINITY;
-        w.z = s0 + 2 <= pos ? sc[4 * q4 + 2] : -INFINITY;
-        w.w = s0 + 3 <= pos ? sc[4 * q4 + 3] : -INFINITY;
+        w.x = sa <= pos ? sc[4 * q4] : -INFINITY;
+        w.y = sa + 1 <= pos ? sc[4 * q4 + 1] : -INFINITY;
+        w.z = sa + 2 <= pos ? sc[4 * q4 + 2] : -INFINITY;
+        w.w = sa + 3 <= pos ? sc[4 * q4 + 3] : -INFINITY;
         *reinterpret_cast<float4*>(srow + s0) = w;
       }
     }
     if (cc + 1 < nch) stash(v, (cc + 1) & 1);      // the buffer chunk cc - 1 used
-    if (cc + 2 < nch) issue(cc + 2, v);
+    if (cc + 2 < nch) issue(c0 + cc + 2, v);
     __syncthreads();
   }
 }
@@ -466,15 +473,16 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
   for (int i = (int)out_base + tid; i < K; i += TK_NT) orow[i] = -1;
 }
 
-// The same selection for short rows (nc <= 256 * PER, e.g. the two-level rows of top_k
-// blocks): one workgroup of 256 threads, each holding PER consecutive candidates' keys in
-// registers for all three levels and the compaction, with one LDS histogram.
-template <int BS, bool TWO, int PER>
-__global__ __launch_bounds__(TKS_NT) void token_topk_small_kernel(const float* __restrict__ scores, int nc, int K,
+// The same selection for rows of at most NT * PER candidates: one workgroup of NT threads,
+// each holding PER consecutive candidates' keys in registers for all three levels and the
+// compaction, with one LDS histogram.  Short rows (two-level rows of top_k blocks) take 256
+// threads, prefill rows of up to 32768 positions 1024.
+template <int BS, bool TWO, int PER, int NT>
+__global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __restrict__ scores, int nc, int K,
                                                                   const int32_t* __restrict__ block_idx, int kblk,
                                                                   int32_t* __restrict__ token_idx, int Hkv,
                                                                   const int32_t* __restrict__ kv_lens, RowWindow rw) {
-  constexpr int NW = TKS_NT / 64;
+  constexpr int NW = NT / 64;
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t red[NW + 1];
   __shared__ uint32_t sel_s[3];
@@ -505,7 +513,7 @@ __global__ __launch_bounds__(TKS_NT) void token_topk_small_kernel(const float* _
     const int shift = lv == 0 ? 21 : (lv == 1 ? 10 : 0);
     const int nbits = lv == 2 ? 10 : 11;
     const uint32_t dmask = (1u << nbits) - 1u;
-    for (int i = tid; i < TK_BINS; i += TKS_NT) hist[i] = 0u;
+    for (int i = tid; i < TK_BINS; i += NT) hist[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < PER; u++)
@@ -513,7 +521,7 @@ __global__ __launch_bounds__(TKS_NT) void token_topk_small_kernel(const float* _
     __syncthreads();
     const uint32_t need = (uint32_t)K - above;
     const int nb = 1 << nbits;
-    const int per = nb / TKS_NT;
+    const int per = nb / NT;
     uint32_t mine = 0;
     for (int k = 0; k < per; k++) mine += hist[nb - 1 - (tid * per + k)];
     uint32_t tot;
@@ -563,7 +571,7 @@ __global__ __launch_bounds__(TKS_NT) void token_topk_small_kernel(const float* _
 #pragma unroll
   for (int u = 0; u < PER; u++)
     if (keep[u] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c0 + u, brow);
-  for (int i = (int)ktot + tid; i < K; i += TKS_NT) orow[i] = -1;
+  for (int i = (int)ktot + tid; i < K; i += NT) orow[i] = -1;
 }
 
 size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level) {
@@ -581,7 +589,7 @@ static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_
   const int nc = two ? d.top_k * d.page_size : d.pt_stride * d.page_size;
   const int nrows = d.batch * rw.CT;
   if (gemm) {
-    dim3 g0((rw.CT + 127) / 128, d.num_kv_heads, d.batch);
+    dim3 g0((rw.CT + 127) / 128, (nc + TG_RANGE - 1) / TG_RANGE, d.num_kv_heads * d.batch);
 #define BSG_TG(DD, BB)                                                                                         \
   hipLaunchKernelGGL((token_score_gemm_kernel<DD, BB>), g0, dim3(256), 0, stream, (const bf16_t*)q, kv_lens,    \
                      (const bf16_t*)k_cache, page_table, scores, nc, d.num_q_heads, d.num_kv_heads, d.num_pages, \
@@ -614,14 +622,15 @@ static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(d.num_kv_heads, nrows);
-  if (nc <= TKS_NT * 16) {                         // short rows: keys in registers
-#define BSG_TKS(BB, TW, PP)                                                                                    \
-  hipLaunchKernelGGL((token_topk_small_kernel<BB, TW, PP>), g2, dim3(TKS_NT), 0, stream, scores, nc, top_k_tokens, \
-                     block_idx, d.top_k, token_idx, d.num_kv_heads, kv_lens, rw)
+  if (nc <= TKM_NT * TKM_PER) {                    // rows whose keys fit in registers
+#define BSG_TKS(BB, TW, PP, NN)                                                                                \
+  hipLaunchKernelGGL((token_topk_small_kernel<BB, TW, PP, NN>), g2, dim3(NN), 0, stream, scores, nc,            \
+                     top_k_tokens, block_idx, d.top_k, token_idx, d.num_kv_heads, kv_lens, rw)
 #define BSG_TKS_P(BB, TW)                                    \
   do {                                                       \
-    if (nc <= TKS_NT * 8) BSG_TKS(BB, TW, 8);                \
-    else BSG_TKS(BB, TW, 16);                                \
+    if (nc <= TKS_NT * 8) BSG_TKS(BB, TW, 8, TKS_NT);        \
+    else if (nc <= TKS_NT * 16) BSG_TKS(BB, TW, 16, TKS_NT); \
+    else BSG_TKS(BB, TW, TKM_PER, TKM_NT);                   \
   } while (0)
     if (d.page_size == 64) {
       if (two) BSG_TKS_P(64, true); else BSG_TKS_P(64, false);
