@@ -960,7 +960,7 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
   __shared__ uint64_t tau_s;
   __shared__ int wl[64];                       // kept blocks, ascending, own block last
   __shared__ int wpg[64];                      // their physical pages
-  __shared__ int wsel[64];
+  __shared__ uint64_t kept[DU_MAXC / 64];      // kept candidate blocks, one bit each
   __shared__ uint32_t red[DU_WAVES + 1];
   __shared__ uint32_t sel_s[3];
   __shared__ int counter_s;
@@ -995,6 +995,7 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
     pids[c] = (cnt > 0 && jb < w1) ? page_id(ptrow[jb], num_pages) : 0;
   }
   const int own_page = page_id(ptrow[min(own, pt_stride - 1)], num_pages);
+  if (tid < DU_MAXC / 64) kept[tid] = 0ull;
   // ---- 0. group-summed query (fp32, heads in order): the group's G query rows with one
   // 16-byte load per thread, parked in LDS as floats, then summed
   float* qf = reinterpret_cast<float*>(du_smem + D * 4 + DU_MAXC * 8);   // [G][D] (the histogram area)
@@ -1089,7 +1090,8 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
   }
   __syncthreads();
 
-  // ---- 2. select the cnt largest keys (distinct: the low half holds the block index)
+  // ---- 2. select the cnt largest keys (distinct: the low half holds the block index).  The
+  // kept blocks are marked in a bitmap of the candidates, which gives them in ascending order.
   bool ranked = false;                                      // workgroup-uniform
   if (cnt > 0) {
     // lower bound tau: the cnt-th largest of 64 group maxima.  The groups are disjoint sets of
@@ -1111,8 +1113,11 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
       for (int e = lane; e < ncand; e += 64) mx = max(mx, keys[e]);
       gmax[lane] = mx;
     }
+    if (tid == 0) counter_s = 0;
     __syncthreads();
-    if (wave == 0) {
+    // every wave ranks the 64 maxima itself, so no barrier separates tau from the survivors
+    uint64_t tau;
+    {
       const uint64_t gm = gmax[lane];
       const ulonglong2* g2 = reinterpret_cast<const ulonglong2*>(gmax);
       int rank = 0;
@@ -1121,12 +1126,12 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
         const ulonglong2 v = g2[i];
         rank += (v.x > gm ? 1 : 0) + (v.y > gm ? 1 : 0);
       }
-      // the real maxima are distinct; empty groups (0) rank last
-      if (gm != 0ull && rank == cnt - 1) tau_s = gm;
-      if (lane == 0) counter_s = 0;
+      // the real maxima are distinct and empty groups (0) rank last: exactly one lane holds it
+      const uint64_t hit = __ballot(gm != 0ull && rank == cnt - 1);
+      const int src = (int)__builtin_ctzll(hit);
+      tau = ((uint64_t)(uint32_t)__shfl((int)(gm >> 32), src, 64) << 32) |
+            (uint64_t)(uint32_t)__shfl((int)(uint32_t)gm, src, 64);
     }
-    __syncthreads();
-    const uint64_t tau = tau_s;
     for (int e = tid; e < ncand; e += DU_NT) {
       const uint64_t k = keys[e];
       if (k >= tau) {
@@ -1147,7 +1152,10 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
           rank += (v.x > k ? 1 : 0) + (v.y > k ? 1 : 0);
         }
         if (ns & 1) rank += surv[ns - 1] > k ? 1 : 0;
-        if (rank < cnt) wsel[rank] = sel_key_index(k);
+        if (rank < cnt) {
+          const int j = sel_key_index(k);
+          atomicOr(&kept[j >> 6], 1ull << (j & 63));
+        }
       }
       ranked = true;
     }
@@ -1203,26 +1211,31 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
       __syncthreads();
     }
     // the kept keys are those whose masked top bits are >= prefix (exactly cnt of them)
-    if (tid == 0) counter_s = 0;
-    __syncthreads();
     for (int e = tid; e < ncand; e += DU_NT) {
       const uint64_t k = keys[e];
-      if ((k & pmask) >= prefix) {
-        const int at = atomicAdd(&counter_s, 1);
-        if (at < 64) wsel[at] = sel_key_index(k);
-      }
+      if ((k & pmask) >= prefix) atomicOr(&kept[e >> 6], 1ull << (e & 63));
     }
     __syncthreads();
   }
-  if (cnt > 0) {
-    if (tid < cnt) {                                         // ascending
-      const int ji = wsel[tid];
-      int r2 = 0;
-      for (int i = 0; i < cnt; i++) r2 += wsel[i] < ji ? 1 : 0;
-      wl[r2] = ji;
+  // ascending list from the bitmap (wave 0: a word per lane, positions by a prefix count),
+  // the own block appended
+  if (wave == 0) {
+    uint64_t bits = lane < DU_MAXC / 64 ? kept[lane] : 0ull;
+    const int n1 = __popcll(bits);
+    int incl = n1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
     }
+    int at = incl - n1;
+    while (bits) {
+      const int b0 = (int)__builtin_ctzll(bits);
+      bits &= bits - 1;
+      wl[at++] = lane * 64 + b0;
+    }
+    if (lane == 0) wl[cnt] = own;
   }
-  if (tid == 0) wl[cnt] = own;
   __syncthreads();
   if (sm == 0 && tid < top_k) block_idx[((size_t)b * Hkv + g) * top_k + tid] = tid <= cnt ? wl[tid] : -1;
   // pages in the attention order: the own block first (its page from the table), then the
