@@ -914,6 +914,11 @@ def main():
             dt = run_decode_tokens(ds, SPECS.index(ds), max(steps, 64), args.warmup, K, two)
             dt["workload"] = ds.name + (f" (block top-{ds.top_k}, then token top-{K})" if two else f" (token top-{K})")
             line[key] = dt
+        s4 = spec_by_name("decode_bf16_b4_ctx512k_1m")
+        dt = run_decode_tokens(s4, SPECS.index(s4), max(steps, 16), args.warmup, 2048, False)
+        dt["workload"] = s4.name + " (token top-2048)"
+        line["decode_tokens_1m"] = dt
+        log(f"token-level decode ~1M x 4: {dt['us_per_step']:.0f} us per step")
     if "prefill_tokens" in parts:
         s1 = spec_by_name("prefill_bf16_s32768")
         for key, K, two in (("prefill_tokens", 2048, False), ("prefill_two_level", 512, True)):

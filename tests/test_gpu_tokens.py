@@ -130,10 +130,12 @@ def test_token_attention_on_oracle_lists():
     assert np.abs(lse.cpu().numpy() - rlse[:, :, 0]).max() <= 2e-3
 
 
-def test_token_level_full_size_sampled():
-    """The 128K x 32 decode workload at K = 2048 tokens, two sequences against the oracle."""
-    spec = SPECS[2]
-    w = make_workload(spec, 2, device=DEV)
+@pytest.mark.parametrize("cfg", [2, 4], ids=["ctx128k_b32", "ctx512k_1m_b4"])
+def test_token_level_full_size_sampled(cfg):
+    """The 128K x 32 decode workload (two sequences) and the ragged ~1M x 4 one (its shortest
+    sequence) at K = 2048 tokens, against the oracle."""
+    spec = SPECS[cfg]
+    w = make_workload(spec, cfg, device=DEV)
     B, Hq, _, D = w.q.shape
     Hkv, K = spec.num_kv_heads, 2048
     scale = 1.0 / math.sqrt(D)
@@ -144,7 +146,7 @@ def test_token_level_full_size_sampled():
     bsg.decode_step_tokens(q1, w.kv_lens, w.k_cache, w.v_cache, w.page_table, scale, tok, out, lse)
     torch.cuda.synchronize()
     from gpu_util import mini_pool
-    seqs = [0, 21]
+    seqs = [0, 21] if cfg == 2 else [int(np.argmin(w.kv_lens_host))]
     note(f"[case] token-level full decode {spec.name}: sequences {seqs}")
     qn, kp, vp, ptm, kv = mini_pool(w, seqs)
     r = O.decode_tokens_reference(qn, kp, vp, ptm, kv, K, scale)
