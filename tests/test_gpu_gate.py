@@ -62,8 +62,9 @@ def test_prefill_gated(spec, per_dim):
 @pytest.mark.parametrize("per_dim", [0, 1])
 @pytest.mark.parametrize("spec", [
     SPECS[2].replace(batch=3, ctx_len=64 * 60 + 9),                                       # fused decode step
+    SPECS[2].replace(batch=40, ctx_len=64 * 12 + 9),             # 160 units: one workgroup each, gate in that kernel
     SPECS[2].replace(batch=2, ctx_len=64 * 30 + 1, num_q_heads=40, head_dim=64, num_kv_heads=2),   # G = 20: split path
-], ids=["fused", "split"])
+], ids=["fused", "fused_one_member", "split"])
 def test_decode_step_gated(spec, per_dim):
     w = make_workload(spec, 43, device=DEV, tail_fill=float("nan"))
     note(f"[case] gated decode {spec.name} G={spec.group_size} per_dim={per_dim}")

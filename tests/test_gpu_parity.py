@@ -331,6 +331,20 @@ def test_decode_edge_shapes_end_to_end(case, api):
     check_decode(w, idx, out, lse)
 
 
+@pytest.mark.parametrize("batch", [40, 31, 32, 3], ids=["one_member", "two_members_idle_slots", "two_members",
+                                                     "four_members"])
+def test_decode_step_member_counts(batch):
+    """The one-kernel decode step serves a (sequence, group) unit with S = 1, 2 or 4 workgroups
+    (by the number of units against the CUs; 4 KV heads here): 160 units take one each and
+    write the rows themselves, 124 and 128 units two (124 leaves four slots of the last group of
+    eight idle), 12 units four; the partials of S > 1 go through the merge kernel."""
+    spec = SPECS[2].replace(batch=batch, ctx_len=64 * 24 + 5)
+    note(f"[case] decode_step with {batch * spec.num_kv_heads} units")
+    w = make_workload(spec, 19, tail_fill=float("nan")).to(DEV)
+    cache, idx, out, lse = run_decode_gpu(w, "step")
+    check_decode(w, idx, out, lse)
+
+
 def test_decode_step_ragged_batch_and_reuse():
     """Ragged lengths (some shorter than the others by many chunks); workspace reused."""
     spec = SPECS[4].replace(batch=4, ctx_range=(64 * 30, 64 * 900), num_q_heads=16, num_kv_heads=2)
