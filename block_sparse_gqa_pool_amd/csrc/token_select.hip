@@ -481,7 +481,8 @@ template <int BS, bool TWO, int PER, int NT>
 __global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __restrict__ scores, int nc, int K,
                                                                   const int32_t* __restrict__ block_idx, int kblk,
                                                                   int32_t* __restrict__ token_idx, int Hkv,
-                                                                  const int32_t* __restrict__ kv_lens, RowWindow rw) {
+                                                                  const int32_t* __restrict__ kv_lens, RowWindow rw,
+                                                                  int stride, int pt_stride, int full_rows) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t red[NW + 1];
@@ -490,7 +491,11 @@ __global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __res
   const int b = rw.seq(rl), t = rw.pos(rl);
   if (t >= rw.T) return;
   const int tid = threadIdx.x;
-  const float* row = scores + ((size_t)rl * Hkv + g) * nc;
+  const float* row = scores + ((size_t)rl * Hkv + g) * stride;
+  // two level over full rows (prefill): the candidates' scores sit at their token positions
+  // in a row of every position's score (row stride `stride`), gathered through the block list
+  const bool gather = TWO && full_rows != 0;
+  const int pos = kv_lens[b] - rw.T + t;
   const int32_t* brow = TWO ? block_idx + (((size_t)b * Hkv + g) * rw.T + t) * kblk : nullptr;
   int32_t* orow = token_idx + (((size_t)b * Hkv + g) * rw.T + t) * K;
   nc = row_candidates<TWO>(nc, kv_lens[b] - rw.T + t);
@@ -499,8 +504,20 @@ __global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __res
 #pragma unroll
   for (int u = 0; u < PER / 4; u++) {
     const int c = c0 + 4 * u;
-    const float4 v = c < nc ? *reinterpret_cast<const float4*>(row + c)
-                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (gather) {                                  // 4 consecutive slots: 4 tokens of one block
+      const int j = c < nc ? brow[c / BS] : -1;
+      const int tk = j >= 0 ? block_id(j, pt_stride) * BS + c % BS : -1;
+      if (tk >= 0) {
+        v = *reinterpret_cast<const float4*>(row + tk);
+        v.x = tk <= pos ? v.x : -INFINITY;           // past the position: not written, not a candidate
+        v.y = tk + 1 <= pos ? v.y : -INFINITY;
+        v.z = tk + 2 <= pos ? v.z : -INFINITY;
+        v.w = tk + 3 <= pos ? v.w : -INFINITY;
+      }
+    } else if (c < nc) {
+      v = *reinterpret_cast<const float4*>(row + c);
+    }
     key[4 * u] = tk_key(v.x);
     key[4 * u + 1] = tk_key(v.y);
     key[4 * u + 2] = tk_key(v.z);
@@ -587,13 +604,15 @@ static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_
                                   int32_t* token_idx, float* scores, RowWindow rw, bool gemm, hipStream_t stream) {
   const bool two = block_idx != nullptr;
   const int nc = two ? d.top_k * d.page_size : d.pt_stride * d.page_size;
+  const int nfull = d.pt_stride * d.page_size;
+  const int stride = gemm ? nfull : nc;          // gemm: every position's score, two level gathers
   const int nrows = d.batch * rw.CT;
   if (gemm) {
-    dim3 g0((rw.CT + 127) / 128, (nc + TG_RANGE - 1) / TG_RANGE, d.num_kv_heads * d.batch);
+    dim3 g0((rw.CT + 127) / 128, (nfull + TG_RANGE - 1) / TG_RANGE, d.num_kv_heads * d.batch);
 #define BSG_TG(DD, BB)                                                                                         \
   hipLaunchKernelGGL((token_score_gemm_kernel<DD, BB>), g0, dim3(256), 0, stream, (const bf16_t*)q, kv_lens,    \
-                     (const bf16_t*)k_cache, page_table, scores, nc, d.num_q_heads, d.num_kv_heads, d.num_pages, \
-                     d.pt_stride, rw)
+                     (const bf16_t*)k_cache, page_table, scores, nfull, d.num_q_heads, d.num_kv_heads,          \
+                     d.num_pages, d.pt_stride, rw)
     if (d.head_dim == 128) {
       if (d.page_size == 64) BSG_TG(128, 64); else BSG_TG(128, 128);
     } else {
@@ -625,7 +644,8 @@ static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_
   if (nc <= TKM_NT * TKM_PER) {                    // rows whose keys fit in registers
 #define BSG_TKS(BB, TW, PP, NN)                                                                                \
   hipLaunchKernelGGL((token_topk_small_kernel<BB, TW, PP, NN>), g2, dim3(NN), 0, stream, scores, nc,            \
-                     top_k_tokens, block_idx, d.top_k, token_idx, d.num_kv_heads, kv_lens, rw)
+                     top_k_tokens, block_idx, d.top_k, token_idx, d.num_kv_heads, kv_lens, rw, stride, d.pt_stride,  \
+                     gemm ? 1 : 0)
 #define BSG_TKS_P(BB, TW)                                    \
   do {                                                       \
     if (nc <= TKS_NT * 8) BSG_TKS(BB, TW, 8, TKS_NT);        \
@@ -670,8 +690,8 @@ hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv
 // scores of one window (B * CT * Hkv rows of nc floats) stay within TOKEN_PREFILL_WS bytes.
 static constexpr size_t TOKEN_PREFILL_WS = (size_t)1 << 30;
 
-static int token_prefill_window(const bsg_dims& d, int q_len, bool two) {
-  const size_t nc = two ? (size_t)d.top_k * d.page_size : (size_t)d.pt_stride * d.page_size;
+static int token_prefill_window(const bsg_dims& d, int q_len) {
+  const size_t nc = (size_t)d.pt_stride * d.page_size;
   const size_t per_pos = (size_t)d.batch * d.num_kv_heads * nc * sizeof(float);
   long long ct = (long long)(TOKEN_PREFILL_WS / per_pos);
   if (ct >= 128) ct = ct / 128 * 128;                  // whole tiles of the matrix-core kernel
@@ -680,18 +700,18 @@ static int token_prefill_window(const bsg_dims& d, int q_len, bool two) {
 }
 
 size_t token_topk_prefill_workspace_bytes(const bsg_dims& d, int q_len, bool two_level) {
-  const size_t nc = two_level ? (size_t)d.top_k * d.page_size : (size_t)d.pt_stride * d.page_size;
-  return (size_t)d.batch * token_prefill_window(d, q_len, two_level) * d.num_kv_heads * nc * sizeof(float);
+  (void)two_level;                                 // both forms score full rows
+  const size_t nc = (size_t)d.pt_stride * d.page_size;
+  return (size_t)d.batch * token_prefill_window(d, q_len) * d.num_kv_heads * nc * sizeof(float);
 }
 
 hipError_t launch_token_topk_prefill(const bsg_dims& d, const void* q, int q_len, const int32_t* kv_lens,
                                      const void* k_cache, const int32_t* page_table, const int32_t* block_idx,
                                      int top_k_tokens, int32_t* token_idx, void* workspace, hipStream_t stream) {
-  const bool two = block_idx != nullptr;
-  const int ct = token_prefill_window(d, q_len, two);
+  const int ct = token_prefill_window(d, q_len);
   for (int t0 = 0; t0 < q_len; t0 += ct) {
     hipError_t e = token_topk_rows(d, q, kv_lens, k_cache, page_table, block_idx, top_k_tokens, token_idx,
-                                   (float*)workspace, RowWindow{q_len, t0, ct}, !two, stream);
+                                   (float*)workspace, RowWindow{q_len, t0, ct}, true, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -404,9 +404,9 @@ int bsg_decode_step_tokens(const bsg_dims* dims, const void* q, const int32_t* k
  * [B, Hkv, q_len, top_k_tokens] (ascending, -1 padded); block_idx (two level) is
  * [B, Hkv, q_len, dims.top_k] as bsg_group_score_topk writes it, NULL for token level.
  *
- * bsg_token_topk_prefill -- scores and exact top-K of every row.  Token level scores each
- * tile of 128 positions against all earlier tokens on the matrix cores (the fp32
- * group-summed query as three bf16 terms); two level scores each row's block tokens.  The
+ * bsg_token_topk_prefill -- scores and exact top-K of every row.  Each tile of 128 positions
+ * is scored against all earlier tokens on the matrix cores (the fp32 group-summed query as
+ * three bf16 terms); two level then selects among the tokens of each row's blocks only.  The
  * positions go through in windows whose scores fit the workspace: >=
  * bsg_token_topk_prefill_workspace_bytes(dims, q_len, two_level) bytes, no initialisation.
  * dtype must be BSG_BF16.
