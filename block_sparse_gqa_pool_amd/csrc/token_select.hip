@@ -324,7 +324,8 @@ template <int BS, bool TWO>
 __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restrict__ scores, int nc, int K,
                                                           const int32_t* __restrict__ block_idx, int kblk,
                                                           int32_t* __restrict__ token_idx, int Hkv,
-                                                          const int32_t* __restrict__ kv_lens, RowWindow rw) {
+                                                          const int32_t* __restrict__ kv_lens, RowWindow rw,
+                                                          int nparts, int32_t* __restrict__ part_lists) {
   extern __shared__ uint32_t hcopy[];              // level 1: TK_BINS bins x TK_COPIES copies
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t red[TK_NW + 1];
@@ -337,6 +338,16 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
   const int32_t* brow = TWO ? block_idx + (((size_t)b * Hkv + g) * rw.T + t) * kblk : nullptr;
   int32_t* orow = token_idx + (((size_t)b * Hkv + g) * rw.T + t) * K;
   nc = row_candidates<TWO>(nc, kv_lens[b] - rw.T + t);
+  // nparts > 1 (token level): this workgroup selects the top K of part blockIdx.z of the row
+  // (a multiple of 64 candidates) into part_lists, absolute candidate ids, for the second stage
+  int c_off = 0;
+  if (nparts > 1) {
+    const int seg = ((nc + nparts - 1) / nparts + 63) / 64 * 64;
+    c_off = min((int)blockIdx.z * seg, nc);
+    nc = min(nc - c_off, seg);
+    row += c_off;
+    orow = part_lists + (((size_t)rl * Hkv + g) * nparts + blockIdx.z) * K;
+  }
   // TK_UNR tiles of the row from cb on, 4 scores per thread per tile, all loads in flight
   // together (-inf past the row; nc is a multiple of 64)
   auto load_batch = [&](int cb, float4* v) {
@@ -465,7 +476,7 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
       uint32_t o = out_base + tk_scan<TK_NW>(n_keep, red, &ktot);
 #pragma unroll
       for (int e = 0; e < 4; e++)
-        if (keep[e] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c + e, brow);
+        if (keep[e] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c_off + c + e, brow);
       out_base += ktot;
       eq_base += eq_tot;
     }
@@ -482,7 +493,8 @@ __global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __res
                                                                   const int32_t* __restrict__ block_idx, int kblk,
                                                                   int32_t* __restrict__ token_idx, int Hkv,
                                                                   const int32_t* __restrict__ kv_lens, RowWindow rw,
-                                                                  int stride, int pt_stride, int full_rows) {
+                                                                  int stride, int pt_stride, int full_rows,
+                                                                  const int32_t* __restrict__ part_lists) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t red[NW + 1];
@@ -493,19 +505,28 @@ __global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __res
   const int tid = threadIdx.x;
   const float* row = scores + ((size_t)rl * Hkv + g) * stride;
   // two level over full rows (prefill): the candidates' scores sit at their token positions
-  // in a row of every position's score (row stride `stride`), gathered through the block list
+  // in a row of every position's score (row stride `stride`), gathered through the block list.
+  // part_lists (token level, second stage): the candidates are the first stage's kept ids
+  // (ascending, -1 padded), their scores gathered from the row.
   const bool gather = TWO && full_rows != 0;
+  const int32_t* lst = part_lists ? part_lists + ((size_t)rl * Hkv + g) * nc : nullptr;
   const int pos = kv_lens[b] - rw.T + t;
   const int32_t* brow = TWO ? block_idx + (((size_t)b * Hkv + g) * rw.T + t) * kblk : nullptr;
   int32_t* orow = token_idx + (((size_t)b * Hkv + g) * rw.T + t) * K;
-  nc = row_candidates<TWO>(nc, kv_lens[b] - rw.T + t);
+  if (!lst) nc = row_candidates<TWO>(nc, pos);        // a list holds nc entries (-1 padded)
   const int c0 = tid * PER;
   uint32_t key[PER];
 #pragma unroll
   for (int u = 0; u < PER / 4; u++) {
     const int c = c0 + 4 * u;
     float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (gather) {                                  // 4 consecutive slots: 4 tokens of one block
+    if (lst) {
+      const int4 tk4 = c < nc ? *reinterpret_cast<const int4*>(lst + c) : make_int4(-1, -1, -1, -1);
+      v.x = tk4.x >= 0 ? row[tk4.x] : -INFINITY;
+      v.y = tk4.y >= 0 ? row[tk4.y] : -INFINITY;
+      v.z = tk4.z >= 0 ? row[tk4.z] : -INFINITY;
+      v.w = tk4.w >= 0 ? row[tk4.w] : -INFINITY;
+    } else if (gather) {                           // 4 consecutive slots: 4 tokens of one block
       const int j = c < nc ? brow[c / BS] : -1;
       const int tk = j >= 0 ? block_id(j, pt_stride) * BS + c % BS : -1;
       if (tk >= 0) {
@@ -587,13 +608,53 @@ __global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __res
   uint32_t o = tk_scan<NW>(n_keep, red, &ktot);
 #pragma unroll
   for (int u = 0; u < PER; u++)
-    if (keep[u] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c0 + u, brow);
+    if (keep[u] && o < (uint32_t)K) orow[o++] = lst ? lst[c0 + u] : cand_token<BS, TWO>(c0 + u, brow);
   for (int i = (int)ktot + tid; i < K; i += NT) orow[i] = -1;
 }
 
 size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level) {
   const size_t nc = two_level ? (size_t)d.top_k * d.page_size : (size_t)d.pt_stride * d.page_size;
-  return (size_t)d.batch * d.num_kv_heads * nc * sizeof(float);
+  // rows longer than the register selection also get room for their parts' lists
+  const size_t lists = nc > (size_t)TKM_NT * TKM_PER ? (size_t)TKM_NT * TKM_PER : 0;
+  return (size_t)d.batch * d.num_kv_heads * (nc + lists) * sizeof(float);
+}
+
+// The register selection (token_topk_small_kernel) of rows of at most TKM_NT * TKM_PER
+// candidates: nc candidates per row (a row of scores, a block list over full rows, or the
+// parts' lists), 8 / 16 / 32 keys per thread.
+static hipError_t token_topk_registers(const bsg_dims& d, bool two, const float* scores, int nc, int K,
+                                       const int32_t* block_idx, int32_t* token_idx, const int32_t* kv_lens,
+                                       RowWindow rw, int stride, int full_rows, const int32_t* lists, dim3 grid,
+                                       hipStream_t stream) {
+#define BSG_TKS(BB, TW, PP, NN)                                                                                \
+  hipLaunchKernelGGL((token_topk_small_kernel<BB, TW, PP, NN>), grid, dim3(NN), 0, stream, scores, nc, K,       \
+                     block_idx, d.top_k, token_idx, d.num_kv_heads, kv_lens, rw, stride, d.pt_stride, full_rows, \
+                     lists)
+#define BSG_TKS_P(BB, TW)                                    \
+  do {                                                       \
+    if (nc <= TKS_NT * 8) BSG_TKS(BB, TW, 8, TKS_NT);        \
+    else if (nc <= TKS_NT * 16) BSG_TKS(BB, TW, 16, TKS_NT); \
+    else BSG_TKS(BB, TW, TKM_PER, TKM_NT);                   \
+  } while (0)
+  if (d.page_size == 64) {
+    if (two) BSG_TKS_P(64, true); else BSG_TKS_P(64, false);
+  } else {
+    if (two) BSG_TKS_P(128, true); else BSG_TKS_P(128, false);
+  }
+#undef BSG_TKS_P
+#undef BSG_TKS
+  return hipGetLastError();
+}
+
+// Parts per long token-level row: doubled while every part still gets a CU (one 128 KiB
+// selection workgroup per CU), the parts' lists (P * K ids) fit the register selection and a
+// part keeps at least 4 K candidates.
+static int token_topk_parts(const bsg_dims& d, int nrows, int nc, int K, bool two) {
+  if (two) return 1;
+  const long long units = (long long)nrows * d.num_kv_heads;
+  int P = 1;
+  while (P < 16 && units * P * 2 <= 256 && (long long)P * 2 * K <= TKM_NT * TKM_PER && nc / (P * 2) >= 4 * K) P *= 2;
+  return P;
 }
 
 // Scores of rows rw (B * rw.CT of them) into `scores`, then their exact top-K into token_idx.
@@ -601,7 +662,8 @@ size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level) {
 // kernel (decode rows, and two-level rows whose candidates differ from row to row).
 static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
                                   const int32_t* page_table, const int32_t* block_idx, int top_k_tokens,
-                                  int32_t* token_idx, float* scores, RowWindow rw, bool gemm, hipStream_t stream) {
+                                  int32_t* token_idx, float* scores, RowWindow rw, bool gemm, int32_t* lists,
+                                  hipStream_t stream) {
   const bool two = block_idx != nullptr;
   const int nc = two ? d.top_k * d.page_size : d.pt_stride * d.page_size;
   const int nfull = d.pt_stride * d.page_size;
@@ -641,34 +703,22 @@ static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(d.num_kv_heads, nrows);
-  if (nc <= TKM_NT * TKM_PER) {                    // rows whose keys fit in registers
-#define BSG_TKS(BB, TW, PP, NN)                                                                                \
-  hipLaunchKernelGGL((token_topk_small_kernel<BB, TW, PP, NN>), g2, dim3(NN), 0, stream, scores, nc,            \
-                     top_k_tokens, block_idx, d.top_k, token_idx, d.num_kv_heads, kv_lens, rw, stride, d.pt_stride,  \
-                     gemm ? 1 : 0)
-#define BSG_TKS_P(BB, TW)                                    \
-  do {                                                       \
-    if (nc <= TKS_NT * 8) BSG_TKS(BB, TW, 8, TKS_NT);        \
-    else if (nc <= TKS_NT * 16) BSG_TKS(BB, TW, 16, TKS_NT); \
-    else BSG_TKS(BB, TW, TKM_PER, TKM_NT);                   \
-  } while (0)
-    if (d.page_size == 64) {
-      if (two) BSG_TKS_P(64, true); else BSG_TKS_P(64, false);
-    } else {
-      if (two) BSG_TKS_P(128, true); else BSG_TKS_P(128, false);
-    }
-#undef BSG_TKS_P
-#undef BSG_TKS
-    return hipGetLastError();
-  }
+  if (nc <= TKM_NT * TKM_PER)                      // rows whose keys fit in registers
+    return token_topk_registers(d, two, scores, nc, top_k_tokens, block_idx, token_idx, kv_lens, rw, stride,
+                                gemm ? 1 : 0, nullptr, g2, stream);
+  // long rows: with few rows, each row's parts are selected by workgroups of their own and the
+  // register selection then takes the top K of the parts' lists (the global top K lies in
+  // their union, and the lists are in candidate order, so ties resolve as in one pass)
+  const int P = lists ? token_topk_parts(d, nrows, nc, top_k_tokens, two) : 1;
   const size_t smem = (size_t)TK_BINS * TK_COPIES * sizeof(uint32_t);
+  dim3 g3(d.num_kv_heads, nrows, P);
 #define BSG_TK(BB, TW)                                                                                         \
   do {                                                                                                          \
     auto kfn = token_topk_kernel<BB, TW>;                                                                       \
     hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
     if (ea != hipSuccess) return ea;                                                                            \
-    hipLaunchKernelGGL(kfn, g2, dim3(TK_NT), smem, stream, scores, nc, top_k_tokens, block_idx, d.top_k,        \
-                       token_idx, d.num_kv_heads, kv_lens, rw);                                                 \
+    hipLaunchKernelGGL(kfn, g3, dim3(TK_NT), smem, stream, scores, nc, top_k_tokens, block_idx, d.top_k,        \
+                       token_idx, d.num_kv_heads, kv_lens, rw, P, lists);                                       \
   } while (0)
   if (d.page_size == 64) {
     if (two) BSG_TK(64, true); else BSG_TK(64, false);
@@ -676,14 +726,21 @@ static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_
     if (two) BSG_TK(128, true); else BSG_TK(128, false);
   }
 #undef BSG_TK
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || P == 1) return e;
+  return token_topk_registers(d, two, scores, P * top_k_tokens, top_k_tokens, block_idx, token_idx, kv_lens, rw,
+                              stride, 0, lists, g2, stream);
 }
 
 hipError_t launch_token_topk(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* k_cache,
                              const int32_t* page_table, const int32_t* block_idx, int top_k_tokens,
                              int32_t* token_idx, void* workspace, hipStream_t stream) {
+  const size_t nc = block_idx ? (size_t)d.top_k * d.page_size : (size_t)d.pt_stride * d.page_size;
+  int32_t* lists = nc > (size_t)TKM_NT * TKM_PER
+                       ? reinterpret_cast<int32_t*>((float*)workspace + (size_t)d.batch * d.num_kv_heads * nc)
+                       : nullptr;
   return token_topk_rows(d, q, kv_lens, k_cache, page_table, block_idx, top_k_tokens, token_idx, (float*)workspace,
-                         RowWindow{1, 0, 1}, false, stream);
+                         RowWindow{1, 0, 1}, false, lists, stream);
 }
 
 // Prefill: the q_len positions go through in windows of CT rows per sequence, so that the
@@ -711,7 +768,7 @@ hipError_t launch_token_topk_prefill(const bsg_dims& d, const void* q, int q_len
   const int ct = token_prefill_window(d, q_len);
   for (int t0 = 0; t0 < q_len; t0 += ct) {
     hipError_t e = token_topk_rows(d, q, kv_lens, k_cache, page_table, block_idx, top_k_tokens, token_idx,
-                                   (float*)workspace, RowWindow{q_len, t0, ct}, true, stream);
+                                   (float*)workspace, RowWindow{q_len, t0, ct}, true, nullptr, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

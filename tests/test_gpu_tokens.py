@@ -34,8 +34,9 @@ CASES = [
     (SPECS[2].replace(batch=2, ctx_len=64 * 5 + 3), 2048),                                    # K above every length
     (SPECS[2].replace(batch=2, ctx_len=64 * 20), 1),                                          # K = 1
     (SPECS[2].replace(batch=2, ctx_len=64 * 90 + 5), 700),                                    # rows > 4096
+    (SPECS[2].replace(batch=2, ctx_len=64 * 700 + 3), 1500),                                  # rows > 32768: parts
 ]
-IDS = ["g8_bs64", "ragged", "bs128_d64_g16", "k_all", "k1", "long_rows"]
+IDS = ["g8_bs64", "ragged", "bs128_d64_g16", "k_all", "k1", "long_rows", "parts"]
 
 
 @pytest.mark.parametrize("spec,K", CASES, ids=IDS)
@@ -103,6 +104,23 @@ def test_two_level_step_matches_oracle(spec, K):
     same = np.repeat((~(gi != r["token_idx"]).any(-1) & blk_same)[:, :, 0], spec.group_size, axis=1)
     check_out(to_np(out)[same], r["out"][:, :, 0][same], "bf16", "two-level out")
     assert np.abs(lse.cpu().numpy()[same] - r["lse"][:, :, 0][same]).max() <= 2e-3
+
+
+@pytest.mark.parametrize("ctx,K", [(64 * 700 + 3, 1500), (64 * 300 + 9, 999)], ids=["parts", "one_pass"])
+def test_token_level_ties_keep_lower_tokens(ctx, K):
+    """Every key of the cache equal: every candidate scores the same, so the kept tokens must
+    be the K lowest positions, exactly; rows past 32768 candidates are selected in parts and
+    then over the parts' lists, and the ties must still resolve as in one pass."""
+    spec = SPECS[2].replace(batch=2, ctx_len=ctx)
+    w = make_workload(spec, 64, device=DEV)
+    w.k_cache.copy_(w.k_cache[0, 0, 0].expand_as(w.k_cache))
+    B, Hq, _, D = w.q.shape
+    tok = torch.full((B, spec.num_kv_heads, K), -7, dtype=torch.int32, device=DEV)
+    note(f"[case] token-level ties ctx={ctx} K={K}")
+    bsg.token_topk(w.q[:, :, 0].contiguous(), w.kv_lens, w.k_cache, w.page_table, tok)
+    torch.cuda.synchronize()
+    want = torch.arange(K, dtype=torch.int32, device=DEV).expand_as(tok)
+    assert torch.equal(tok, want)
 
 
 def test_token_attention_on_oracle_lists():
