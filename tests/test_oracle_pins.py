@@ -682,3 +682,63 @@ def test_two_level_reduces_to_block_and_to_token_selection():
             blocks = set(int(j) for j in r4["block_idx"][b, g, 0] if j >= 0)
             toks = [int(s) for s in r4["token_idx"][b, g, 0] if s >= 0]
             assert len(toks) == 70 and all(s // bs in blocks for s in toks)
+
+
+# prefill rows of the token forms: every position of a prompt is a row at its own position
+def test_token_topk_of_every_prefill_position_is_dense_causal_gqa():
+    """K at least the prompt length: every row keeps every earlier token, so the token-level
+    prefill is dense causal GQA attention (torch's scaled_dot_product_attention, is_causal)."""
+    spec = SPECS[0].replace(seq_len=150)
+    w = make_workload(spec, 35)
+    q, kp, vp, pt, kv = _np(w)
+    L = kv[0]
+    sc = O.token_scores(q, kp, pt, kv)
+    idx = O.select_tokens(sc, L)
+    for t in (0, 1, 77, L - 1):                     # row t keeps tokens 0..t, ascending
+        assert list(idx[0, 0, t, :t + 1]) == list(range(t + 1)) and np.all(idx[0, 0, t, t + 1:] == -1)
+    out, lse = O.token_attention(q, kp, vp, pt, kv, idx, 1.0 / math.sqrt(spec.head_dim))
+    K = O.gather_tokens(kp, pt[0], L).astype(np.float64)
+    V = O.gather_tokens(vp, pt[0], L).astype(np.float64)
+    G = spec.num_q_heads // spec.num_kv_heads
+    ref = _sdpa_dense(q.astype(np.float64), np.repeat(K, G, axis=0)[None], np.repeat(V, G, axis=0)[None],
+                      causal=True, scale=1.0 / math.sqrt(spec.head_dim))
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_token_prefill_rows_equal_decode_steps():
+    """Prefill row t (queries at the end of a longer context included) is the decode step at
+    kv_len = position + 1 with that query: the same scores (up to the summation order of the
+    two matrix products), kept tokens and output."""
+    spec = SPECS[0].replace(seq_len=64 * 3 + 20, q_len=90)
+    w = make_workload(spec, 36)
+    q, kp, vp, pt, kv = _np(w)
+    L, ql, K = kv[0], q.shape[2], 37
+    sc = O.token_scores(q, kp, pt, kv)
+    idx = O.select_tokens(sc, K)
+    out, lse = O.token_attention(q, kp, vp, pt, kv, idx, 0.125)
+    for t in (0, 5, ql - 1):
+        p = L - ql + t
+        r = O.decode_tokens_reference(q[:, :, t:t + 1], kp, vp, pt, [p + 1], K, 0.125)
+        np.testing.assert_allclose(r["scores"][:, :, 0, :p + 1], sc[:, :, t, :p + 1], rtol=1e-13, atol=1e-12)
+        assert np.array_equal(r["token_idx"][:, :, 0], idx[:, :, t])
+        np.testing.assert_allclose(r["out"][:, :, 0], out[:, :, t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(r["lse"][:, :, 0], lse[:, :, t], rtol=1e-12, atol=1e-12)
+
+
+def test_two_level_prefill_with_whole_blocks_is_block_prefill():
+    """Two level at prefill, K = k * bs: every token of each row's kept blocks is kept, which
+    is the block-level prefill of the same rows."""
+    spec = SPECS[0].replace(seq_len=64 * 5 + 13, top_k=3)
+    w = make_workload(spec, 37)
+    q, kp, vp, pt, kv = _np(w)
+    bs, k = spec.page_size, spec.top_k
+    r = O.prefill_reference(q, kp, vp, pt, kv, bs, k, "f32")
+    sc = O.token_scores(q, kp, pt, kv, block_idx=r["block_idx"])
+    idx = O.select_tokens(sc, k * bs)
+    for t in (0, 64, q.shape[2] - 1):                # the kept blocks' valid tokens, ascending
+        want = sorted(s for j in r["block_idx"][0, 0, t] if j >= 0
+                      for s in range(j * bs, min((j + 1) * bs, t + 1)))
+        assert [int(s) for s in idx[0, 0, t] if s >= 0] == want
+    out, lse = O.token_attention(q, kp, vp, pt, kv, idx, 1.0 / math.sqrt(spec.head_dim))
+    np.testing.assert_allclose(out, r["out"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, r["lse"], rtol=1e-10, atol=1e-12)
