@@ -937,7 +937,7 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
     float scale, int32_t* __restrict__ block_idx, bf16_t* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv,
     int top_k, int num_pages, int pt_stride, gate_args ga, const float* __restrict__ rep_scales,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, int nunits, int S,
-    float* __restrict__ part) {
+    float* __restrict__ part, int select_only) {
   constexpr int ES = F8 ? 1 : 2;             // bytes per cache element
   constexpr int VPP = F8 ? 16 : 8;           // values per 16-byte piece of a representative
   constexpr int SEG = D / VPP;               // lanes per representative
@@ -1238,6 +1238,7 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
   }
   __syncthreads();
   if (sm == 0 && tid < top_k) block_idx[((size_t)b * Hkv + g) * top_k + tid] = tid <= cnt ? wl[tid] : -1;
+  if (select_only) return;                             // the block selection alone
   // pages in the attention order: the own block first (its page from the table), then the
   // kept blocks ascending (their pages from the scan)
   if (tid <= cnt) {
@@ -1479,7 +1480,7 @@ static hipError_t launch_decode_unit(const bsg_dims& d, const void* q, const int
     if (ea != hipSuccess) return ea;                                                                                \
     hipLaunchKernelGGL(kfn, grid, dim3(DU_NT), smem, stream, (const bf16_t*)q, kv_lens, block_cache, k_cache,       \
                        v_cache, page_table, scale, block_idx, (bf16_t*)out, lse, d.num_q_heads, d.num_kv_heads,     \
-                       d.top_k, d.num_pages, d.pt_stride, ga, rep_scales, k_scales, v_scales, nunits, S, part);    \
+                       d.top_k, d.num_pages, d.pt_stride, ga, rep_scales, k_scales, v_scales, nunits, S, part, 0); \
   } while (0)
 #define BSG_DU_F(DD, BB)                 \
   do {                                   \
@@ -1502,6 +1503,33 @@ static hipError_t launch_decode_unit(const bsg_dims& d, const void* q, const int
   else
     hipLaunchKernelGGL((attn_decode_merge_kernel<bf16_t, 64>), mgrid, dim3(64), 0, stream, part, (bf16_t*)out, lse,
                        d.num_q_heads, d.num_kv_heads, S, ga);
+  return hipGetLastError();
+}
+
+// The scan and exact block selection of decode_unit_kernel alone, one workgroup per (sequence,
+// group), for bsg_group_score_topk at q_len = 1 (and the two-level decode step's block stage).
+hipError_t launch_decode_unit_select(const bsg_dims& d, const void* q, const int32_t* kv_lens,
+                                     const void* block_cache, const int32_t* page_table, int32_t* block_idx,
+                                     hipStream_t stream) {
+  const size_t smem = decode_unit_smem(d);
+  const int nunits = d.batch * d.num_kv_heads;
+  dim3 grid((nunits + 7) / 8 * 8);
+#define BSG_DUS(DD, BB)                                                                                             \
+  do {                                                                                                              \
+    auto kfn = decode_unit_kernel<DD, BB, false>;                                                                   \
+    hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);   \
+    if (ea != hipSuccess) return ea;                                                                                \
+    hipLaunchKernelGGL(kfn, grid, dim3(DU_NT), smem, stream, (const bf16_t*)q, kv_lens, block_cache, nullptr,       \
+                       nullptr, page_table, 1.0f, block_idx, nullptr, nullptr, d.num_q_heads, d.num_kv_heads,       \
+                       d.top_k, d.num_pages, d.pt_stride, gate_args{nullptr, 0, nullptr}, nullptr, nullptr, nullptr, \
+                       nunits, 1, nullptr, 1);                                                                      \
+  } while (0)
+  if (d.head_dim == 128) {
+    if (d.page_size == 64) BSG_DUS(128, 64); else BSG_DUS(128, 128);
+  } else {
+    if (d.page_size == 64) BSG_DUS(64, 64); else BSG_DUS(64, 128);
+  }
+#undef BSG_DUS
   return hipGetLastError();
 }
 

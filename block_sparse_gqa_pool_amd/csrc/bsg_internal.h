@@ -40,6 +40,10 @@ hipError_t launch_group_score_topk_fused(const bsg_dims& d, const void* q, int q
 
 // Decode scoring + selection (q_len = 1): chunked block-cache scan + tournament merge.
 bool decode_select_supported(const bsg_dims& d, int q_len);
+bool decode_unit_supported(const bsg_dims& d);
+hipError_t launch_decode_unit_select(const bsg_dims& d, const void* q, const int32_t* kv_lens,
+                                     const void* block_cache, const int32_t* page_table, int32_t* block_idx,
+                                     hipStream_t stream);
 size_t decode_select_workspace_bytes(const bsg_dims& d);
 hipError_t launch_decode_select(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
                                 const int32_t* page_table, int32_t* block_idx, void* workspace, hipStream_t stream);

@@ -240,6 +240,8 @@ hipError_t launch_decode_score_chunks(const bsg_dims& d, const void* q, const in
 
 hipError_t launch_decode_select(const bsg_dims& d, const void* q, const int32_t* kv_lens, const void* block_cache,
                                 const int32_t* page_table, int32_t* block_idx, void* workspace, hipStream_t stream) {
+  if (decode_unit_supported(d))                    // rows of at most 4096 blocks: one kernel
+    return launch_decode_unit_select(d, q, kv_lens, block_cache, page_table, block_idx, stream);
   const int nchunks = decode_select_nchunks(d);
   const int m = d.top_k - 1;
   uint64_t* lists = (uint64_t*)workspace;
