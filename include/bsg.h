@@ -234,10 +234,12 @@ int bsg_sparse_attn_decode(const bsg_dims* dims, const void* q, const int32_t* k
 /*
  * bsg_decode_step -- one whole decode step: group scores against the block
  * cache, causal top-k selection, and sparse attention over the selected
- * blocks, for q_len = 1.  Same results as bsg_group_score_topk followed by
- * bsg_sparse_attn_decode (the selection is also written to block_idx,
- * [B, Hkv, top_k]), but the selection is finished inside the attention
- * kernel, which saves one launch and one pass over the selection lists.
+ * blocks, for q_len = 1.  The same selection as bsg_group_score_topk (also
+ * written to block_idx, [B, Hkv, top_k]) and the same attention as
+ * bsg_sparse_attn_decode on it (outputs within bf16 rounding: the split of the
+ * pages over workgroups differs).  Page-table rows of at most 4096 blocks run
+ * scan, selection and attention in one kernel plus a merge of partials; longer
+ * rows scan in chunks and finish the selection inside the attention kernel.
  * Follows the Ling 2.0 page, "Summarizing the Breakthrough" (decode reads the
  * block cache, picks the top-k blocks and fetches only those).
  * q: [B, Hq, D]; out: [B, Hq, D]; lse: fp32 [B, Hq] or NULL.  `workspace`
