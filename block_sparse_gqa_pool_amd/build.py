@@ -61,13 +61,26 @@ def lib_path(variant: str = "release") -> str:
     return os.path.join(PKG, VARIANTS[variant][0])
 
 
+def source_hash() -> str:
+    """Hash of the library's sources and headers (what a build was made from)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*")) + glob.glob(os.path.join(INCLUDE, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def is_stale(variant: str = "release") -> bool:
-    """True when the variant's library is missing or older than a source or header."""
+    """True when the variant's library is missing or was built from other sources (the hash
+    written beside it at build time differs from the sources' hash now)."""
     lib = lib_path(variant)
-    if not os.path.exists(lib):
+    stamp = lib + ".srchash"
+    if not (os.path.exists(lib) and os.path.exists(stamp)):
         return True
-    srcs = glob.glob(os.path.join(CSRC, "*")) + glob.glob(os.path.join(INCLUDE, "*.h"))
-    return max(os.path.getmtime(f) for f in srcs) > os.path.getmtime(lib)
+    with open(stamp) as fh:
+        return fh.read().strip() != source_hash()
 
 
 def asan_runtime() -> str:
@@ -93,6 +106,8 @@ def build(verbose: bool = False, jobs: int = 8, variant: str = "release") -> str
     tmp = lib + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *lflags, *objs, "-o", tmp], verbose)
     os.replace(tmp, lib)
+    with open(lib + ".srchash", "w") as fh:
+        fh.write(source_hash() + "\n")
     return lib
 
 
