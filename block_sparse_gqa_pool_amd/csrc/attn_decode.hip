@@ -204,14 +204,22 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
     const void* __restrict__ v_cache, const int32_t* __restrict__ page_table, int32_t* __restrict__ block_idx,
     const uint64_t* __restrict__ lists, float scale, float* __restrict__ part, int Hq, int Hkv, int top_k,
     int num_pages, int pt_stride, int nwg, int ppw, int nchunks, int lt, const float* __restrict__ k_scales,
-    const float* __restrict__ v_scales) {
+    const float* __restrict__ v_scales, int nunits) {
   constexpr int NDS = D / 32;          // k-steps of the score product
   constexpr int NDT = D / 16;          // 16-wide d tiles of the output
   constexpr int VS = D + DM_VPAD;      // LDS row stride of V (elements)
   constexpr int SUB = 64;              // keys per sub-block
   extern __shared__ __attribute__((aligned(16))) unsigned char dm_smem[];
   const int G = Hq / Hkv;
-  const int g = blockIdx.y, b = blockIdx.z;
+  // workgroup x is workgroup (x / 8) % nwg of unit (x / 8 nwg) * 8 + x % 8: the nwg workgroups
+  // of a (sequence, group) unit sit 8 apart in dispatch order, so on the same XCD (workgroups
+  // go to the eight XCDs in turn), and the unit's selection lists come from memory once into
+  // that XCD's L2
+  const int xw = blockIdx.x;
+  const int split = (xw >> 3) % nwg;
+  const int unit = (xw / (8 * nwg)) * 8 + (xw & 7);
+  if (unit >= nunits) return;
+  const int g = unit % Hkv, b = unit / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, qd = lane >> 4;
   bf16_t* Vs = reinterpret_cast<bf16_t*>(dm_smem) + (size_t)wave * SUB * VS;
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
   for (int i = 0; i < NDT; i++) o[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int vtr = (16 * 0 + 4 * qd + ((lane & 15) >> 2)) * VS + 4 * (lane & 3);   // tr-read base (key, d)
 
-  const int e0 = (blockIdx.x * 4 + wave) * ppw;
+  const int e0 = (split * 4 + wave) * ppw;
   const int e1 = min(e0 + min(ppw, 2), top_k);         // ppw is 1 or 2
   // the wave's block ids and their pages, fetched together
   int jv[2], pv[2];
@@ -419,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (FUSED && blockIdx.x == 0) {  // the selection, ascending, to block_idx (own block last)
+  if (FUSED && split == 0) {  // the selection, ascending, to block_idx (own block last)
     for (int i = tid; i < top_k; i += 256) {
       const int v = wl[i];
       int r = i;
@@ -453,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
   }
   __syncthreads();
   const size_t pstride = (size_t)G * (D + 2);
-  float* myp = part + (((size_t)b * Hkv + g) * nwg + blockIdx.x) * pstride;
+  float* myp = part + (((size_t)b * Hkv + g) * nwg + split) * pstride;
   for (int e = tid; e < G * D; e += 256) {
     const int h = e / D, d = e % D;
     float mm = -INFINITY;
@@ -809,7 +817,8 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
     const size_t smem_v = (size_t)4 * 64 * (d.head_dim + DM_VPAD) * sizeof(bf16_t);
     const size_t smem_m = (size_t)4 * 16 * (d.head_dim + 2) * sizeof(float);
     const size_t smem = smem_v > smem_m ? smem_v : smem_m;
-    dim3 grid(nwg, d.num_kv_heads, d.batch);
+    const int nunits = d.batch * d.num_kv_heads;
+    dim3 grid((nunits + 7) / 8 * 8 * nwg);
 #define BSG_DM(DD, BB)                                                                                            \
   do {                                                                                                             \
     auto kfn = attn_decode_mfma_kernel<DD, BB, false, false>;                                                      \
@@ -818,7 +827,7 @@ hipError_t launch_attn_decode(const bsg_dims& d, const void* q, const int32_t* k
     hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, (const bf16_t*)k_cache,      \
                        (const bf16_t*)v_cache, page_table, const_cast<int32_t*>(block_idx), nullptr, scale, part,  \
                        d.num_q_heads, d.num_kv_heads, d.top_k, d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d),  \
-                       0, 1, nullptr, nullptr);                                                                    \
+                       0, 1, nullptr, nullptr, nunits);                                                            \
   } while (0)
     if (d.head_dim == 128) {
       if (d.page_size == 64) BSG_DM(128, 64); else BSG_DM(128, 128);
@@ -1578,7 +1587,8 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
   int lt = 0;
   const size_t smem = decode_step_smem(d, &lt);
   if (smem > 150 * 1024) return hipErrorInvalidValue;
-  dim3 grid(nwg, d.num_kv_heads, d.batch);
+  const int nunits = d.batch * d.num_kv_heads;
+  dim3 grid((nunits + 7) / 8 * 8 * nwg);
 #define BSG_DF(DD, BB, F)                                                                                         \
   do {                                                                                                             \
     auto kfn = attn_decode_mfma_kernel<DD, BB, true, F>;                                                           \
@@ -1586,7 +1596,7 @@ hipError_t launch_decode_step(const bsg_dims& d, const void* q, const int32_t* k
     if (ea != hipSuccess) return ea;                                                                               \
     hipLaunchKernelGGL(kfn, grid, dim3(256), smem, stream, (const bf16_t*)q, kv_lens, k_cache, v_cache,            \
                        page_table, block_idx, lists, scale, part, d.num_q_heads, d.num_kv_heads, d.top_k,           \
-                       d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d), nchunks, lt, k_scales, v_scales);         \
+                       d.num_pages, d.pt_stride, nwg, decode_mfma_ppw(d), nchunks, lt, k_scales, v_scales, nunits); \
   } while (0)
 #define BSG_DF_F(DD, BB)                 \
   do {                                   \

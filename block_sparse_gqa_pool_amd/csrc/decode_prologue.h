@@ -40,16 +40,18 @@ __device__ void decode_select_prologue(const uint64_t* __restrict__ lists_row, i
     *counter = 0;
     *tau_s = 1ull;
   }
-  // lists -> LDS, 4 loads in flight per thread; a list's first T keys also go to tops
-  for (int e0 = 0; e0 < NL; e0 += 4 * 256) {
-    uint64_t v[4];
+  // lists -> LDS, 16 loads in flight per thread (32 KiB per workgroup round trip: the lists
+  // of a 16K-block row take two); a list's first T keys also go to tops
+  constexpr int LU = 16;
+  for (int e0 = 0; e0 < NL; e0 += LU * 256) {
+    uint64_t v[LU];
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
+    for (int u = 0; u < LU; u++) {
       const int e = e0 + u * 256 + tid;
       v[u] = e < NL ? lists_row[e] : 0ull;
     }
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
+    for (int u = 0; u < LU; u++) {
       const int e = e0 + u * 256 + tid;
       if (e < NL) {
         L[e] = v[u];
