@@ -32,6 +32,7 @@ namespace bsg {
 namespace {
 constexpr int TS_CH = 64;      // candidates per score workgroup
 constexpr int TS_HPW = 4;      // KV heads per score workgroup
+constexpr int TS_GMAX = 16;    // query heads per KV head the score workgroup takes
 constexpr int TK_NT = 1024;    // threads of the selection workgroup
 constexpr int TK_NW = TK_NT / 64;
 constexpr int TK_BINS = 2048;  // radix bins per level (11 bits)
@@ -72,17 +73,38 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   constexpr int SEG = D / 8;                       // lanes per key row
   constexpr int PPH = TS_CH * SEG;                 // 16-byte pieces per head
   constexpr int NP = TS_HPW * PPH / 256;           // pieces per thread
+  constexpr int QP = TS_HPW * TS_GMAX * (D / 8) / 256;   // query pieces per thread, at most
   __shared__ float qs[TS_HPW][D];
+  __shared__ uint4 qraw[TS_HPW * TS_GMAX * (D / 8)];     // the workgroup's query rows, raw bf16
   const int c0 = blockIdx.x * TS_CH, g0 = blockIdx.y * TS_HPW, rl = blockIdx.z;
   const int b = rw.seq(rl), t = rw.pos(rl);
   if (t >= rw.T) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int G = Hq / Hkv;
   const int pos = kv_lens[b] - rw.T + t;
-  // per head of this workgroup: the chunk's first token and key rows (a chunk is 64
-  // consecutive tokens of one block; at token level the same block for every head)
+  // token level: a chunk wholly past the query's position lies past what the selection reads
+  // (the position rounded up to 64), so it is neither scored nor written
+  if (!TWO && c0 > pos) return;
+  // the query rows first (one round trip, ahead of the key loads in the in-order load count).
+  // The workgroup's TS_HPW groups own the consecutive heads g0 G .. (g0 + TS_HPW) G - 1; piece
+  // i is 8 dims of head g0 G + i / (D / 8).  With G > TS_GMAX each summing thread reads its
+  // rows itself, below.
+  const bool qlds = G <= TS_GMAX;
+  const int nq = qlds ? min(TS_HPW * G, Hq - g0 * G) * (D / 8) : 0;
+  uint4 qv[QP];
+#pragma unroll
+  for (int u = 0; u < QP; u++) {
+    const int i = u * 256 + tid;
+    qv[u] = make_uint4(0, 0, 0, 0);
+    if (i < nq)
+      qv[u] = *reinterpret_cast<const uint4*>(q + (((size_t)b * Hq + g0 * G + i / (D / 8)) * rw.T + t) * D +
+                                              8 * (i % (D / 8)));
+  }
+  // per head of this workgroup: the chunk's first token and the element offset of its key rows
+  // (a chunk is 64 consecutive tokens of one block; at token level the same block for every
+  // head); all workgroup-uniform
   int tok0[TS_HPW];
-  const bf16_t* rows[TS_HPW];
+  size_t roff[TS_HPW];
 #pragma unroll
   for (int hh = 0; hh < TS_HPW; hh++) {
     const int g = g0 + hh;
@@ -91,46 +113,56 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     const int j = t0 >= 0 ? t0 / BS : -1;
     const bool live = j >= 0 && j < pt_stride && t0 <= pos;
     const int p = live ? page_id(page_table[(size_t)b * pt_stride + j], num_pages) : 0;
-    tok0[hh] = live ? t0 : -1;
-    rows[hh] = k_cache + (((size_t)p * Hkv + (live ? g : 0)) * BS + (live ? t0 % BS : 0)) * D;
+    tok0[hh] = __builtin_amdgcn_readfirstlane(live ? t0 : -1);
+    roff[hh] = (((size_t)p * Hkv + (live ? g : 0)) * BS + (live ? t0 % BS : 0)) * D / 8;
   }
+  // the keys: head hh's 64 rows are PPH consecutive 16-byte pieces, UPH per thread
+  constexpr int UPH = NP / TS_HPW;
+  const uint4* kc4 = reinterpret_cast<const uint4*>(k_cache);
   uint4 raw[NP];
 #pragma unroll
-  for (int u = 0; u < NP; u++) {
-    const int pi = u * 256 + tid;
-    const int hh = pi / PPH;
-    raw[u] = tok0[hh] >= 0 ? *reinterpret_cast<const uint4*>(rows[hh] + (size_t)(pi % PPH) * 8)
-                           : make_uint4(0, 0, 0, 0);
+  for (int hh = 0; hh < TS_HPW; hh++) {
+#pragma unroll
+    for (int v = 0; v < UPH; v++) raw[hh * UPH + v] = make_uint4(0, 0, 0, 0);
+    if (tok0[hh] >= 0) {
+#pragma unroll
+      for (int v = 0; v < UPH; v++) raw[hh * UPH + v] = kc4[roff[hh] + v * 256 + tid];
+    }
   }
-  // group-summed queries (fp32, heads in order), 8 dims per thread from 16-byte loads
+#pragma unroll
+  for (int u = 0; u < QP; u++)
+    if (u * 256 + tid < nq) qraw[u * 256 + tid] = qv[u];
+  __syncthreads();
+  // group-summed queries (fp32, heads in order), 8 dims per thread
   if (tid < TS_HPW * (D / 8)) {
-    const int hh = tid / (D / 8), d0 = 8 * (tid % (D / 8)), g = g0 + hh;
+    const int hh = tid / (D / 8), d8 = tid % (D / 8);
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    if (g < Hkv)
-      for (int h = 0; h < G; h++) {
-        const uint4 v = *reinterpret_cast<const uint4*>(q + (((size_t)b * Hq + g * G + h) * rw.T + t) * D + d0);
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    for (int h = 0; h < G && g0 + hh < Hkv; h++) {
+      const uint4 v = qlds ? qraw[(hh * G + h) * (D / 8) + d8]
+                           : *reinterpret_cast<const uint4*>(q + (((size_t)b * Hq + (g0 + hh) * G + h) * rw.T + t) * D +
+                                                             8 * d8);
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          acc[2 * i] += __uint_as_float(wd[i] << 16);
-          acc[2 * i + 1] += __uint_as_float(wd[i] & 0xffff0000u);
-        }
+      for (int i = 0; i < 4; i++) {
+        acc[2 * i] += __uint_as_float(wd[i] << 16);
+        acc[2 * i + 1] += __uint_as_float(wd[i] & 0xffff0000u);
       }
+    }
 #pragma unroll
-    for (int i = 0; i < 8; i++) qs[hh][d0 + i] = acc[i];
+    for (int i = 0; i < 8; i++) qs[hh][8 * d8 + i] = acc[i];
   }
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < NP; u++) {
-    const int pi = u * 256 + tid;
-    const int hh = pi / PPH, r = (pi % PPH) / SEG, w = pi % SEG;
-    const float* qv = &qs[hh][w * 8];
+    const int hh = u / UPH, pp = (u % UPH) * 256 + tid;    // piece pp of head hh's rows
+    const int r = pp / SEG, w = pp % SEG;
+    const float* qvs = &qs[hh][w * 8];
     const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      s = fmaf(qv[2 * i], __uint_as_float(wd[i] << 16), s);
-      s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
+      s = fmaf(qvs[2 * i], __uint_as_float(wd[i] << 16), s);
+      s = fmaf(qvs[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
     }
     s = seg_sum_dpp<SEG>(s);
     const int g = g0 + hh;
