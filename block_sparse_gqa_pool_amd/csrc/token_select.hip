@@ -137,15 +137,20 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   if (tid < TS_HPW * (D / 8)) {
     const int hh = tid / (D / 8), d8 = tid % (D / 8);
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int h = 0; h < G && g0 + hh < Hkv; h++) {
-      const uint4 v = qlds ? qraw[(hh * G + h) * (D / 8) + d8]
-                           : *reinterpret_cast<const uint4*>(q + (((size_t)b * Hq + (g0 + hh) * G + h) * rw.T + t) * D +
-                                                             8 * d8);
+    auto add8 = [&](const uint4 v) {
       const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         acc[2 * i] += __uint_as_float(wd[i] << 16);
         acc[2 * i + 1] += __uint_as_float(wd[i] & 0xffff0000u);
+      }
+    };
+    if (g0 + hh < Hkv) {
+      if (qlds) {
+        for (int h = 0; h < G; h++) add8(qraw[(hh * G + h) * (D / 8) + d8]);
+      } else {
+        const uint4* qg = reinterpret_cast<const uint4*>(q);
+        for (int h = 0; h < G; h++) add8(qg[(((size_t)b * Hq + (g0 + hh) * G + h) * rw.T + t) * (D / 8) + d8]);
       }
     }
 #pragma unroll

@@ -106,6 +106,27 @@ def test_two_level_step_matches_oracle(spec, K):
     assert np.abs(lse.cpu().numpy()[same] - r["lse"][:, :, 0][same]).max() <= 2e-3
 
 
+@pytest.mark.parametrize("hq,hkv,D", [(80, 4, 64), (36, 6, 128)], ids=["g20", "hkv6"])
+def test_token_selection_other_groupings(hq, hkv, D):
+    """Token-level selection alone (bsg_token_topk) at groupings the token attention does not
+    take or that leave a score workgroup's last groups empty: with G = 20 each summing thread
+    reads its query rows itself (more than the 16 per group staged in LDS); with Hkv = 6 the
+    second workgroup of four groups has two."""
+    spec = SPECS[2].replace(batch=2, ctx_len=64 * 30 + 5, num_q_heads=hq, num_kv_heads=hkv, head_dim=D)
+    w = make_workload(spec, 65, device=DEV, tail_fill=float("nan"))
+    note(f"[case] token-level selection Hq={hq} Hkv={hkv} D={D}")
+    B, Hq, _, D = w.q.shape
+    K = 300
+    tok = torch.full((B, hkv, K), -7, dtype=torch.int32, device=DEV)
+    bsg.token_topk(w.q[:, :, 0].contiguous(), w.kv_lens, w.k_cache, w.page_table, tok)
+    torch.cuda.synchronize()
+    q, kp, vp, pt, kv = _host(w)
+    r = O.decode_tokens_reference(q, kp, vp, pt, kv, K, 1.0 / math.sqrt(D))
+    bad, exempt = compare_token_selection(tok.cpu().numpy()[:, :, None, :], r["token_idx"], r["scores"], K)
+    note(f"  exempt {len(exempt)}, bad {len(bad)}")
+    assert not bad, bad
+
+
 @pytest.mark.parametrize("ctx,K", [(64 * 700 + 3, 1500), (64 * 300 + 9, 999)], ids=["parts", "one_pass"])
 def test_token_level_ties_keep_lower_tokens(ctx, K):
     """Every key of the cache equal: every candidate scores the same, so the kept tokens must
