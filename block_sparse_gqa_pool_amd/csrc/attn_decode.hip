@@ -236,8 +236,8 @@ __global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(
     const int cnt = min(m, min(own, pt_stride));
     if (cnt > 0) {
       uint64_t* Lk = reinterpret_cast<uint64_t*>(dm_smem);
-      decode_select_prologue(lists + ((size_t)b * Hkv + g) * nchunks * m, nchunks, m, lt, cnt, Lk,
-                             Lk + (((size_t)nchunks * m + 1) & ~(size_t)1), wl, &cnt_s, &tau_s);
+      decode_select_prologue(lists + ((size_t)b * Hkv + g) * nchunks * m, nchunks, m, lt, cnt, Lk, wl, &cnt_s,
+                             &tau_s);
     }
     if (tid == 0) wl[cnt] = own;
     for (int i = cnt + 1 + tid; i < top_k; i += 256) wl[i] = -1;

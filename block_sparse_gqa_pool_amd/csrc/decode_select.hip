@@ -186,8 +186,8 @@ __global__ __launch_bounds__(256) void decode_select_kernel(const uint64_t* __re
   const int cnt = min(m, min(own, pt_stride));
   int32_t* out = block_idx + (size_t)row * top_k;
   if (cnt > 0) {
-    decode_select_prologue(lists + (size_t)row * nchunks * m, nchunks, m, lt, cnt, dsel_smem,
-                           dsel_smem + (((size_t)nchunks * m + 1) & ~(size_t)1), kept, &counter_s, &tau_s);
+    decode_select_prologue(lists + (size_t)row * nchunks * m, nchunks, m, lt, cnt, dsel_smem, kept, &counter_s,
+                           &tau_s);
     if (tid < cnt) {                                         // ascending
       const int ji = kept[tid];
       int r2 = 0;
