@@ -189,8 +189,11 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 // last candidate rounded up to 64 (what the selection reads).
 constexpr int TG_RANGE = 2048;                    // candidates per workgroup of token_score_gemm_kernel
 
+// Three waves per SIMD at D = 128 (the three query terms take 96 registers): with the plain
+// launch bound the compiler aimed higher and spilled 12 registers to scratch.
 template <int D, int BS>
-__global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4, D == 128 ? 3 : 8))) void token_score_gemm_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
     const int32_t* __restrict__ page_table, float* __restrict__ scores, int nc, int Hq, int Hkv, int num_pages,
     int pt_stride, RowWindow rw) {
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
       }
   }
 
-  auto issue = [&](int cc, uint4* v) {
+  auto issue = [&](int cc, uint4 (&v)[NPC]) {
     const int s0 = cc * CH;
     const int j = min(s0 / BS, pt_stride - 1);
     const int p = page_id(page_table[(size_t)b * pt_stride + j], num_pages);
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void token_score_gemm_kernel(
       v[u] = *reinterpret_cast<const uint4*>(base + (size_t)(e / CPR) * D + 8 * (e % CPR));
     }
   };
-  auto stash = [&](const uint4* v, int buf) {
+  auto stash = [&](const uint4 (&v)[NPC], int buf) {
 #pragma unroll
     for (int u = 0; u < NPC; u++) {
       const int e = u * 256 + tid;
