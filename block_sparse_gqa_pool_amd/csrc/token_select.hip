@@ -484,6 +484,10 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
   const uint32_t tau = all ? 1u : prefix;          // all: every candidate (key >= 1)
   const uint32_t take_eq = all ? 0u : (uint32_t)K - above;
   const bool rank_eq = !all && take_eq < m_eq;     // ties at tau split by index
+  // the kept ids go through LDS (the histogram, free by now) when they fit, so that the row is
+  // written with whole-line stores rather than a scatter of 4-byte ones
+  const bool staged = K <= TK_BINS;
+  int32_t* stage = reinterpret_cast<int32_t*>(hist);
   uint32_t out_base = 0, eq_base = 0;
   for (int cb = 0; cb < nc; cb += TK_UNR * 4 * TK_NT) {
     float4 vb[TK_UNR];
@@ -516,12 +520,23 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
       uint32_t o = out_base + tk_scan<TK_NW>(n_keep, red, &ktot);
 #pragma unroll
       for (int e = 0; e < 4; e++)
-        if (keep[e] && o < (uint32_t)K) orow[o++] = cand_token<BS, TWO>(c_off + c + e, brow);
+        if (keep[e] && o < (uint32_t)K) {
+          const int32_t id = cand_token<BS, TWO>(c_off + c + e, brow);
+          if (staged) stage[o] = id;
+          else orow[o] = id;
+          o++;
+        }
       out_base += ktot;
       eq_base += eq_tot;
     }
   }
-  for (int i = (int)out_base + tid; i < K; i += TK_NT) orow[i] = -1;
+  const int nkept = min((int)out_base, K);
+  if (staged) {
+    __syncthreads();
+    for (int i = tid; i < K; i += TK_NT) orow[i] = i < nkept ? stage[i] : -1;
+  } else {
+    for (int i = nkept + tid; i < K; i += TK_NT) orow[i] = -1;
+  }
 }
 
 // The same selection for rows of at most NT * PER candidates: one workgroup of NT threads,
@@ -646,10 +661,25 @@ __global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __res
   }
   uint32_t ktot;
   uint32_t o = tk_scan<NW>(n_keep, red, &ktot);
+  // the kept ids, in candidate order, go through LDS (the histogram, free by now) when they fit,
+  // so that the row is written with whole-line stores rather than a scatter of 4-byte ones
+  const bool staged = K <= TK_BINS;
+  int32_t* stage = reinterpret_cast<int32_t*>(hist);
 #pragma unroll
   for (int u = 0; u < PER; u++)
-    if (keep[u] && o < (uint32_t)K) orow[o++] = lst ? lst[c0 + u] : cand_token<BS, TWO>(c0 + u, brow);
-  for (int i = (int)ktot + tid; i < K; i += NT) orow[i] = -1;
+    if (keep[u] && o < (uint32_t)K) {
+      const int32_t id = lst ? lst[c0 + u] : cand_token<BS, TWO>(c0 + u, brow);
+      if (staged) stage[o] = id;
+      else orow[o] = id;
+      o++;
+    }
+  const int nkept = min((int)ktot, K);
+  if (staged) {
+    __syncthreads();
+    for (int i = tid; i < K; i += NT) orow[i] = i < nkept ? stage[i] : -1;
+  } else {
+    for (int i = nkept + tid; i < K; i += NT) orow[i] = -1;
+  }
 }
 
 size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level) {
