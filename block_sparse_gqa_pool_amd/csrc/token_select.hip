@@ -186,7 +186,9 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 // group-summed query (exact to ~2^-24 relative, as in the fused block selection), so the
 // scores are the fp32 dot products up to accumulation order.  Each lane holds 16 candidates
 // of one query; candidates past the query's position are written as -inf, up to the tile's
-// last candidate rounded up to 64 (what the selection reads).
+// last candidate rounded up to 64 (what the selection reads).  A wave's 32 x 32 tile goes
+// through LDS and out row by row (eight lanes per 128-byte row), rather than as 16-byte
+// pieces of 32 rows per store.
 constexpr int TG_RANGE = 2048;                    // candidates per workgroup of token_score_gemm_kernel
 
 // Three waves per SIMD at D = 128 (the three query terms take 96 registers): with the plain
@@ -204,6 +206,8 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4, D == 128 ? 3 : 8))) void to
   constexpr int NPC = CH * CPR / 256;              // pieces per thread per chunk
   static_assert(NPC * 256 == CH * CPR && BS % CH == 0, "chunk split");
   __shared__ __attribute__((aligned(16))) bf16_t kt[2][CH * RS];
+  constexpr int TS = CH + 4;                       // row stride of a wave's staged score tile
+  __shared__ __attribute__((aligned(16))) float stile[4][32 * TS];
   const int g = blockIdx.z % Hkv, b = blockIdx.z / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -220,7 +224,6 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4, D == 128 ? 3 : 8))) void to
   const int cbeg = blockIdx.y * TG_RANGE;               // this workgroup's candidates
   if (cbeg >= ncand) return;
   const int cend = min(ncand, cbeg + TG_RANGE);
-  const size_t rl = (size_t)b * rw.CT + (t - rw.t0);
 
   // group-summed query of position t (fp32, heads in order), as three bf16 terms; the
   // B operand of k-step ks holds dims 16 ks + 8 half .. + 7 of query col
@@ -286,7 +289,6 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4, D == 128 ? 3 : 8))) void to
   stash(v, 0);
   if (nch > 1) issue(c0 + 1, v);
   __syncthreads();
-  float* srow = scores + (rl * Hkv + g) * nc + (size_t)c0 * CH;
   for (int cc = 0; cc < nch; cc++) {
     const bf16_t* R = kt[cc & 1];
     f32x16_t sc;
@@ -299,18 +301,37 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4, D == 128 ? 3 : 8))) void to
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qm[ks], sc, 0, 0, 0);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[ks], sc, 0, 0, 0);
     }
-    if (row_ok) {
+    {
+      // the wave's 32 x 32 tile (query col, candidates) through LDS, then written row by row:
+      // eight lanes cover a row's 32 candidates (128 bytes)
+      float* tw = stile[wave];
 #pragma unroll
       for (int q4 = 0; q4 < 4; q4++) {
-        const int s0 = cc * CH + 8 * q4 + 4 * half;         // within the range
-        const int sa = c0 * CH + s0;                         // candidate position
+        const int cl = 8 * q4 + 4 * half;                   // candidate within the chunk
+        const int sa = c0 * CH + cc * CH + cl;               // candidate position
         float4 w;
         w.x = sa <= pos ? sc[4 * q4] : -INFINITY;
         w.y = sa + 1 <= pos ? sc[4 * q4 + 1] : -INFINITY;
         w.z = sa + 2 <= pos ? sc[4 * q4 + 2] : -INFINITY;
         w.w = sa + 3 <= pos ? sc[4 * q4 + 3] : -INFINITY;
-        *reinterpret_cast<float4*>(srow + s0) = w;
+        *reinterpret_cast<float4*>(tw + col * TS + cl) = w;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int it = 0; it < 4; it++) {
+        const int r = it * 8 + (lane >> 3), c4 = 4 * (lane & 7);
+        const int tr = tw0 + wave * 32 + r;
+        if (tr < tend) {
+          const size_t rlr = (size_t)b * rw.CT + (tr - rw.t0);
+          *reinterpret_cast<float4*>(scores + (rlr * Hkv + g) * nc + (size_t)(c0 + cc) * CH + c4) =
+              *reinterpret_cast<const float4*>(tw + r * TS + c4);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (cc + 1 < nch) stash(v, (cc + 1) & 1);      // the buffer chunk cc - 1 used
     if (cc + 2 < nch) issue(c0 + cc + 2, v);
