@@ -85,6 +85,9 @@ __device__ __forceinline__ void wait_copies_barrier() {
 //  * workgroups are mapped to tiles XCD by XCD: the dispatcher deals workgroups to the 8
 //    XCDs round robin, so consecutive ids are remapped to give each XCD a contiguous range
 //    of tiles, whose selections overlap, in its own L2.
+//  * the output rows leave through LDS: each lane's 8-byte pieces of its row are staged over
+//    the ring, then 16 lanes write a 256-byte row (instead of sixteen bytes of 32 rows per
+//    store).
 template <int D, int BS>
 __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
@@ -417,11 +420,14 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   }
 
   const float l = l_i + __shfl_xor(l_i, 32, 64);
-  if (!row_ok) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   const size_t row = ((size_t)b * Hq + h) * q_len + t;
-  bf16_t* op = out + row * D;
   typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  // the workgroup's 256 output rows go through LDS (the ring is free once every wave has left
+  // the loop) and out row by row, 16 lanes per 256-byte row
+  constexpr int OS = D + 8;                        // LDS row stride (bf16)
+  bf16_t* ot = reinterpret_cast<bf16_t*>(pf_smem);
+  __syncthreads();
 #pragma unroll
   for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
@@ -430,7 +436,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
       float a[4];
 #pragma unroll
       for (int x = 0; x < 4; x++) a[x] = o[dc][4 * e4 + x] * inv;
-      if (ga.g) {                                      // out = g A + (1 - g) x, one rounding
+      if (ga.g && row_ok) {                            // out = g A + (1 - g) x, one rounding
         const bf16x4_t xv = *reinterpret_cast<const bf16x4_t*>(static_cast<const bf16_t*>(ga.x) + row * D + d0);
         float g4[4];
         if (ga.per_dim) {
@@ -445,9 +451,22 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
       bf16x4_t v4;
 #pragma unroll
       for (int x = 0; x < 4; x++) v4[x] = (__bf16)a[x];   // v_cvt_pk_bf16_f32 (nearest even)
-      *reinterpret_cast<bf16x4_t*>(op + d0) = v4;
+      *reinterpret_cast<bf16x4_t*>(ot + r * OS + d0) = v4;
     }
-  if (lse && half == 0) lse[((size_t)b * Hq + h) * q_len + t] = m_i * scale + logf(l);
+  if (lse && half == 0 && row_ok) lse[row] = m_i * scale + logf(l);
+  __syncthreads();
+  constexpr int PPR = D / 8;                       // 16-byte pieces per row
+#pragma unroll
+  for (int it = 0; it < PF_ROWS * PPR / NT; it++) {
+    const int pce = it * NT + tid;
+    const int rr = pce / PPR, ch = pce % PPR;
+    const int t2 = t0 + rr / HG;
+    if (t2 < q_len) {
+      const int h2 = g * G + hs * HG + (rr % HG);
+      const size_t row2 = ((size_t)b * Hq + h2) * q_len + t2;
+      *reinterpret_cast<uint4*>(out + row2 * D + 8 * ch) = *reinterpret_cast<const uint4*>(ot + rr * OS + 8 * ch);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -540,7 +559,9 @@ hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, cons
     int nst = PF_MAX_STAGES;                       // deepest ring that fits the 160 KiB of LDS
     while (nst > 2 && fixed + nst * stage > 160 * 1024) nst--;
     const size_t smem = fixed + nst * stage;
-    if (smem <= 160 * 1024) {
+    // the output rows are staged over the ring (and the schedule after it) at the end
+    const size_t ostage = (size_t)PF_ROWS * (d.head_dim + 8) * 2;
+    if (smem <= 160 * 1024 && smem >= ostage) {
       const int n_tt = (q_len + TT - 1) / TT;
       const long long nwg = (long long)n_tt * d.num_kv_heads * (G / HG) * d.batch;
       if (nwg < (1LL << 31)) {
