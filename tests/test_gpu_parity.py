@@ -530,15 +530,18 @@ def test_decode_step_wide_page_table(case, fp8):
     assert torch.equal(lse, lse2)
 
 
-@pytest.mark.parametrize("nblk", [2000, 4000])
-def test_decode_step_selection_with_piled_keys(nblk):
+@pytest.mark.parametrize("nblk,wide", [(2000, False), (4000, False), (2000, True), (4000, True)],
+                         ids=["2000", "4000", "2000_wide_table", "4000_wide_table"])
+def test_decode_step_selection_with_piled_keys(nblk, wide):
     """Representatives whose scores grow with the block index put every kept block in the last
     groups of candidates, so many keys pass the one-workgroup step's lower bound: about 960
     (ranked directly) at 2000 blocks, about 1900 (the radix select over all keys) at 4000.
     Many scores tie exactly (bf16 representatives), and the lower index must win as in the
-    oracle."""
+    oracle.  Behind a page table wider than 4096 columns the same rows take the chunked scan
+    and the selection prologue, where the kept keys fill the last chunks' sorted lists past
+    their first 8 keys, so the prologue reads those lists on."""
     spec = SPECS[2].replace(batch=1, ctx_len=64 * nblk + 5, num_q_heads=16, num_kv_heads=2)
-    note(f"[case] decode step, piled keys, {nblk} blocks")
+    note(f"[case] decode step, piled keys, {nblk} blocks, wide table {wide}")
     w = make_workload(spec, 29).to(DEV)
     B, Hq, _, D = w.q.shape
     Hkv, k, G = spec.num_kv_heads, spec.top_k, spec.group_size
@@ -555,7 +558,11 @@ def test_decode_step_selection_with_piled_keys(nblk):
     idx = torch.full((B, Hkv, k), -7, dtype=torch.int32, device=DEV)
     out = torch.empty(B, Hq, D, dtype=w.q.dtype, device=DEV)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
-    bsg.decode_step(w.q[:, :, 0].contiguous(), w.kv_lens, cache, w.k_cache, w.v_cache, w.page_table,
+    table = w.page_table
+    if wide:
+        table = torch.zeros(w.page_table.shape[0], 4200, dtype=torch.int32, device=DEV)
+        table[:, :w.page_table.shape[1]] = w.page_table
+    bsg.decode_step(w.q[:, :, 0].contiguous(), w.kv_lens, cache, w.k_cache, w.v_cache, table,
                     1.0 / math.sqrt(D), idx, out, lse)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), r["block_idx"][:, :, 0])
