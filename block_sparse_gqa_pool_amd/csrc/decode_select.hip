@@ -10,8 +10,9 @@
 //     workgroup streams whole page rows with 16-byte loads; each 16-byte piece is dotted
 //     with the matching slice of the fp32 group-summed query and reduced over the D/8 lanes
 //     that hold one (block, group).  The query row and the chunk's page ids are fetched
-//     first, with one load each per thread, so that all row loads then go out together
-//     (no page-table round trip between them).  Then one wave per group ranks the chunk's
+//     first, with one load each per thread, so that the row loads then go out without a
+//     page-table round trip between them, four per thread at a time (more in flight measured
+//     slower: the requests congest rather than hide latency).  Then one wave per group ranks the chunk's
 //     64 keys (score, lower-index-first; rank = number of larger keys) and writes its best
 //     top_k - 1 keys, sorted descending.
 //  B. decode_select_kernel, one workgroup per (sequence, group): the exact selection of the
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(DS_NT) void decode_score_chunk_kernel(
   float* sc = ds_smem + Hkv * D;         // [Hkv][DS_CH]
   constexpr int VPP = F8 ? 16 : 8;       // values per 16-byte piece
   constexpr int SEG = D / VPP;           // lanes per (block, group)
-  constexpr int U = 8;                   // 16-byte loads in flight per thread
+  constexpr int U = 4;                   // 16-byte loads in flight per thread
   const int b = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
