@@ -52,14 +52,6 @@ __device__ __forceinline__ int tile_swz(int r) {
   else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-// Asynchronous copy global -> LDS, 16 bytes per lane: lane l's 16 bytes land at byte
-// lds_base + 16 l (gfx950 global_load_lds_dwordx4; the LDS base goes through M0).  Written
-// as inline asm so that the compiler does not serialise the later LDS reads of other ring
-// stages behind it; completion is waited for explicitly with vmcnt.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
-}
-
 // Wait until at most N of this wave's global->LDS copies are outstanding and all its LDS
 // accesses are done, then workgroup barrier.
 template <int N>

@@ -163,4 +163,13 @@ __device__ __forceinline__ void sort_ints_asc(int (&v)[N]) {
 #define BSG_DEBUG_FILE(name)
 #endif
 
+// Asynchronous copy global -> LDS, 16 bytes per lane: lane l's 16 bytes land at byte
+// lds_base + 16 l (gfx950 global_load_lds_dwordx4; the LDS base goes through M0, which the
+// compiler reserves and sets before each of its own uses).  Written as inline asm so that the
+// compiler does not serialise later LDS reads of other buffers behind it; completion is waited
+// for explicitly with vmcnt.  Lanes outside EXEC copy nothing.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
+}
+
 }  // namespace bsg

@@ -560,66 +560,17 @@ __global__ __launch_bounds__(TK_NT) void token_topk_kernel(const float* __restri
   }
 }
 
-// The same selection for rows of at most NT * PER candidates: one workgroup of NT threads,
-// each holding PER consecutive candidates' keys in registers for all three levels and the
-// compaction, with one LDS histogram.  Short rows (two-level rows of top_k blocks) take 256
-// threads, prefill rows of up to 32768 positions 1024.
+// The three radix levels and the index-order compaction of a row whose keys sit in registers,
+// PER consecutive candidates per thread from c0 = tid * PER (a list's entries when lst is set,
+// else candidate positions); the kept ids go to orow, ascending, -1 padded to K.  Every thread
+// of the workgroup calls it (it holds barriers).
 template <int BS, bool TWO, int PER, int NT>
-__global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __restrict__ scores, int nc, int K,
-                                                                  const int32_t* __restrict__ block_idx, int kblk,
-                                                                  int32_t* __restrict__ token_idx, int Hkv,
-                                                                  const int32_t* __restrict__ kv_lens, RowWindow rw,
-                                                                  int stride, int pt_stride, int full_rows,
-                                                                  const int32_t* __restrict__ part_lists) {
+__device__ __forceinline__ void tk_select_keys(const uint32_t (&key)[PER], int K, int c0,
+                                               const int32_t* __restrict__ lst, const int32_t* __restrict__ brow,
+                                               int32_t* __restrict__ orow, uint32_t* hist, uint32_t* red,
+                                               uint32_t* sel_s) {
   constexpr int NW = NT / 64;
-  __shared__ uint32_t hist[TK_BINS];
-  __shared__ uint32_t red[NW + 1];
-  __shared__ uint32_t sel_s[3];
-  const int g = blockIdx.x, rl = blockIdx.y;
-  const int b = rw.seq(rl), t = rw.pos(rl);
-  if (t >= rw.T) return;
   const int tid = threadIdx.x;
-  const float* row = scores + ((size_t)rl * Hkv + g) * stride;
-  // two level over full rows (prefill): the candidates' scores sit at their token positions
-  // in a row of every position's score (row stride `stride`), gathered through the block list.
-  // part_lists (token level, second stage): the candidates are the first stage's kept ids
-  // (ascending, -1 padded), their scores gathered from the row.
-  const bool gather = TWO && full_rows != 0;
-  const int32_t* lst = part_lists ? part_lists + ((size_t)rl * Hkv + g) * nc : nullptr;
-  const int pos = kv_lens[b] - rw.T + t;
-  const int32_t* brow = TWO ? block_idx + (((size_t)b * Hkv + g) * rw.T + t) * kblk : nullptr;
-  int32_t* orow = token_idx + (((size_t)b * Hkv + g) * rw.T + t) * K;
-  if (!lst) nc = row_candidates<TWO>(nc, pos);        // a list holds nc entries (-1 padded)
-  const int c0 = tid * PER;
-  uint32_t key[PER];
-#pragma unroll
-  for (int u = 0; u < PER / 4; u++) {
-    const int c = c0 + 4 * u;
-    float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (lst) {
-      const int4 tk4 = c < nc ? *reinterpret_cast<const int4*>(lst + c) : make_int4(-1, -1, -1, -1);
-      v.x = tk4.x >= 0 ? row[tk4.x] : -INFINITY;
-      v.y = tk4.y >= 0 ? row[tk4.y] : -INFINITY;
-      v.z = tk4.z >= 0 ? row[tk4.z] : -INFINITY;
-      v.w = tk4.w >= 0 ? row[tk4.w] : -INFINITY;
-    } else if (gather) {                           // 4 consecutive slots: 4 tokens of one block
-      const int j = c < nc ? brow[c / BS] : -1;
-      const int tk = j >= 0 ? block_id(j, pt_stride) * BS + c % BS : -1;
-      if (tk >= 0) {
-        v = *reinterpret_cast<const float4*>(row + tk);
-        v.x = tk <= pos ? v.x : -INFINITY;           // past the position: not written, not a candidate
-        v.y = tk + 1 <= pos ? v.y : -INFINITY;
-        v.z = tk + 2 <= pos ? v.z : -INFINITY;
-        v.w = tk + 3 <= pos ? v.w : -INFINITY;
-      }
-    } else if (c < nc) {
-      v = *reinterpret_cast<const float4*>(row + c);
-    }
-    key[4 * u] = tk_key(v.x);
-    key[4 * u + 1] = tk_key(v.y);
-    key[4 * u + 2] = tk_key(v.z);
-    key[4 * u + 3] = tk_key(v.w);
-  }
   uint32_t prefix = 0, pmask = 0;
   uint32_t above = 0, m_eq = 0;
   bool all = false;
@@ -703,6 +654,128 @@ __global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __res
   }
 }
 
+// The same selection for rows of at most NT * PER candidates: one workgroup of NT threads,
+// each holding PER consecutive candidates' keys in registers for all three levels and the
+// compaction, with one LDS histogram.  Short rows (two-level rows of top_k blocks) take 256
+// threads, prefill rows of up to 32768 positions 1024.
+template <int BS, bool TWO, int PER, int NT>
+__global__ __launch_bounds__(NT) void token_topk_small_kernel(const float* __restrict__ scores, int nc, int K,
+                                                                  const int32_t* __restrict__ block_idx, int kblk,
+                                                                  int32_t* __restrict__ token_idx, int Hkv,
+                                                                  const int32_t* __restrict__ kv_lens, RowWindow rw,
+                                                                  int stride, int pt_stride, int full_rows,
+                                                                  const int32_t* __restrict__ part_lists) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t red[NW + 1];
+  __shared__ uint32_t sel_s[3];
+  const int g = blockIdx.x, rl = blockIdx.y;
+  const int b = rw.seq(rl), t = rw.pos(rl);
+  if (t >= rw.T) return;
+  const int tid = threadIdx.x;
+  const float* row = scores + ((size_t)rl * Hkv + g) * stride;
+  // two level over full rows (prefill): the candidates' scores sit at their token positions
+  // in a row of every position's score (row stride `stride`), gathered through the block list.
+  // part_lists (token level, second stage): the candidates are the first stage's kept ids
+  // (ascending, -1 padded), their scores gathered from the row.
+  const bool gather = TWO && full_rows != 0;
+  const int32_t* lst = part_lists ? part_lists + ((size_t)rl * Hkv + g) * nc : nullptr;
+  const int pos = kv_lens[b] - rw.T + t;
+  const int32_t* brow = TWO ? block_idx + (((size_t)b * Hkv + g) * rw.T + t) * kblk : nullptr;
+  int32_t* orow = token_idx + (((size_t)b * Hkv + g) * rw.T + t) * K;
+  if (!lst) nc = row_candidates<TWO>(nc, pos);        // a list holds nc entries (-1 padded)
+  const int c0 = tid * PER;
+  uint32_t key[PER];
+#pragma unroll
+  for (int u = 0; u < PER / 4; u++) {
+    const int c = c0 + 4 * u;
+    float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (lst) {
+      const int4 tk4 = c < nc ? *reinterpret_cast<const int4*>(lst + c) : make_int4(-1, -1, -1, -1);
+      v.x = tk4.x >= 0 ? row[tk4.x] : -INFINITY;
+      v.y = tk4.y >= 0 ? row[tk4.y] : -INFINITY;
+      v.z = tk4.z >= 0 ? row[tk4.z] : -INFINITY;
+      v.w = tk4.w >= 0 ? row[tk4.w] : -INFINITY;
+    } else if (gather) {                           // 4 consecutive slots: 4 tokens of one block
+      const int j = c < nc ? brow[c / BS] : -1;
+      const int tk = j >= 0 ? block_id(j, pt_stride) * BS + c % BS : -1;
+      if (tk >= 0) {
+        v = *reinterpret_cast<const float4*>(row + tk);
+        v.x = tk <= pos ? v.x : -INFINITY;           // past the position: not written, not a candidate
+        v.y = tk + 1 <= pos ? v.y : -INFINITY;
+        v.z = tk + 2 <= pos ? v.z : -INFINITY;
+        v.w = tk + 3 <= pos ? v.w : -INFINITY;
+      }
+    } else if (c < nc) {
+      v = *reinterpret_cast<const float4*>(row + c);
+    }
+    key[4 * u] = tk_key(v.x);
+    key[4 * u + 1] = tk_key(v.y);
+    key[4 * u + 2] = tk_key(v.z);
+    key[4 * u + 3] = tk_key(v.w);
+  }
+  tk_select_keys<BS, TWO, PER, NT>(key, K, c0, lst, brow, orow, hist, red, sel_s);
+}
+
+// Token-level rows of 4097..TKM_NT * TKM_PER candidates (prefill windows, short decode rows):
+// the register selection above, but each workgroup walks rows blockIdx.y, + gridDim.y, ... of
+// group blockIdx.x, and the next row's scores stream into LDS (global -> LDS copies) while the
+// current row is selected, so the row's load latency is not waited for row by row.  Thread t's
+// PER consecutive candidates are copied by thread t itself: its u-th 16-byte piece lands at
+// slot u * NT + t, so that the reads back are conflict-free, consecutive lanes consecutive slots.
+template <int BS>
+__global__ __launch_bounds__(TKM_NT) void token_topk_rows_kernel(const float* __restrict__ scores, int nc, int K,
+                                                                 int32_t* __restrict__ token_idx, int Hkv,
+                                                                 const int32_t* __restrict__ kv_lens, RowWindow rw,
+                                                                 int stride, int nrows) {
+  constexpr int NT = TKM_NT, PER = TKM_PER, NW = NT / 64, NPC = PER / 4;
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t red[NW + 1];
+  __shared__ uint32_t sel_s[3];
+  extern __shared__ __attribute__((aligned(16))) float rowbuf[];   // [NPC][NT] 16-byte pieces
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int c0 = tid * PER;
+  const uint32_t buf_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)rowbuf;
+  // candidates a row's selection reads (0 for a row past the window)
+  auto row_nc = [&](int rl) {
+    const int b = rw.seq(rl), t = rw.pos(rl);
+    if (t >= rw.T) return 0;
+    return row_candidates<false>(nc, kv_lens[b] - rw.T + t);
+  };
+  auto prefetch = [&](int rl) {
+    const int n = row_nc(rl);                        // a multiple of 4
+    const float* row = scores + ((size_t)rl * Hkv + g) * stride;
+#pragma unroll
+    for (int u = 0; u < NPC; u++)
+      if (c0 + 4 * u < n)
+        lds_dma16(row + c0 + 4 * u, __builtin_amdgcn_readfirstlane(buf_base + (uint32_t)(u * NT + wave * 64) * 16u));
+  };
+  if (blockIdx.y < nrows) prefetch(blockIdx.y);
+  for (int rl = blockIdx.y; rl < nrows; rl += gridDim.y) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of the row have landed
+    __syncthreads();                                   // and every other wave's
+    const int b = rw.seq(rl), t = rw.pos(rl);
+    const int n = row_nc(rl);
+    uint32_t key[PER];
+#pragma unroll
+    for (int u = 0; u < NPC; u++) {
+      float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (c0 + 4 * u < n) v = *reinterpret_cast<const float4*>(rowbuf + 4 * (u * NT + tid));
+      key[4 * u] = tk_key(v.x);
+      key[4 * u + 1] = tk_key(v.y);
+      key[4 * u + 2] = tk_key(v.z);
+      key[4 * u + 3] = tk_key(v.w);
+    }
+    __syncthreads();                                   // the buffer is free for the next row
+    if (rl + (int)gridDim.y < nrows) prefetch(rl + gridDim.y);
+    if (t < rw.T) {                                    // workgroup-uniform
+      int32_t* orow = token_idx + (((size_t)b * Hkv + g) * rw.T + t) * K;
+      tk_select_keys<BS, false, PER, NT>(key, K, c0, nullptr, nullptr, orow, hist, red, sel_s);
+    }
+  }
+}
+
 size_t token_topk_workspace_bytes(const bsg_dims& d, bool two_level) {
   const size_t nc = two_level ? (size_t)d.top_k * d.page_size : (size_t)d.pt_stride * d.page_size;
   // rows longer than the register selection also get room for their parts' lists
@@ -746,6 +819,32 @@ static int token_topk_parts(const bsg_dims& d, int nrows, int nc, int K, bool tw
   int P = 1;
   while (P < 16 && units * P * 2 <= 256 && (long long)P * 2 * K <= TKM_NT * TKM_PER && nc / (P * 2) >= 4 * K) P *= 2;
   return P;
+}
+
+// token_topk_rows_kernel over nrows rows: one workgroup per CU (its row buffer takes 128 KiB of
+// LDS), the rows of each group dealt round robin to its share of the CUs.
+static hipError_t token_topk_rows_persistent(const bsg_dims& d, const float* scores, int nc, int K,
+                                             int32_t* token_idx, const int32_t* kv_lens, RowWindow rw, int stride,
+                                             int nrows, hipStream_t stream) {
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 256;
+  int per_group = ncu / d.num_kv_heads;
+  if (per_group < 1) per_group = 1;
+  if (per_group > nrows) per_group = nrows;
+  const size_t smem = (size_t)TKM_NT * TKM_PER * sizeof(float);
+  dim3 grid(d.num_kv_heads, per_group);
+#define BSG_TKR(BB)                                                                                              \
+  do {                                                                                                           \
+    auto kfn = token_topk_rows_kernel<BB>;                                                                       \
+    hipError_t ea = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
+    if (ea != hipSuccess) return ea;                                                                             \
+    hipLaunchKernelGGL(kfn, grid, dim3(TKM_NT), smem, stream, scores, nc, K, token_idx, d.num_kv_heads, kv_lens,  \
+                       rw, stride, nrows);                                                                       \
+  } while (0)
+  if (d.page_size == 64) BSG_TKR(64); else BSG_TKR(128);
+#undef BSG_TKR
+  return hipGetLastError();
 }
 
 // Scores of rows rw (B * rw.CT of them) into `scores`, then their exact top-K into token_idx.
@@ -794,6 +893,8 @@ static hipError_t token_topk_rows(const bsg_dims& d, const void* q, const int32_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(d.num_kv_heads, nrows);
+  if (!two && nc > TKS_NT * 16 && nc <= TKM_NT * TKM_PER)   // token-level rows for the 1024-thread form
+    return token_topk_rows_persistent(d, scores, nc, top_k_tokens, token_idx, kv_lens, rw, stride, nrows, stream);
   if (nc <= TKM_NT * TKM_PER)                      // rows whose keys fit in registers
     return token_topk_registers(d, two, scores, nc, top_k_tokens, block_idx, token_idx, kv_lens, rw, stride,
                                 gemm ? 1 : 0, nullptr, g2, stream);
