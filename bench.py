@@ -70,8 +70,10 @@ def _profile_record(name: str, src_files):
     return rec
 
 
-def _traffic(kernel_key: str, src_files):
-    rec = _profile_record(f"{kernel_key}_traffic", src_files)
+def _traffic(kernel_key: str):
+    """HBM bytes per launch from the committed counters of TRAFFIC_KERNELS[kernel_key], if the kernel's
+    sources still hash as they did when the counters were taken."""
+    rec = _profile_record(f"{kernel_key}_traffic", TRAFFIC_KERNELS[kernel_key][1])
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
@@ -680,12 +682,12 @@ def cpu_baseline_decode(spec, seed, n_sample=8, n_steps=5):
 # HBM traffic (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) and matrix-core utilisation of the kernels
 TRAFFIC_KERNELS = {
     # key: (kernel-name substring, source files, workload); the fp8 instantiations carry F8 = true
-    "sparse_attn_prefill_s131072": ("attn_prefill_mfma", ["attn_prefill.hip"], "prefill_bf16_s131072"),
-    "decode_unit_b32_ctx131072": ("decode_unit_kernel<128, 64, false>", ["attn_decode.hip", "decode_prologue.h"],
+    "sparse_attn_prefill_s131072": ("attn_prefill_mfma", ["attn_prefill.hip", "bsg_device.h"], "prefill_bf16_s131072"),
+    "decode_unit_b32_ctx131072": ("decode_unit_kernel<128, 64, false>", ["attn_decode.hip", "decode_prologue.h", "bsg_device.h"],
                                   "decode_bf16_b32_ctx131072"),
-    "decode_merge_b32_ctx131072": ("attn_decode_merge_kernel<unsigned short, 128>", ["attn_decode.hip"],
+    "decode_merge_b32_ctx131072": ("attn_decode_merge_kernel<unsigned short, 128>", ["attn_decode.hip", "bsg_device.h"],
                                    "decode_bf16_b32_ctx131072 (bf16 and fp8 steps)"),
-    "decode_fp8_unit_b32_ctx131072": ("decode_unit_kernel<128, 64, true>", ["attn_decode.hip", "decode_prologue.h"],
+    "decode_fp8_unit_b32_ctx131072": ("decode_unit_kernel<128, 64, true>", ["attn_decode.hip", "decode_prologue.h", "bsg_device.h"],
                                       "decode_bf16_b32_ctx131072 in fp8"),
 }
 CALIB_BYTES = 1 << 30
@@ -791,7 +793,7 @@ def summarize_counters(pmc_dir, trace_dir):
         # GRBM_GUI_ACTIVE is summed over the XCDs; per XCD it counts the kernel's active GPU cycles
         active = c["GRBM_GUI_ACTIVE"] / NUM_XCDS
         rec = {"kernel": "attn_prefill_mfma_kernel", "workload": f"prefill_bf16_{wl}",
-               "source_hash": _kernel_hash("attn_prefill.hip"), "launches": len(rs), "counters_per_launch": c,
+               "source_hash": _kernel_hash("attn_prefill.hip", "bsg_device.h"), "launches": len(rs), "counters_per_launch": c,
                "mfma_busy_frac": busy / (active * NUM_SIMDS) if active else None,
                "mfma_valu_coexec_frac": c["SQ_VALU_MFMA_COEXEC_CYCLES"] / (active * NUM_SIMDS) if active else None,
                "valu_insts_per_mfma": c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"] if c["SQ_INSTS_MFMA"] else None,
@@ -860,8 +862,8 @@ def main():
         r = run_prefill(spec, SPECS.index(spec), steps, args.warmup, tile_stats=True)
         p = prefill_line(spec, r)
         log(f"prefill 128K: {p['tok_per_s'] / 1e6:.2f} M tok/s, attention {p['roofline']['avg_launch_ms']:.2f} ms")
-        roof = dict(p["roofline"], traffic=_traffic("sparse_attn_prefill_s131072", ["attn_prefill.hip"]))
-        mf = _profile_record("sparse_attn_prefill_s131072_mfma", ["attn_prefill.hip"])
+        roof = dict(p["roofline"], traffic=_traffic("sparse_attn_prefill_s131072"))
+        mf = _profile_record("sparse_attn_prefill_s131072_mfma", ["attn_prefill.hip", "bsg_device.h"])
         roof["mfma_util"] = None if mf is None else {k: mf.get(k) for k in (
             "mfma_busy_frac", "mfma_valu_coexec_frac", "valu_insts_per_mfma", "observed_clock_ghz")}
         line.update(value=p["tok_per_s"], unit="tok/s", n_gpus=1, steps=steps, warmup=args.warmup,
@@ -876,7 +878,7 @@ def main():
         s1 = spec_by_name("prefill_bf16_s32768")
         r1 = run_prefill(s1, SPECS.index(s1), steps, args.warmup, tile_stats=True)
         p1 = prefill_line(s1, r1)
-        mf1 = _profile_record("sparse_attn_prefill_s32768_mfma", ["attn_prefill.hip"])
+        mf1 = _profile_record("sparse_attn_prefill_s32768_mfma", ["attn_prefill.hip", "bsg_device.h"])
         p1["roofline"]["mfma_util"] = None if mf1 is None else {k: mf1.get(k) for k in (
             "mfma_busy_frac", "mfma_valu_coexec_frac", "valu_insts_per_mfma", "observed_clock_ghz")}
         line["prefill_s32768"] = p1
@@ -887,8 +889,8 @@ def main():
         seed = SPECS.index(ds)
         warm = run_decode(ds, seed, dsteps, args.warmup)
         cold = run_decode(ds, seed, dsteps, args.warmup, rotate=4)
-        tr_u = _traffic("decode_unit_b32_ctx131072", ["attn_decode.hip", "decode_prologue.h"])
-        tr_m = _traffic("decode_merge_b32_ctx131072", ["attn_decode.hip"])
+        tr_u = _traffic("decode_unit_b32_ctx131072")
+        tr_m = _traffic("decode_merge_b32_ctx131072")
         line["decode"] = decode_line(ds, warm, "bsg_decode_step", (tr_u + tr_m) if (tr_u and tr_m) else None, cold)
         log(f"decode 128K x 32: warm {warm['us']['mean']:.1f} us, cold {cold['us']['mean']:.1f} us")
         if not args.no_cpu_baseline:
@@ -896,8 +898,8 @@ def main():
     if "fp8" in parts:
         ds = spec_by_name("decode_bf16_b32_ctx131072")
         d8 = run_decode(ds, SPECS.index(ds), dsteps, args.warmup, fp8=True)
-        tr_u8 = _traffic("decode_fp8_unit_b32_ctx131072", ["attn_decode.hip", "decode_prologue.h"])
-        tr_m = _traffic("decode_merge_b32_ctx131072", ["attn_decode.hip"])
+        tr_u8 = _traffic("decode_fp8_unit_b32_ctx131072")
+        tr_m = _traffic("decode_merge_b32_ctx131072")
         l8 = decode_line(ds, d8, "bsg_decode_step_fp8", (tr_u8 + tr_m) if (tr_u8 and tr_m) else None)
         l8["workload"] = ds.name + " (K, V and block cache in fp8 E4M3)"
         line["decode_fp8"] = l8
