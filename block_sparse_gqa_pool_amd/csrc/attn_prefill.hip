@@ -76,7 +76,9 @@ __device__ __forceinline__ void wait_copies_barrier() {
 //    sub-block would push a lane's sum of weights past 2^64 (or on the row's first block);
 //  * workgroups are mapped to tiles XCD by XCD: the dispatcher deals workgroups to the 8
 //    XCDs round robin, so consecutive ids are remapped to give each XCD a contiguous range
-//    of tiles, whose selections overlap, in its own L2.
+//    of tiles, whose selections overlap, in its own L2; within a range the last tiles go
+//    first, as later positions have more causal blocks to select from and cost more, so the
+//    cheap tiles fill the end of the launch.
 //  * the output rows leave through LDS: each lane's 8-byte pieces of its row are staged over
 //    the ring, then 16 lanes write a 256-byte row (instead of sixteen bytes of 32 rows per
 //    store).
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int qd8 = nwg >> 3, rd8 = nwg & 7;
   const int logical = xcd * qd8 + min(xcd, rd8) + slot;
-  const int tile = logical % n_tt;
+  const int tile = n_tt - 1 - logical % n_tt;     // later tiles (larger selections) first
   const int rest = logical / n_tt;
   const int gs = rest % (Hkv * slices);
   const int b = rest / (Hkv * slices);
