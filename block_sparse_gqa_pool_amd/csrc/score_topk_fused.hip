@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, (KCAP > 32 ? 1 : 2)) void score_topk_fused_ker
 
   const int G = Hq / Hkv;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int t0 = blockIdx.x * FS_TOK;
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * FS_TOK;   // later tiles (more candidates) first
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int L = kv_lens[b];
