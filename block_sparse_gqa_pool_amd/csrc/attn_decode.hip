@@ -510,7 +510,8 @@ __global__ __launch_bounds__(256, 2) void attn_decode_tokens_kernel(
   constexpr int NV = SUB * PPR / 64;
   extern __shared__ __attribute__((aligned(16))) unsigned char dm_smem[];
   const int G = Hq / Hkv;
-  const int g = blockIdx.y, rl = blockIdx.z;
+  // rows last first: a prefill row's list is shorter the earlier its position, so those fill the end
+  const int g = blockIdx.y, rl = (int)gridDim.z - 1 - (int)blockIdx.z;
   const int b = rw.seq(rl), tq = rw.pos(rl);
   if (tq >= rw.T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
