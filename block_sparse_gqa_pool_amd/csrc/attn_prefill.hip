@@ -75,10 +75,11 @@ __device__ __forceinline__ void wait_copies_barrier() {
 //  * each row keeps a lazy reference maximum: the output and sum are only rescaled when a
 //    sub-block would push a lane's sum of weights past 2^64 (or on the row's first block);
 //  * workgroups are mapped to tiles XCD by XCD: the dispatcher deals workgroups to the 8
-//    XCDs round robin, so consecutive ids are remapped to give each XCD a contiguous range
-//    of tiles, whose selections overlap, in its own L2; within a range the last tiles go
-//    first, as later positions have more causal blocks to select from and cost more, so the
-//    cheap tiles fill the end of the launch.
+//    XCDs round robin, so the ids are remapped to give each XCD two contiguous ranges of
+//    tiles (whose selections overlap, in its own L2), one early and one late in position:
+//    later positions have more causal blocks to select from and cost more, so pairing them
+//    evens out the XCDs' work; the later range and, within a range, the last tiles go first,
+//    so the cheap tiles fill the end of the launch.
 //  * the output rows leave through LDS: each lane's 8-byte pieces of its row are staged over
 //    the ring, then 16 lanes write a 256-byte row (instead of sixteen bytes of 32 rows per
 //    store).
@@ -109,14 +110,28 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   __shared__ int wsum[PF_WAVES];
   __shared__ int n_union;
 
-  // ---- XCD-aware tile: each XCD (workgroup id mod 8) gets a contiguous run of tiles
+  // ---- XCD-aware tile (the workgroup id mod 8 is its XCD).  The tiles (head-major, positions
+  // ascending) are cut into 16 equal contiguous parts and XCD x takes parts x and 15 - x: one
+  // earlier and one later range, so that the XCDs get equal work although a tile's union grows
+  // with its position, and each range stays contiguous for the XCD's L2.  The part with the
+  // later positions goes first and each part runs last position first (costliest first).
   const int G = Hq / Hkv;
   const int slices = G / HG;
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int qd8 = nwg >> 3, rd8 = nwg & 7;
-  const int logical = xcd * qd8 + min(xcd, rd8) + slot;
-  const int tile = n_tt - 1 - logical % n_tt;     // later tiles (larger selections) first
+  int logical;
+  if (nwg % 16 == 0) {
+    const int P = nwg >> 4;
+    const int pa = xcd, pb = 15 - xcd;
+    const int oa = (int)(((long long)pa * P) % n_tt), ob = (int)(((long long)pb * P) % n_tt);
+    const int first = ob > oa ? pb : pa, second = ob > oa ? pa : pb;
+    logical = slot < P ? first * P + (P - 1 - slot) : second * P + (2 * P - 1 - slot);
+  } else {                                         // a contiguous run per XCD
+    const int qd8 = nwg >> 3, rd8 = nwg & 7;
+    logical = xcd * qd8 + min(xcd, rd8) + slot;
+    logical = (logical / n_tt) * n_tt + (n_tt - 1 - logical % n_tt);
+  }
+  const int tile = logical % n_tt;
   const int rest = logical / n_tt;
   const int gs = rest % (Hkv * slices);
   const int b = rest / (Hkv * slices);
