@@ -952,7 +952,7 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
   constexpr int VPP = F8 ? 16 : 8;           // values per 16-byte piece of a representative
   constexpr int SEG = D / VPP;               // lanes per representative
   constexpr int BPI = 64 / SEG;              // representatives per wave-wide load
-  constexpr int U = 64 / BPI;                // loads in flight per lane: one batch = 64 blocks
+  constexpr int U = 64 / BPI;                // loads per lane of one batch of 64 blocks
   constexpr int NDS = D / 32;
   constexpr int NDT = D / 16;
   constexpr int VS = D + DM_VPAD;
@@ -1030,7 +1030,7 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
     __syncthreads();
   }
 
-  // ---- 1. scan: wave w takes blocks [w0, w1), 64 per batch (BPI per load, U loads in flight)
+  // ---- 1. scan: wave w takes blocks [w0, w1), 64 per batch (BPI per load, U loads per lane)
   if (cnt > 0) {
     const int piece = lane % SEG, sg = lane / SEG;
     float qv[VPP];
@@ -1044,18 +1044,21 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
       const int jb = w0 + 64 * c + lane;
       if (jb < w1) cpage[jb] = pids[c];
     }
-    // row loads of batch c (64 blocks, U per lane)
-    uint4 raw[2][U];
-    float scl[2][U];                                      // F8: the representative's scale
-    auto issue_rows = [&](int c, uint4 (&rw)[U], float (&sc)[U]) {
+    // row loads of half h of batch c (32 blocks, U / 2 per lane), into buffer h: one half in
+    // flight while the other is summed (whole 64-block batches in flight measured slower: more
+    // outstanding reads only add to the memory system's queues)
+    constexpr int UH = U / 2;
+    uint4 raw[2][UH];
+    float scl[2][UH];                                     // F8: the representative's scale
+    auto issue_rows = [&](int c, int h, uint4 (&rw)[UH], float (&sc)[UH]) {
       const int base = w0 + 64 * c;
       int pid = 0;
 #pragma unroll
       for (int c2 = 0; c2 < NPB; c2++)
         if (c2 == c) pid = pids[c2];
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int jl = u * BPI + sg;                      // block of this lane, relative to base
+      for (int u = 0; u < UH; u++) {
+        const int jl = 32 * h + u * BPI + sg;             // block of this lane, relative to base
         const int p = __shfl(pid, jl, 64);
         rw[u] = base + jl < w1 ? *reinterpret_cast<const uint4*>(bc + (size_t)p * Hkv * D * ES)
                                : make_uint4(0, 0, 0, 0);
@@ -1063,38 +1066,42 @@ __global__ __launch_bounds__(DU_NT, 1) void decode_unit_kernel(
       }
     };
     const int nbat = (w1 - w0 + 63) / 64;
-    if (nbat > 0) issue_rows(0, raw[0], scl[0]);
+    if (nbat > 0) issue_rows(0, 0, raw[0], scl[0]);
 #pragma unroll
     for (int c = 0; c < NPB; c++) {
       if (c >= nbat) break;
-      if (c + 1 < nbat) issue_rows(c + 1, raw[(c + 1) & 1], scl[(c + 1) & 1]);
-      const int base = w0 + 64 * c;
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int jb = base + u * BPI + sg;
-        const uint4 rr = raw[c & 1][u];
-        const uint32_t wd[4] = {rr.x, rr.y, rr.z, rr.w};
-        float s = 0.0f;
-        if constexpr (F8) {
+      for (int h = 0; h < 2; h++) {
+        if (h == 0) issue_rows(c, 1, raw[1], scl[1]);
+        else if (c + 1 < nbat) issue_rows(c + 1, 0, raw[0], scl[0]);
+        const int base = w0 + 64 * c + 32 * h;
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], true);
-            s = fmaf(qv[4 * i], lo[0], s);
-            s = fmaf(qv[4 * i + 1], lo[1], s);
-            s = fmaf(qv[4 * i + 2], hi[0], s);
-            s = fmaf(qv[4 * i + 3], hi[1], s);
+        for (int u = 0; u < UH; u++) {
+          const int jb = base + u * BPI + sg;
+          const uint4 rr = raw[h][u];
+          const uint32_t wd[4] = {rr.x, rr.y, rr.z, rr.w};
+          float s = 0.0f;
+          if constexpr (F8) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], false);
+              const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], true);
+              s = fmaf(qv[4 * i], lo[0], s);
+              s = fmaf(qv[4 * i + 1], lo[1], s);
+              s = fmaf(qv[4 * i + 2], hi[0], s);
+              s = fmaf(qv[4 * i + 3], hi[1], s);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              s = fmaf(qv[2 * i], __uint_as_float(wd[i] << 16), s);
+              s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
+            }
           }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            s = fmaf(qv[2 * i], __uint_as_float(wd[i] << 16), s);
-            s = fmaf(qv[2 * i + 1], __uint_as_float(wd[i] & 0xffff0000u), s);
-          }
+          s = seg_sum_dpp<SEG>(s);
+          if (F8) s *= scl[h][u];
+          if (piece == 0 && jb < w1) keys[jb] = sel_key(s, jb);
         }
-        s = seg_sum_dpp<SEG>(s);
-        if (F8) s *= scl[c & 1][u];
-        if (piece == 0 && jb < w1) keys[jb] = sel_key(s, jb);
       }
     }
   }
