@@ -163,7 +163,36 @@ def decode_bytes(block_idx, kv_lens, page_size, Hkv, D, elem=2):
 
 
 # ------------------------------------------------------------------------------------ prefill
-def run_prefill(spec, seed, steps, warmup, tile_stats=False):
+def planted_recall(idx, w):
+    """Share of the generator's planted blocks that the device selection kept.  The planted blocks
+    are the group's true top blocks by construction, so this is the recall check of the index (a
+    soft quality figure, not parity).  idx: device [B, Hkv, q_len, k] logical block ids."""
+    import torch
+    B, Hkv, q_len, k = idx.shape
+    dev = idx.device
+    if w.planted is not None:
+        pl = w.planted.to(dev)                                        # [B, Hkv, q_len, n]
+    else:
+        pr = w.planted_region.to(dev)                                 # [B, Hkv, regions, n]
+        pl = torch.empty(B, Hkv, q_len, pr.shape[-1], dtype=pr.dtype, device=dev)
+        for b in range(B):
+            pos = torch.arange(w.kv_lens_host[b] - q_len, w.kv_lens_host[b], device=dev)
+            pl[b] = pr[b][:, pos // w.spec.region]
+    hit = torch.zeros((), dtype=torch.int64, device=dev)
+    tot = torch.zeros((), dtype=torch.int64, device=dev)
+    step = max(1, (1 << 27) // max(1, B * Hkv * k * pl.shape[-1]))   # bound the comparison's memory
+    for t0 in range(0, q_len, step):
+        p = pl[:, :, t0:t0 + step]
+        got = (idx[:, :, t0:t0 + step, None, :] == p[..., None]).any(-1) & (p >= 0)
+        hit += got.sum()
+        tot += (p >= 0).sum()
+    n = int(tot)
+    return {"planted": n, "kept": int(hit), "recall": (int(hit) / n) if n else None}
+
+
+def run_prefill(spec, seed, steps, warmup, tile_stats=False, keep_ranges=None):
+    """keep_ranges: (starts, length) of query ranges whose device selections and outputs are copied
+    to the host (for the oracle comparison of the cpu_baseline leg)."""
     import torch
     import block_sparse_gqa_pool_amd as bsg
     from workloads import make_workload
@@ -211,6 +240,11 @@ def run_prefill(spec, seed, steps, warmup, tile_stats=False):
                stage=stage, attn_flops=flops)
     if tile_stats:
         res["tiles"] = prefill_tile_stats(idx, w.kv_lens, S, bs, spec.group_size, D)
+    res["planted_recall"] = planted_recall(idx, w)
+    if keep_ranges is not None:
+        starts, n = keep_ranges
+        res["kept_rows"] = [(int(t0), idx[:, :, t0:t0 + n].cpu().numpy(), out[:, :, t0:t0 + n].float().cpu().numpy())
+                            for t0 in starts]
     del w, cache, idx, out, ws
     torch.cuda.empty_cache()
     return res
@@ -229,6 +263,8 @@ def prefill_line(spec, r):
     if "tiles" in r:
         t = r["tiles"]
         d["tiles"] = dict(t, selected_over_issued=r["attn_flops"] / t["issued_flops"])
+    if "planted_recall" in r:
+        d["planted_recall"] = r["planted_recall"]
     return d
 
 
@@ -410,7 +446,8 @@ def run_decode(spec, seed, steps, warmup, fp8=False, rotate=1, graph_replay=True
              for s in sets]
     nbytes = sum(p[0] for p in parts) / rotate
     res = dict(us=_stats(per_step), wall_us_per_step=1e6 * wall / (n_rep * PER_GRAPH), bytes=nbytes,
-               bytes_parts=parts[0][1], steps=n_rep * PER_GRAPH)
+               bytes_parts=parts[0][1], steps=n_rep * PER_GRAPH,
+               planted_recall=planted_recall(sets[0]["idx"][:, :, None, :], sets[0]["w"]))
     del graph, sets
     torch.cuda.empty_cache()
     return res
@@ -425,6 +462,8 @@ def decode_line(spec, d, api, traffic=None, cold=None):
     line = {"workload": spec.name, "api": api, "us_per_step": d["us"]["mean"], "us_per_step_median": d["us"]["median"],
             "steps": d["steps"], "timing": f"{PER_GRAPH} steps per HIP graph replay, HIP events per replay",
             "roofline": dict(roof(d), bytes_parts=d["bytes_parts"], traffic=traffic)}
+    if "planted_recall" in d:
+        line["planted_recall"] = d["planted_recall"]
     if cold is not None:
         line["cold"] = {"us_per_step": cold["us"]["mean"], "us_per_step_median": cold["us"]["median"],
                         "steps": cold["steps"], "rotation": "4 workloads of different seeds, cycled step by step",
@@ -529,13 +568,39 @@ def _oracle_prefill_range(args):
     """Oracle scores, top-k and attention for the queries [t0, t0 + n) of a prefill: the chunk of a
     prefill whose queries end at position t0 + n - 1, i.e. kv_len = t0 + n, q_len = n."""
     import oracle as O
-    q_rows, pt, t0, Hkv, bs, k, scale = args
+    q_rows, pt, t0, Hkv, bs, k, scale = args[:7]
     n = q_rows.shape[2]
     kv = [t0 + n]
     sc = O.group_scores(q_rows, _ORACLE["cache"], pt, kv, Hkv, bs)
     idx = O.select_blocks(sc, kv, n, bs, k)
-    O.sparse_attention(q_rows, _ORACLE["k"], _ORACLE["v"], pt, kv, idx, scale)
-    return n
+    out, _ = O.sparse_attention(q_rows, _ORACLE["k"], _ORACLE["v"], pt, kv, idx, scale)
+    if len(args) == 7:
+        return n, None
+    return n, _compare_rows(args[7], args[8], idx, out, sc, k)
+
+
+def _compare_rows(gpu_idx, gpu_out, ora_idx, ora_out, scores, k, tie_rel=1e-4):
+    """Device selections and outputs of sampled rows against the oracle's: rows whose selection
+    differs (and how many of those lie inside the tie window: the oracle's last kept and first
+    dropped candidates within tie_rel of each other, every differing block inside that window),
+    and the absolute output errors."""
+    import numpy as np
+    diff = np.nonzero((gpu_idx != ora_idx).any(-1))
+    exempt = 0
+    for b, g, t in zip(*diff):
+        row = scores[b, g, t]
+        own = int(ora_idx[b, g, t][ora_idx[b, g, t] >= 0][-1])
+        cands = sorted(range(own), key=lambda j: (-np.float32(row[j]), j))
+        m = k - 1
+        if len(cands) > m >= 1:
+            sa, sb = row[cands[m - 1]], row[cands[m]]
+            win = tie_rel * max(abs(sa), abs(sb))
+            sym = set(int(x) for x in gpu_idx[b, g, t] if x >= 0) ^ set(int(x) for x in ora_idx[b, g, t] if x >= 0)
+            if abs(sa - sb) < win and all(abs(row[j] - sa) <= win or abs(row[j] - sb) <= win for j in sym if j < own):
+                exempt += 1
+    err = np.abs(gpu_out.astype(np.float64) - ora_out)
+    return dict(rows=int(np.prod(gpu_idx.shape[:3])), idx_rows_differing=int(len(diff[0])), idx_rows_in_tie_window=exempt,
+                out_max_abs_err=float(err.max()), out_abs_err_sum=float(err.sum()), out_elems=int(err.size))
 
 
 def _oracle_decode_seq(args):
@@ -578,7 +643,15 @@ def _pool(paths, n):
     return ex
 
 
-def cpu_baseline_prefill(spec, seed, n_ranges=32, range_len=192):
+BASELINE_RANGES = (32, 192)       # query ranges x tokens the prefill cpu_baseline samples
+
+
+def baseline_ranges(S, n_ranges=BASELINE_RANGES[0], range_len=BASELINE_RANGES[1]):
+    import numpy as np
+    return np.linspace(0, S - range_len, n_ranges).astype(np.int64), range_len
+
+
+def cpu_baseline_prefill(spec, seed, n_ranges=BASELINE_RANGES[0], range_len=BASELINE_RANGES[1], kept_rows=None):
     """The oracle on the host's cores: the block pool over all blocks (one process, vectorised), then
     scores + top-k + attention for n_ranges query ranges of range_len tokens spread over the sequence,
     extrapolated linearly to all tokens."""
@@ -593,8 +666,9 @@ def cpu_baseline_prefill(spec, seed, n_ranges=32, range_len=192):
     pt = w.page_table.cpu().numpy()
     kv = list(w.kv_lens_host)
     S = w.q.shape[2]
-    starts = np.linspace(0, S - range_len, n_ranges).astype(np.int64)
+    starts, _ = baseline_ranges(S, n_ranges, range_len)
     q_rows = [w.q[:, :, t0:t0 + range_len].float().cpu().numpy() for t0 in starts]
+    gpu = {t0: (gi, go) for t0, gi, go in kept_rows} if kept_rows else {}
     del w
     torch.cuda.empty_cache()
     t0 = time.perf_counter()
@@ -608,13 +682,23 @@ def cpu_baseline_prefill(spec, seed, n_ranges=32, range_len=192):
         ex = _pool(paths, nw)
         try:
             t1 = time.perf_counter()
-            done = sum(ex.map(_oracle_prefill_range, [(q, pt, int(s), spec.num_kv_heads, spec.page_size, spec.top_k,
-                                                       scale) for q, s in zip(q_rows, starts)]))
+            res = list(ex.map(_oracle_prefill_range, [(q, pt, int(s), spec.num_kv_heads, spec.page_size, spec.top_k,
+                                                        scale) + tuple(gpu.get(int(s), ())) for q, s in zip(q_rows, starts)]))
             t_att = time.perf_counter() - t1
         finally:
             ex.shutdown()
+    done = sum(r[0] for r in res)
+    cmp = [r[1] for r in res if r[1] is not None]
+    parity = None
+    if cmp:
+        parity = {key: sum(c[key] for c in cmp) for key in ("rows", "idx_rows_differing", "idx_rows_in_tie_window",
+                                                            "out_elems")}
+        parity["out_max_abs_err"] = max(c["out_max_abs_err"] for c in cmp)
+        parity["out_mean_abs_err"] = sum(c["out_abs_err_sum"] for c in cmp) / parity.pop("out_elems")
+        parity["sample"] = (f"the device's selections and outputs of the same {done} query tokens (all heads) from the "
+                            "timed prefill steps, against the oracle")
     est = t_pool + t_att / done * S
-    return dict(value=S / est, unit="tok/s", cores=nw, kind="oracle",
+    return dict(value=S / est, unit="tok/s", cores=nw, kind="oracle", parity=parity,
                 sample=(f"block_pool over all {pt.shape[1]} blocks ({t_pool:.1f} s, one process) + scores, top-k and "
                         f"attention for {n_ranges} query ranges of {range_len} tokens spread over the sequence "
                         f"({done} tokens, {t_att:.1f} s wall on {nw} worker processes), extrapolated linearly to all "
@@ -859,7 +943,8 @@ def main():
     spec = spec_by_name("prefill_bf16_s131072")
     line = {"metric": METRIC}
     if "prefill" in parts:
-        r = run_prefill(spec, SPECS.index(spec), steps, args.warmup, tile_stats=True)
+        r = r_pf = run_prefill(spec, SPECS.index(spec), steps, args.warmup, tile_stats=True,
+                               keep_ranges=None if args.no_cpu_baseline else baseline_ranges(spec.seq_len))
         p = prefill_line(spec, r)
         log(f"prefill 128K: {p['tok_per_s'] / 1e6:.2f} M tok/s, attention {p['roofline']['avg_launch_ms']:.2f} ms")
         roof = dict(p["roofline"], traffic=_traffic("sparse_attn_prefill_s131072"))
@@ -928,7 +1013,10 @@ def main():
             line[key] = prefill_tokens_line(s1, r, two)
             log(f"{key} 32K: {r['ms_per_step']:.2f} ms per prefill")
     if "prefill" in parts:
-        line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(spec, SPECS.index(spec))
+        line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(
+            spec, SPECS.index(spec), kept_rows=r_pf.pop("kept_rows", None))
+        if line["cpu_baseline"] is not None:
+            line["parity_sample"] = line["cpu_baseline"].pop("parity")
     print(json.dumps(line), flush=True)
 
 
