@@ -958,7 +958,8 @@ def main():
                             "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
                             "head_dim": spec.head_dim, "block_size": spec.page_size, "top_k": spec.top_k},
                     roofline=roof, stages_ms=p["stages_ms"], wall_ms_per_step=r["wall_ms_per_step"],
-                    pipeline_mfma_frac=p["pipeline_mfma_frac"], tiles=p["tiles"])
+                    pipeline_mfma_frac=p["pipeline_mfma_frac"], tiles=p["tiles"],
+                    planted_recall=p.get("planted_recall"))
     if "prefill32k" in parts:
         s1 = spec_by_name("prefill_bf16_s32768")
         r1 = run_prefill(s1, SPECS.index(s1), steps, args.warmup, tile_stats=True)
