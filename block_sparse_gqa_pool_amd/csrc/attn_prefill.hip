@@ -261,17 +261,16 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   const uint32_t wave_slot = __builtin_amdgcn_readfirstlane((wave - PF_CW0) * 1024);
   const bf16_t* kbase = k_cache + (size_t)g * BS * D;   // + page * Hkv * BS * D
   const bf16_t* vbase = v_cache + (size_t)g * BS * D;
-  // copies of sub-block ic (block cj in page cp) into LDS stage c_stage; ic advances
+  // this wave's share of the copies of sub-block ic (block cj in page cp) into LDS stage c_stage
   int ic = 0, c_stage = 0;
-  auto issue = [&](int cj, int cp) {
+  auto copy_sub = [&](int cj, int cp) {
     const int h2 = ic % NSUB;
     const int nvb = min(BS, L - cj * BS);                // valid keys of the block (>= 1)
     const size_t poff = (size_t)cp * Hkv * BS * D + (size_t)h2 * SUB * D;
     const bf16_t* kp = kbase + poff;
     const bf16_t* vp = vbase + poff;
     const uint32_t sb = smem_base + (uint32_t)(c_stage * STG) + wave_slot;
-    if (!copier) {
-    } else if (nvb >= (h2 + 1) * SUB) {                  // every key of the sub-block is valid
+    if (nvb >= (h2 + 1) * SUB) {                         // every key of the sub-block is valid
 #pragma unroll
       for (int c = 0; c < NCP; c++) {
         lds_dma16(kp + coff[c], sb + c * PF_CW * 1024);
@@ -286,6 +285,10 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
         lds_dma16(vp + eo, sb + c * PF_CW * 1024 + TILE);
       }
     }
+  };
+  // the next sub-block's copies (waves 0-3), and every wave's count of issued sub-blocks
+  auto issue = [&](int cj, int cp) {
+    if (copier) copy_sub(cj, cp);
     ic++;
     c_stage = c_stage + 1 == nst ? 0 : c_stage + 1;
   };
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   const int NS = U * NSUB;
   while (ic < nst - 1 && ic < NS) {
     const int u = ic / NSUB;
-    issue(__builtin_amdgcn_readfirstlane(ulist[u]), __builtin_amdgcn_readfirstlane(upage[u]));
+    issue(copier ? __builtin_amdgcn_readfirstlane(ulist[u]) : 0, copier ? __builtin_amdgcn_readfirstlane(upage[u]) : 0);
   }
   // the block schedule is read one block ahead, so that no LDS latency sits between the
   // barrier and the first product: jn = next union block, selc = this row's next selection
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
     else wait_copies_barrier<0>();
     // schedule entry of this iteration's copy, read now and used at the end
     int cj = 0, cp = 0;
-    if (ic < NS) {
+    if (copier && ic < NS) {
       cj = ulist[ic / NSUB];
       cp = upage[ic / NSUB];
     }
