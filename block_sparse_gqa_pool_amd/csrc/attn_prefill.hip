@@ -186,13 +186,15 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
         bits &= bits - 1;
         const int j = (w << 5) + bit;
         ulist[off] = j;
-        upage[off] = page_id(page_table[(size_t)b * pt_stride + j], num_pages);
         off++;
       }
     }
   }
   __syncthreads();
   const int U = n_union;
+  // the union's physical pages: one page-table lookup per thread, all in flight together
+  for (int u = tid; u < U; u += NT) upage[u] = page_id(page_table[(size_t)b * pt_stride + ulist[u]], num_pages);
+  __syncthreads();
 
   // ---- this lane's query row
   const int col = lane & 31;
