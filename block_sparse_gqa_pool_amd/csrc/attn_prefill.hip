@@ -116,21 +116,30 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   __shared__ int n_union;
 
   // ---- XCD-aware tile (the workgroup id mod 8 is its XCD).  The tiles (head-major, positions
-  // ascending) are cut into 16 equal contiguous parts and XCD x takes parts x and 15 - x: one
-  // earlier and one later range, so that the XCDs get equal work although a tile's union grows
-  // with its position, and each range stays contiguous for the XCD's L2.  The part with the
-  // later positions goes first and each part runs last position first (costliest first).
+  // ascending) are cut into equal contiguous parts and XCD x takes parts x and 15 - x of every
+  // 16: one earlier and one later range, so that the XCDs get equal work although a tile's union
+  // grows with its position, and each range stays contiguous for the XCD's L2.  The part with
+  // the later positions goes first and each part runs last position first (costliest first).
   const int G = Hq / Hkv;
   const int slices = G / HG;
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   int logical;
   if (nwg % 16 == 0) {
-    const int P = nwg >> 4;
-    const int pa = xcd, pb = 15 - xcd;
+    // R rounds of 16 equal parts; in round k XCD x takes parts 16k + x and 16k + 15 - x.  One
+    // round while a part is at least half of one (sequence, group)'s tiles: the two parts of an
+    // XCD are then an early and a late range.  With shorter parts a pair can be two middle
+    // ranges, which cost more (a tile's union grows with its position and then saturates), so
+    // the parts are made finer (down to 32 tiles), every round covering other positions.
+    int R = 1;
+    if (2 * (nwg / 16) < n_tt)
+      while (R < 8 && nwg % (32 * R) == 0 && nwg / (32 * R) >= 32) R *= 2;
+    const int P = nwg / (16 * R);
+    const int k = slot / (2 * P), s2 = slot % (2 * P);
+    const int pa = 16 * k + xcd, pb = 16 * k + 15 - xcd;
     const int oa = (int)(((long long)pa * P) % n_tt), ob = (int)(((long long)pb * P) % n_tt);
     const int first = ob > oa ? pb : pa, second = ob > oa ? pa : pb;
-    logical = slot < P ? first * P + (P - 1 - slot) : second * P + (2 * P - 1 - slot);
+    logical = s2 < P ? first * P + (P - 1 - s2) : second * P + (2 * P - 1 - s2);
   } else {                                         // a contiguous run per XCD
     const int qd8 = nwg >> 3, rd8 = nwg & 7;
     logical = xcd * qd8 + min(xcd, rd8) + slot;
