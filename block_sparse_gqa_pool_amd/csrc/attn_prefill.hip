@@ -125,7 +125,20 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   int logical;
-  if (nwg % 16 == 0) {
+  const int NR = nwg / n_tt;                         // (sequence, group, head slice) ranges
+  if (NR % 8 == 0 && n_tt % 16 == 0 && n_tt / 16 >= 32) {
+    // Each range is cut into 16 parts of P tiles.  In round k (of 8 per eight ranges, run
+    // k = 7 down to 0) XCD x takes parts 15 - k, then k, of range 8c + (x + k) mod 8: every XCD
+    // sees every position pair and every range once, whatever the ranges' cost profiles, and
+    // at any time the XCDs work on eight different ranges (different strides of the caches).
+    const int P = n_tt / 16;
+    const int rnd = slot / (2 * P), s2 = slot % (2 * P);
+    const int c = rnd >> 3, k = 7 - (rnd & 7);
+    const int rest8 = 8 * c + ((xcd + k) & 7);
+    const int part = s2 < P ? 15 - k : k;
+    const int within = s2 < P ? s2 : s2 - P;
+    logical = rest8 * n_tt + part * P + (P - 1 - within);
+  } else if (nwg % 16 == 0) {
     // R rounds of 16 equal parts; in round k XCD x takes parts 16k + x and 16k + 15 - x.  One
     // round while a part is at least half of one (sequence, group)'s tiles: the two parts of an
     // XCD are then an early and a late range.  With shorter parts a pair can be two middle
