@@ -80,11 +80,11 @@ __device__ __forceinline__ void wait_copies_barrier() {
 //  * each row keeps a lazy reference maximum: the output and sum are only rescaled when a
 //    sub-block would push a lane's sum of weights past 2^64 (or on the row's first block);
 //  * workgroups are mapped to tiles XCD by XCD: the dispatcher deals workgroups to the 8
-//    XCDs round robin, so the ids are remapped to give each XCD two contiguous ranges of
-//    tiles (whose selections overlap, in its own L2), one early and one late in position:
+//    XCDs round robin, so the ids are remapped to give each XCD contiguous ranges of tiles
+//    (whose selections overlap, in its own L2) in pairs, one early and one late in position:
 //    later positions have more causal blocks to select from and cost more, so pairing them
 //    evens out the XCDs' work; the later range and, within a range, the last tiles go first,
-//    so the cheap tiles fill the end of the launch.
+//    so the cheap tiles fill the end of the launch (three forms, below).
 //  * the output rows leave through LDS: each lane's 8-byte pieces of its row are staged over
 //    the ring, then 16 lanes write a 256-byte row (instead of sixteen bytes of 32 rows per
 //    store).
