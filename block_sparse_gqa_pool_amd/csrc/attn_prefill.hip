@@ -67,10 +67,10 @@ __device__ __forceinline__ void wait_copies_barrier() {
 // ---------------------------------------------------------------------------------------
 // Data movement and scheduling:
 //  * the union's blocks are streamed in 64-key sub-blocks through a ring of nst LDS stages
-//    (K and V tile each); the copies of sub-block i+nst-1 are issued straight from global
-//    memory into LDS (no register staging) at the end of iteration i by waves 0-3, into the
-//    stage every wave released before that iteration's barrier, so up to nst-1 sub-blocks are
-//    in flight while one is computed;
+//    (K and V tile each), copied by waves 0-3 straight from global memory into LDS (no
+//    register staging) into stages every wave released at an earlier barrier: with 4 stages
+//    the sub-blocks go in pairs, one barrier per pair and the next pair in flight while one is
+//    computed; with fewer, one barrier per sub-block and up to nst-1 sub-blocks in flight;
 //  * a workgroup is 8 waves (256 query rows = 32 tokens x 8 heads for G = 8): the selections
 //    of neighbouring tokens overlap, so the union grows much slower than the row count and
 //    the K/V bytes fetched per query row drop with the tile size;
@@ -88,7 +88,7 @@ __device__ __forceinline__ void wait_copies_barrier() {
 //  * the output rows leave through LDS: each lane's 8-byte pieces of its row are staged over
 //    the ring, then 16 lanes write a 256-byte row (instead of sixteen bytes of 32 rows per
 //    store).
-template <int D, int BS>
+template <int D, int BS, bool PAIRS>
 __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kv_lens, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
@@ -318,7 +318,13 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   };
 
   const int NS = U * NSUB;
-  while (ic < nst - 1 && ic < NS) {
+  // With a ring of 4 stages the sub-blocks go in pairs: one barrier per pair, the pair's copies
+  // issued at the start of the pair before (into the stages of the pair before that, released
+  // at that barrier).  With fewer stages (large tables leave less LDS), one barrier per
+  // sub-block, the copies of sub-block i+nst-1 issued at the end of iteration i.  Pairs halve
+  // the barriers and even out the waves' work per barrier: when the waves attend to different
+  // sub-blocks (32K prompt: ~2-3 of 8 waves per block), a barrier waits for the busiest SIMD.
+  while (ic < (PAIRS ? 2 : nst - 1) && ic < NS) {
     const int u = ic / NSUB;
     issue(copier ? __builtin_amdgcn_readfirstlane(ulist[u]) : 0, copier ? __builtin_amdgcn_readfirstlane(upage[u]) : 0);
   }
@@ -329,18 +335,34 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   int j = 0;
   bool mine = false;
   int r_stage = 0;                                      // stage of sub-block i
-  for (int i = 0; i < NS; i++) {
-    // stage i has landed once at most min(nst-2, NS-1-i) younger stages are outstanding
-    const int ahead = min(nst - 2, NS - 1 - i);
-    if (ahead >= 2) wait_copies_barrier<4 * NCP>();
-    else if (ahead == 1) wait_copies_barrier<2 * NCP>();
-    else wait_copies_barrier<0>();
-    // schedule entry of this iteration's copy, read now and used at the end
+  constexpr int PER = PAIRS ? 2 : 1;                   // sub-blocks per barrier
+  for (int i0 = 0; i0 < NS; i0 += PER) {
     int cj = 0, cp = 0;
-    if (copier && ic < NS) {
-      cj = ulist[ic / NSUB];
-      cp = upage[ic / NSUB];
+    if constexpr (PAIRS) {
+      // pair i0/2 has landed (nothing younger is in flight); the next pair's copies
+      wait_copies_barrier<0>();
+#pragma unroll 1
+      for (int c2 = 0; c2 < 2; c2++) {
+        if (ic < NS) {
+          const int u = ic / NSUB;
+          issue(copier ? __builtin_amdgcn_readfirstlane(ulist[u]) : 0, copier ? __builtin_amdgcn_readfirstlane(upage[u]) : 0);
+        }
+      }
+    } else {
+      const int i = i0;
+      // stage i has landed once at most min(nst-2, NS-1-i) younger stages are outstanding
+      const int ahead = min(nst - 2, NS - 1 - i);
+      if (ahead >= 2) wait_copies_barrier<4 * NCP>();
+      else if (ahead == 1) wait_copies_barrier<2 * NCP>();
+      else wait_copies_barrier<0>();
+      // schedule entry of this iteration's copy, read now and used at the end
+      if (copier && ic < NS) {
+        cj = ulist[ic / NSUB];
+        cp = upage[ic / NSUB];
+      }
     }
+#pragma unroll 1
+  for (int i = i0; i < i0 + PER && i < NS; i++) {
     const int h2 = i % NSUB;
     if (h2 == 0) {
       j = __builtin_amdgcn_readfirstlane(jn);
@@ -458,8 +480,9 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
       }
     }
     // next copy, into the stage everyone finished with before this iteration's barrier
-    if (ic < NS) issue(__builtin_amdgcn_readfirstlane(cj), __builtin_amdgcn_readfirstlane(cp));
+    if (!PAIRS && ic < NS) issue(__builtin_amdgcn_readfirstlane(cj), __builtin_amdgcn_readfirstlane(cp));
     r_stage = r_stage + 1 == nst ? 0 : r_stage + 1;
+  }
   }
 
   const float l = l_i + __shfl_xor(l_i, 32, 64);
@@ -611,7 +634,7 @@ hipError_t launch_attn_prefill(const bsg_dims& d, const void* q, int q_len, cons
         dim3 grid((unsigned)nwg);
 #define BSG_PF(DD, BB)                                                                                       \
   do {                                                                                                        \
-    auto kfn = attn_prefill_mfma_kernel<DD, BB>;                                                             \
+    auto kfn = nst == 4 ? attn_prefill_mfma_kernel<DD, BB, true> : attn_prefill_mfma_kernel<DD, BB, false>;   \
     { hipError_t ea_ = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); if (ea_ != hipSuccess) return ea_; } \
     hipLaunchKernelGGL(kfn, grid, dim3(64 * PF_WAVES), smem, stream, (const bf16_t*)q, kv_lens,             \
                        (const bf16_t*)k_cache, (const bf16_t*)v_cache, page_table, block_idx, scale,          \
