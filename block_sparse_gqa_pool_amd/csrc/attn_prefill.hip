@@ -319,8 +319,8 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
 
   const int NS = U * NSUB;
   // With a ring of 4 stages the sub-blocks go in pairs: one barrier per pair, the pair's copies
-  // issued at the start of the pair before (into the stages of the pair before that, released
-  // at that barrier).  With fewer stages (large tables leave less LDS), one barrier per
+  // issued during the pair before, after its first sub-block (into the stages of the pair
+  // before that, released at that pair's barrier).  With fewer stages (large tables leave less LDS), one barrier per
   // sub-block, the copies of sub-block i+nst-1 issued at the end of iteration i.  Pairs halve
   // the barriers and even out the waves' work per barrier: when the waves attend to different
   // sub-blocks (32K prompt: ~2-3 of 8 waves per block), a barrier waits for the busiest SIMD.
@@ -339,15 +339,8 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
   for (int i0 = 0; i0 < NS; i0 += PER) {
     int cj = 0, cp = 0;
     if constexpr (PAIRS) {
-      // pair i0/2 has landed (nothing younger is in flight); the next pair's copies
+      // pair i0/2 has landed (nothing younger is in flight)
       wait_copies_barrier<0>();
-#pragma unroll 1
-      for (int c2 = 0; c2 < 2; c2++) {
-        if (ic < NS) {
-          const int u = ic / NSUB;
-          issue(copier ? __builtin_amdgcn_readfirstlane(ulist[u]) : 0, copier ? __builtin_amdgcn_readfirstlane(upage[u]) : 0);
-        }
-      }
     } else {
       const int i = i0;
       // stage i has landed once at most min(nst-2, NS-1-i) younger stages are outstanding
@@ -481,6 +474,15 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void attn_prefill_mfma_kernel(
     }
     // next copy, into the stage everyone finished with before this iteration's barrier
     if (!PAIRS && ic < NS) issue(__builtin_amdgcn_readfirstlane(cj), __builtin_amdgcn_readfirstlane(cp));
+    if (PAIRS && i == i0) {
+#pragma unroll 1
+      for (int c2 = 0; c2 < 2; c2++) {
+        if (ic < NS) {
+          const int u = ic / NSUB;
+          issue(copier ? __builtin_amdgcn_readfirstlane(ulist[u]) : 0, copier ? __builtin_amdgcn_readfirstlane(upage[u]) : 0);
+        }
+      }
+    }
     r_stage = r_stage + 1 == nst ? 0 : r_stage + 1;
   }
   }
