@@ -3,9 +3,11 @@
 The kernel remaps workgroup ids to tiles so that each XCD gets a balanced set of positions.
 There are three forms, chosen by the launch's shape: eight or more (sequence, head) ranges of
 at least 512 tiles (ranges rotate over the XCDs), shorter parts cut finer, and the plain
-contiguous deal.  A mistake in any of them would leave some tiles unwritten or write others
-twice.  Each case here starts from NaN-filled outputs and requires every output and
-log-sum-exp row to be written with finite values, then compares sampled rows with the oracle.
+contiguous deal.  One more case takes the kernel's form for a three-stage ring (one barrier
+per sub-block instead of pairs).  A mistake in any of them would leave some tiles unwritten or
+write others twice.  Each case here starts from NaN-filled outputs and requires every output
+and log-sum-exp row to be written with finite values, then compares sampled rows with the
+oracle.
 """
 import math
 
@@ -26,10 +28,13 @@ DEV = "cuda:0"
 CASES = [
     # 8 KV heads x 512 tiles of 32 tokens: the rotating form
     (dict(num_q_heads=64, num_kv_heads=8, page_size=128, top_k=16, seq_len=16384), "rotate"),
-    # 4 KV heads x 512 tiles: 16 parts would be quarter ranges, so finer parts (2 rounds)
+    # 4 KV heads x 512 tiles: 16 parts would be quarter ranges, so finer parts (4 rounds of 16)
     (dict(num_q_heads=32, num_kv_heads=4, page_size=64, top_k=32, seq_len=16384), "finer"),
     # 3 KV heads x 97 tiles (ragged last tile): the contiguous form
     (dict(num_q_heads=24, num_kv_heads=3, page_size=64, top_k=8, seq_len=32 * 96 + 17), "contiguous"),
+    # no GQA sharing (256 tokens per tile) and top-40: the selections take 40 KiB of LDS, so the
+    # ring has 3 stages and the kernel runs one barrier per sub-block instead of pairs
+    (dict(num_q_heads=4, num_kv_heads=4, page_size=64, top_k=40, seq_len=4096 + 77), "three_stage_ring"),
 ]
 
 
